@@ -1,0 +1,232 @@
+"""Plain fp64 CPU definition of one DSA layer (indexer -> top-k -> sparse MLA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module;
+it shares no code with the HIP library.  Every function is a direct, unblocked
+transcription of the definition it cites; NumPy matmul/sort are the only library
+steps.
+
+Sources (page titles and sections):
+  [K31]  "vLLM Day-0 support for Kimi K3.1 Pro across GPU, TPU and PPU":
+         "Sparse attention in K3.1 Pro" (32 light heads score every earlier
+         token, keep the top 2,048, exact MLA over those only; FP8 index key of
+         132 B with its scale), "One KV cache, three states" (byte widths; block
+         table -> kernel page addresses), AMD "native MXFP4 indexer" (FP32
+         accumulation, weighted reduction across heads; 68 B MXFP4 keys),
+         "Long context: decode context parallel" (partials merged by LSE).
+  [K3]   "Optimising Kimi K3 on AMD Instinct MI355X", section 4 "MLA" (padding
+         12 -> 16 query heads leaves the real heads' softmax unchanged; history
+         split into parallel pieces and merged).
+The pages defer the indexer formula to the DeepSeek-V3.2 article; the reading
+taken here is the lightning-indexer form
+    score(t, s) = sum_h w_h(t) * ReLU(q_h(t) . k_s),
+with k_s the dequantised key (codes x per-token scale).  MLA latents are 576-d
+(512 "nope" + 64 "rope"), V = the first 512 dims, softmax scale 1/sqrt(192).
+
+Page layout read here (structure-of-arrays inside a page of P tokens):
+  key FP8    [P x 128 E4M3][P x fp32]
+  key MXFP4  [P x 64 B E2M1 pairs][P x 4 E8M0]
+  lat BF16   [P x 576 bf16]
+  lat FP8    [P x 576 E4M3][P x fp32]
+  lat NVFP4  [P x 256 B E2M1 pairs][P x 32 E4M3 scales][P x 64 E4M3 rope]
+Logical token s of request r lives in physical page bt[r][s // P], slot s % P
+(non-paged caches: page r, slot s).  A physical row id is page * P + slot.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import codecs as C
+
+HI, DI, D_LAT, D_V = 32, 128, 576, 512
+
+
+# ---------------------------------------------------------------- dequantise
+def key_pages(pool: np.ndarray, fmt: str, P: int, pages: np.ndarray) -> np.ndarray:
+    """Dequantise whole key pages -> fp64 [len(pages)*P, 128]."""
+    pg = pool[np.asarray(pages, dtype=np.int64)]
+    n = pg.shape[0]
+    if fmt == "fp8":
+        codes = pg[:, : 128 * P].reshape(n, P, 128)
+        scale = C.f32(pg[:, 128 * P: 132 * P]).reshape(n, P)
+        vals = C.e4m3(codes) * scale[..., None]
+    elif fmt == "mxfp4":
+        codes = pg[:, : 64 * P].reshape(n, P, 64)
+        e = C.e8m0(pg[:, 64 * P: 68 * P].reshape(n, P, 4))
+        vals = C.e2m1_packed(codes) * np.repeat(e, 32, axis=-1)
+    else:
+        raise ValueError(fmt)
+    return vals.reshape(n * P, DI)
+
+
+def lat_rows(pool: np.ndarray, fmt: str, P: int, rows: np.ndarray) -> np.ndarray:
+    """Dequantise latent rows (physical ids page*P+slot) -> fp64 [m, 576]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    page, slot = rows // P, rows % P
+
+    def region(off, width):
+        cols = off + slot[:, None] * width + np.arange(width)[None, :]
+        return pool[page[:, None], cols]
+
+    if fmt == "bf16":
+        raw = region(0, 1152)
+        return C.bf16(raw.view("<u2"))
+    if fmt == "fp8":
+        codes = region(0, 576)
+        scale = C.f32(region(576 * P, 4))
+        return C.e4m3(codes) * scale
+    if fmt == "nvfp4":
+        nope = C.e2m1_packed(region(0, 256))                 # [m, 512]
+        sc = C.e4m3(region(256 * P, 32))                     # [m, 32]
+        rope = C.e4m3(region(288 * P, 64))                   # [m, 64]
+        return np.concatenate([nope * np.repeat(sc, 16, axis=-1), rope], axis=-1)
+    raise ValueError(fmt)
+
+
+def request_pages(block_table: Optional[np.ndarray], r: int, n: int, P: int) -> np.ndarray:
+    """Address translation for the scan side: logical pages 0..ceil(n/P)-1 of
+    request r -> physical page ids ([K31] "One KV cache, three states")."""
+    npg = (n + P - 1) // P
+    if block_table is None:
+        assert npg == 1, "non-paged cache holds a request in one page"
+        return np.array([r], dtype=np.int64)
+    return np.asarray(block_table[r, :npg], dtype=np.int64)
+
+
+def request_keys(pool, fmt, P, block_table, r, n) -> np.ndarray:
+    """Dequantised keys of logical tokens 0..n-1 of request r, fp64 [n, 128]."""
+    return key_pages(pool, fmt, P, request_pages(block_table, r, n, P))[:n]
+
+
+def translate(idx: np.ndarray, block_table: Optional[np.ndarray], r: int, P: int) -> np.ndarray:
+    """Selected logical indices -> physical rows page*P + slot; -1 stays -1."""
+    idx = np.asarray(idx, dtype=np.int64)
+    out = np.full(idx.shape, -1, dtype=np.int64)
+    ok = idx >= 0
+    li = idx[ok]
+    page = np.full(li.shape, r, dtype=np.int64) if block_table is None \
+        else np.asarray(block_table[r], dtype=np.int64)[li // P]
+    out[ok] = page * P + li % P
+    return out
+
+
+# ---------------------------------------------------------------- indexer
+def indexer_scores(q: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """score_s = sum_h w_h * max(0, q_h . k_s) for every key row s.
+
+    q [32,128] fp64, w [32], keys [n,128] -> [n] fp64."""
+    dots = keys @ q.T                 # [n, 32]
+    return np.maximum(dots, 0.0) @ w
+
+
+# ---------------------------------------------------------------- top-k
+def topk(scores: np.ndarray, k: int):
+    """The min(k, n) highest scores, ties to the lower index; returns the
+    selected indices in ascending order and tau, the score of the last one
+    selected (rank min(k,n) in (score desc, index asc) order)."""
+    n = scores.shape[0]
+    m = min(k, n)
+    if m == 0:
+        return np.zeros(0, dtype=np.int64), math.inf
+    order = np.lexsort((np.arange(n), -scores))
+    sel = np.sort(order[:m])
+    return sel, float(scores[order[m - 1]])
+
+
+# ---------------------------------------------------------------- sparse MLA
+def sparse_mla(q: np.ndarray, lat: np.ndarray, sm_scale: float):
+    """Exact attention of every head over the given latent rows.
+
+    q [H,576], lat [m,576] -> o [H,512], lse [H] (natural log).  No rows:
+    o = 0, lse = -inf."""
+    H = q.shape[0]
+    if lat.shape[0] == 0:
+        return np.zeros((H, D_V)), np.full(H, -math.inf)
+    logits = sm_scale * (q @ lat.T)                      # [H, m]
+    mx = logits.max(axis=1)
+    e = np.exp(logits - mx[:, None])
+    z = e.sum(axis=1)
+    o = (e @ lat[:, :D_V]) / z[:, None]
+    return o, mx + np.log(z)
+
+
+def lse_merge(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge partial results of disjoint row subsets ([K31] "Long context:
+    decode context parallel"): lse = log sum exp(lse_i),
+    o = sum exp(lse_i - lse) o_i.  Empty parts (lse = -inf) drop out."""
+    mx = np.max(lse_parts, axis=0)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    wts = np.exp(lse_parts - safe[None])
+    z = wts.sum(axis=0)
+    lse = np.where(z > 0, safe + np.log(np.where(z > 0, z, 1.0)), -math.inf)
+    o = np.einsum("sh,shd->hd", wts, o_parts) / np.where(z > 0, z, 1.0)[:, None]
+    return o, lse
+
+
+def dense_mla(q: np.ndarray, lat_all: np.ndarray, sm_scale: float):
+    """Dense MLA over every row given (no index list)."""
+    return sparse_mla(q, lat_all, sm_scale)
+
+
+# ---------------------------------------------------------------- one layer
+def dequant_q_idx(inp: dict, t: int) -> np.ndarray:
+    if inp["q_fmt"] == "bf16":
+        return C.bf16(inp["q_idx"][t])
+    return C.e4m3(inp["q_idx"][t]) * np.asarray(inp["q_idx_scale"][t], np.float64)[:, None]
+
+
+def layer(inp: dict, k: int = 2048, tokens=None, want_scores: bool = True):
+    """Run indexer -> top-k -> translation -> sparse MLA for the query rows in
+    `tokens` (default: all).  `inp` holds NumPy arrays:
+
+      P, key_fmt, lat_fmt, q_fmt, sm_scale, req_token_start [R+1],
+      tok_vis [T], block_table [R, pages] or None, key_pool, lat_pool,
+      q_idx (bf16 bits uint16 [T,32,128] or E4M3 codes), q_idx_scale [T,32],
+      w [T,32], q_mla (bf16 bits uint16 [T,H,576]).
+
+    Returns a dict with per-row lists: scores, idx (ascending), tau, rows,
+    o [H,512], lse [H]."""
+    rts = np.asarray(inp["req_token_start"], dtype=np.int64)
+    vis = np.asarray(inp["tok_vis"], dtype=np.int64)
+    T = vis.shape[0]
+    tok_req = np.searchsorted(rts, np.arange(T), side="right") - 1
+    tokens = range(T) if tokens is None else tokens
+    P, bt = inp["P"], inp["block_table"]
+    out = {"t": [], "scores": [], "idx": [], "tau": [], "rows": [], "o": [], "lse": []}
+    key_cache = {}
+    for t in tokens:
+        r, n = int(tok_req[t]), int(vis[t])
+        if r not in key_cache or key_cache[r].shape[0] < n:
+            key_cache.clear()
+            nmax = int(vis[rts[r]:rts[r + 1]].max())
+            key_cache[r] = request_keys(inp["key_pool"], inp["key_fmt"], P, bt, r, nmax)
+        keys = key_cache[r][:n]
+        sc = indexer_scores(dequant_q_idx(inp, t), np.asarray(inp["w"][t], np.float64), keys)
+        sel, tau = topk(sc, k)
+        rows = translate(sel, bt, r, P)
+        lat = lat_rows(inp["lat_pool"], inp["lat_fmt"], P, rows)
+        o, lse = sparse_mla(C.bf16(inp["q_mla"][t]), lat, inp["sm_scale"])
+        out["t"].append(t)
+        out["scores"].append(sc if want_scores else None)
+        out["idx"].append(sel)
+        out["tau"].append(tau)
+        out["rows"].append(rows)
+        out["o"].append(o)
+        out["lse"].append(lse)
+    return out
+
+
+def mla_on_rows(inp: dict, rows: np.ndarray, tokens=None):
+    """Sparse MLA alone, on given physical rows per query row ([T,k], -1 = none)."""
+    T = rows.shape[0]
+    tokens = range(T) if tokens is None else tokens
+    os, lses = [], []
+    for t in tokens:
+        rr = rows[t][rows[t] >= 0]
+        lat = lat_rows(inp["lat_pool"], inp["lat_fmt"], inp["P"], rr)
+        o, lse = sparse_mla(C.bf16(inp["q_mla"][t]), lat, inp["sm_scale"])
+        os.append(o)
+        lses.append(lse)
+    return np.stack(os), np.stack(lses)
