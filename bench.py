@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Benchmark one DSA layer decode step (indexer -> top-k -> sparse MLA) on one
+MI355X, on seeded synthetic caches shaped like the serving workloads.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  `value` is the algorithmic HBM throughput of the whole
+step (GB/s: bytes the method must move / measured step time, inputs resident in
+HBM); µs per step, query tokens/s and the per-stage split ride along.
+`roofline` covers the dominant kernel (timed with HIP events on the launch
+stream); `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA layer decode µs/step & achieved HBM GB/s (indexer+top-k+MLA), 64K–1M ctx"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="tp8_spec_decode_64k")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target length of the oracle sample (0 disables the CPU baseline)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, seconds, bytes_of_rows):
+    """Time the oracle, request by request, until `seconds` have elapsed."""
+    from oracle import dsa as O
+    from tests.helpers import oracle_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    inp = oracle_inputs(wl)
+    rts = wl.req_token_start.cpu().tolist()
+    done_rows, elapsed, reqs = [], 0.0, 0
+    for r in range(wl.R):
+        rows = list(range(rts[r], rts[r + 1]))
+        t0 = time.perf_counter()
+        O.layer(inp, k=wl.spec.k, tokens=rows, want_scores=False)
+        elapsed += time.perf_counter() - t0
+        done_rows += rows
+        reqs += 1
+        if elapsed >= seconds:
+            break
+    nbytes = bytes_of_rows(reqs, done_rows)
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reqs} of {wl.R} requests ({len(done_rows)} query rows), fp64 NumPy, "
+                      f"{elapsed:.2f} s; same algorithmic-byte accounting as value"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the DSA layer path here runs on a single MI355X "
+              "(no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_03_amd as dsa
+    import synth
+    from sparse_attention_03_amd import bytemodel as BM
+
+    dsa.load()
+    dev = torch.device("cuda:0")
+    spec = synth.CONFIGS[args.workload]
+    t0 = time.time()
+    wl = synth.make_workload(spec, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {spec.name} generated in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    prefill = spec.q_per_req > 64
+    step = dsa.make_step(key_pool=wl.key_pool, lat_pool=wl.lat_pool, page_size=wl.P, key_fmt=spec.key_fmt,
+                         lat_fmt=spec.lat_fmt, req_row_start=wl.req_token_start, tok_req=wl.tok_req,
+                         tok_vis=wl.tok_vis, block_table=wl.block_table, q_idx=wl.q_idx, w=wl.w,
+                         q_mla=wl.q_mla, k=spec.k, sm_scale=spec.sm_scale, q_idx_scale=wl.q_idx_scale,
+                         prefill=prefill, max_vis=spec.N, max_rows_per_req=spec.q_per_req)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    E = torch.cuda.Event
+    ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, end = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        step.indexer()
+        ev[i][1].record()
+        step.topk()
+        ev[i][2].record()
+        step.mla()
+        ev[i][3].record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    st = {n: sum(ev[i][a].elapsed_time(ev[i][b]) for i in range(K)) / K
+          for n, a, b in (("indexer", 0, 1), ("topk", 1, 2), ("mla", 2, 3))}
+
+    vis = wl.tok_vis.cpu().tolist()
+    rts = wl.req_token_start.cpu().tolist()
+    req_vis = [max(vis[rts[r]:rts[r + 1]]) for r in range(wl.R)]
+    page = 0 if spec.page == 0 else wl.P
+    B = BM.step_bytes(req_vis_max=req_vis, row_vis=vis, k=spec.k, H=spec.H, key_fmt=spec.key_fmt,
+                      lat_fmt=spec.lat_fmt, q_fmt=spec.q_fmt, page=page)
+    F = BM.step_flops(row_vis=vis, k=spec.k, H=spec.H)
+    us = ms_step * 1e3
+    value = B["total"] / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel and its roofline
+    dom = max(st, key=st.get)
+    t_dom = st[dom] * 1e-3
+    if dom == "indexer":
+        peak_f = PEAK_FP8_TFLOPS if spec.q_fmt == "fp8" else PEAK_BF16_TFLOPS
+        t_mem, t_cmp = B["indexer"] / (PEAK_HBM_GBS * 1e9), F["indexer"] / (peak_f * 1e12)
+        if t_cmp > t_mem:
+            roof = {"bound": "mfma", "achieved": F["indexer"] / t_dom / 1e12, "peak": peak_f, "unit": "TFLOP/s",
+                    "traffic": None}
+        else:
+            roof = {"bound": "hbm", "achieved": B["indexer"] / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "traffic": None}
+    elif dom == "mla":
+        t_mem, t_cmp = B["mla"] / (PEAK_HBM_GBS * 1e9), F["mla"] / (PEAK_BF16_TFLOPS * 1e12)
+        if t_cmp > t_mem:
+            roof = {"bound": "mfma", "achieved": F["mla"] / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "traffic": None}
+        else:
+            roof = {"bound": "hbm", "achieved": B["mla"] / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "traffic": None}
+    else:
+        nbytes = sum(vis) * 4
+        roof = {"bound": "hbm", "achieved": nbytes / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "traffic": None}
+    roof["kernel"] = dom
+    roof["achieved"] = round(roof["achieved"], 2)
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        def bytes_of_rows(nreq, rows):
+            b = BM.step_bytes(req_vis_max=req_vis[:nreq], row_vis=[vis[t] for t in rows], k=spec.k, H=spec.H,
+                              key_fmt=spec.key_fmt, lat_fmt=spec.lat_fmt, q_fmt=spec.q_fmt, page=page)
+            return b["total"]
+        cpu = cpu_baseline(wl, args.cpu_seconds, bytes_of_rows)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name, "requests": spec.R, "rows_per_request": spec.q_per_req,
+                   "context": spec.N, "page": spec.page, "key_fmt": spec.key_fmt, "latent_fmt": spec.lat_fmt,
+                   "index_q_fmt": spec.q_fmt, "mla_heads": spec.H, "topk": spec.k},
+        "us_per_step": round(us, 2),
+        "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
+        "alg_bytes": B["total"],
+        "step_roofline_frac": round(B["total"] / (PEAK_HBM_GBS * 1e9) / (ms_step * 1e-3), 4),
+        "literal_formula_roofline_us": round(BM.literal_formula_bytes(wl.T, spec.N, spec.k) / 8e12 * 1e6, 2),
+        "stages_us": {k2: round(v * 1e3, 2) for k2, v in st.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek-style sparse attention layer:
+ * lightning indexer -> per-row top-k -> page translation -> sparse MLA.
+ *
+ * The method (Kimi K3.1 Pro day-0 page, "Sparse attention in K3.1 Pro"):
+ * every sparse-attention layer keeps a small indexer beside MLA; 32 light
+ * heads score every earlier token of the query against a per-token FP8 index
+ * key (132 bytes with its scale), the 2,048 best tokens are kept, and MLA then
+ * runs exactly, but only over those tokens.  The indexer score reads as the
+ * DeepSeek-V3.2 form the page defers to,
+ *     score(t, s) = sum_h w_h(t) * ReLU(q_h(t) . k_s),
+ * accumulated in FP32 with a weighted reduction across heads (same page, AMD
+ * section "native MXFP4 indexer").
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE memory owned and allocated by the caller.
+ *     The library never allocates, frees or synchronises; scratch memory is a
+ *     caller-provided workspace sized by dsa_workspace_size().
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is launched and a status is returned.  There is no silent
+ *     fallback to another path.  dsa_last_error() describes the last failure
+ *     of the calling thread.
+ *   - Device-resident metadata (visible counts, block-table entries, row ids)
+ *     cannot be checked on the host.  Kernels bound every access by them: a
+ *     block-table entry outside [0, num_pages) makes its keys score -inf and
+ *     its latent rows count as absent; visible counts are clamped to max_vis.
+ *   - No global mutable state: calls are re-entrant and may run concurrently
+ *     on different streams with different buffers.
+ *
+ * Paged caches (same page, "One KV cache, three states": the engine turns the
+ * block table into kernel page addresses before each step).  A pool is a
+ * sequence of physical pages `page_bytes` apart; a page holds P = 2^p tokens,
+ * structure-of-arrays inside the page, each region starting on a 16-byte
+ * boundary:
+ *     key   FP8    [P x 128 E4M3][P x fp32 scale]                     132 B/token
+ *     key   MXFP4  [P x 64 B E2M1 pairs, low nibble first][P x 4 E8M0]  68 B/token
+ *     lat   BF16   [P x 576 bf16]                                      1152 B/token
+ *     lat   FP8    [P x 576 E4M3][P x fp32 scale]                       580 B/token
+ *     lat   NVFP4  [P x 256 B E2M1 pairs (dims 0..511)]
+ *                  [P x 32 E4M3 scales, one per 16 dims]
+ *                  [P x 64 E4M3 rope dims 512..575, unscaled]           352 B/token
+ * page_bytes may exceed P x (bytes per token): several layers' pages can share
+ * one block row.  Logical token s of request r lives in physical page
+ * block_table[r * bt_stride + (s >> p)], slot s & (P-1); with block_table ==
+ * NULL the cache is non-paged and request r owns physical page r.  A physical
+ * row id is page * P + slot.  Keys and latents of one token share page ids.
+ *
+ * Latent rows are 576-d: 512 "nope" dims followed by 64 "rope" dims; the value
+ * vector is the first 512 dims.  FP8 E4M3 is OCP E4M3FN (bias 7, max 448).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+#define DSA_INDEX_HEADS 32
+#define DSA_INDEX_DIM 128
+#define DSA_LATENT_DIM 576
+#define DSA_VALUE_DIM 512
+#define DSA_MAX_TOPK 2048
+#define DSA_MAX_HEADS 128
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or shape      */
+  DSA_ERR_UNSUPPORTED = 2, /* format or combination this build does not run   */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  DSA_ERR_HIP = 4          /* the HIP runtime reported a launch error         */
+} dsa_status;
+
+/* Cache and query formats. */
+enum { DSA_KEY_FP8 = 1, DSA_KEY_MXFP4 = 2 };
+enum { DSA_LAT_BF16 = 1, DSA_LAT_FP8 = 2, DSA_LAT_NVFP4 = 3 };
+enum { DSA_Q_BF16 = 1, DSA_Q_FP8 = 2 };
+
+/* Operation ids for dsa_workspace_size(). */
+enum { DSA_OP_INDEXER = 1, DSA_OP_TOPK = 2, DSA_OP_MLA_DECODE = 3, DSA_OP_MLA_PREFILL = 4 };
+
+/* One paged pool (index keys or latents) of one layer. */
+typedef struct dsa_cache {
+  const void* base;       /* device, 16-byte aligned: physical page 0         */
+  int64_t page_bytes;     /* stride between physical pages, multiple of 16    */
+  int32_t page_size_log2; /* p: P = 2^p tokens per page, 4 <= p <= 24         */
+  int32_t num_pages;      /* physical pages in the pool (bounds page ids)     */
+  int32_t fmt;            /* DSA_KEY_* for key pools, DSA_LAT_* for latents   */
+} dsa_cache;
+
+/* Query rows of one step, grouped by request.  Rows of request r are
+ * [req_row_start[r], req_row_start[r+1]); row t sees logical keys
+ * 0 .. tok_vis[t]-1 (speculative rows of one request see one more key each;
+ * prefill rows see their prefix plus themselves). */
+typedef struct dsa_batch {
+  int32_t num_requests;          /* R >= 1                                     */
+  int32_t num_rows;              /* T >= 1 query rows                          */
+  const int32_t* req_row_start;  /* device int32 [R+1], non-decreasing, 0..T   */
+  const int32_t* tok_req;        /* device int32 [T]: request of each row      */
+  const int32_t* tok_vis;        /* device int32 [T]: visible keys, 1..max_vis */
+  const int32_t* block_table;    /* device int32 [R, bt_stride] or NULL        */
+  int32_t bt_stride;             /* entries per block-table row                */
+  int32_t max_vis;               /* host bound on tok_vis (sizes the grid)     */
+  int32_t max_rows_per_req;      /* host bound on rows of one request          */
+} dsa_batch;
+
+/* dsa_indexer_scores -- stage 1, the lightning indexer.
+ * For every row t and visible key s < tok_vis[t]:
+ *     scores[t*ld + s] = sum_{h<32} w[t,h] * max(0, q[t,h,:] . k_s)
+ * with k_s the dequantised key (FP8: codes x per-token scale; MXFP4: E2M1 x
+ * 2^(E8M0-127) per 32 dims) and q BF16, or FP8 codes x q_scale[t,h].  Products
+ * are exact and accumulate in fp32.  Positions >= tok_vis[t] are not written.
+ * Rows of one request share each key load (speculative verify rows reuse keys,
+ * same page, AMD "native MXFP4 indexer").  BF16 q runs on BF16 MFMA; FP8 q
+ * runs on FP8 MFMA (the compute-bound prefill shape). */
+typedef struct dsa_indexer_args {
+  dsa_batch batch;
+  dsa_cache keys;                /* fmt DSA_KEY_FP8 or DSA_KEY_MXFP4           */
+  const void* q;                 /* device [T,32,128]: bf16, or E4M3 codes     */
+  int32_t q_fmt;                 /* DSA_Q_BF16 or DSA_Q_FP8                    */
+  const float* q_scale;          /* device fp32 [T,32] for FP8 q, else NULL    */
+  const float* w;                /* device fp32 [T,32] head weights            */
+  float* scores;                 /* device fp32 [T, ld]                        */
+  int64_t ld;                    /* row stride of scores, >= max_vis, %4 == 0  */
+} dsa_indexer_args;
+dsa_status dsa_indexer_scores(const dsa_indexer_args* args, hipStream_t stream);
+
+/* dsa_topk -- stage 2, per-row top-k with a deterministic tie-break.
+ * Keeps K_t = min(k, tok_vis[t]) positions of row t: the highest scores, and
+ * among equal scores the lower index (a unique set).  idx[t, 0..K_t) holds
+ * them in ascending index order, idx[t, K_t..k) = -1.  If rows != NULL the
+ * same entries are also translated to physical latent rows (page * P + slot,
+ * P = 2^page_size_log2) through batch.block_table, so attention can read them
+ * directly (same page, "Low-latency fused DSA decode path": the fused indexer
+ * emits physical KV rows).  count[t] = K_t if count != NULL.  Scores must be
+ * finite; -0.0 ranks equal to +0.0.  The result of a row does not depend on
+ * the other rows of the batch. */
+typedef struct dsa_topk_args {
+  dsa_batch batch;
+  const float* scores;           /* device fp32 [T, ld]                        */
+  int64_t ld;
+  int32_t k;                     /* 1 .. 2048                                  */
+  int32_t* idx;                  /* device int32 [T, k]                        */
+  int32_t* rows;                 /* device int32 [T, k] or NULL                */
+  int32_t page_size_log2;        /* page size of the latent pool (rows != NULL)*/
+  int32_t* count;                /* device int32 [T] or NULL                   */
+  void* workspace;               /* device, 256-byte aligned                   */
+  size_t workspace_bytes;
+} dsa_topk_args;
+dsa_status dsa_topk(const dsa_topk_args* args, hipStream_t stream);
+
+/* dsa_translate_pages -- logical selected indices -> physical rows.
+ * rows[t*k+j] = page * P + (i & (P-1)) with page = block_table[r*bt_stride +
+ * (i >> p)], r = tok_req[t], i = idx[t*k+j]; -1 (or an index outside the
+ * request's block-table row) stays -1.  Non-paged (block_table NULL): page = r. */
+dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* batch,
+                               int32_t page_size_log2, int32_t* rows, hipStream_t stream);
+
+/* sparse_mla_decode / sparse_mla_prefill -- stage 3, exact MLA over the
+ * selected rows.  For row t and head h < num_heads, over the valid entries s
+ * of rows[t, 0..k) (entries < 0 or outside the pool are skipped):
+ *     l_s = sm_scale * q[t,h,:] . c_s        (c_s the dequantised 576-d latent)
+ *     out[t,h,:] = sum_s softmax(l)_s * c_s[0:512],  lse[t,h] = log sum_s e^{l_s}
+ * A row with no valid entry gives out = 0 and lse = -inf.  Heads are padded in
+ * the kernel to a multiple of 16 (the MFMA tile; MI355X Kimi K3 page, section
+ * 4 "MLA": padding 12 -> 16 heads leaves the real heads unchanged); padded
+ * heads are never written.  Decode splits each row's list into num_splits
+ * pieces (0 = automatic) whose partial results merge by log-sum-exp (Kimi
+ * K3.1 Pro day-0 page, "Long context: decode context parallel"); prefill runs
+ * one workgroup per query row over all heads (same page, AMD "Prefill").
+ * q is BF16; products accumulate in fp32; softmax weights enter the value
+ * product as BF16. */
+typedef struct dsa_mla_args {
+  int32_t num_rows;              /* T                                           */
+  int32_t num_heads;             /* H, 1 .. 128                                 */
+  const void* q;                 /* device bf16 [T, H, 576]                     */
+  dsa_cache latents;             /* fmt DSA_LAT_*                               */
+  const int32_t* rows;           /* device int32 [T, k] physical rows           */
+  int32_t k;                     /* 1 .. 2048                                   */
+  float sm_scale;                /* softmax scale (finite, > 0)                 */
+  int32_t num_splits;            /* 0 = automatic, else 1 .. k/16 (decode)      */
+  float* out;                    /* device fp32 [T, H, 512]                     */
+  float* lse;                    /* device fp32 [T, H] or NULL                  */
+  void* workspace;               /* device, 256-byte aligned                    */
+  size_t workspace_bytes;
+} dsa_mla_args;
+dsa_status sparse_mla_decode(const dsa_mla_args* args, hipStream_t stream);
+dsa_status sparse_mla_prefill(const dsa_mla_args* args, hipStream_t stream);
+
+/* Workspace bytes an operation needs for these arguments (0 if none, or if
+ * the arguments are invalid).  `args` points to the op's argument struct. */
+size_t dsa_workspace_size(int32_t op, const void* args);
+
+const char* dsa_status_str(dsa_status status);
+const char* dsa_last_error(void);
+int32_t dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

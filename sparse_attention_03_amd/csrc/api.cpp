@@ -1,0 +1,330 @@
+// Host side of the C ABI: argument validation, workspace sizing, launch
+// planning.  Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int key_token_bytes(int fmt) { return fmt == DSA_KEY_FP8 ? 132 : fmt == DSA_KEY_MXFP4 ? 68 : 0; }
+int lat_token_bytes(int fmt) {
+  return fmt == DSA_LAT_BF16 ? 1152 : fmt == DSA_LAT_FP8 ? 580 : fmt == DSA_LAT_NVFP4 ? 352 : 0;
+}
+
+dsa_status check_cache(const dsa_cache& c, int token_bytes, const char* what) {
+  if (token_bytes == 0) return fail(DSA_ERR_UNSUPPORTED, "%s: unknown format %d", what, c.fmt);
+  if (!c.base || !aligned(c.base, 16)) return fail(DSA_ERR_INVALID_ARG, "%s: base null or not 16-byte aligned", what);
+  if (c.page_size_log2 < 4 || c.page_size_log2 > 24)
+    return fail(DSA_ERR_INVALID_ARG, "%s: page_size_log2 %d outside [4, 24]", what, c.page_size_log2);
+  if (c.num_pages < 1) return fail(DSA_ERR_INVALID_ARG, "%s: num_pages < 1", what);
+  const int64_t need = (int64_t(1) << c.page_size_log2) * token_bytes;
+  if (c.page_bytes % 16 != 0 || c.page_bytes < need)
+    return fail(DSA_ERR_INVALID_ARG, "%s: page_bytes %lld not a multiple of 16 or below %lld", what,
+                (long long)c.page_bytes, (long long)need);
+  return DSA_OK;
+}
+
+dsa_status check_batch(const dsa_batch& b, int plog2, bool need_meta) {
+  if (b.num_requests < 1 || b.num_rows < 1) return fail(DSA_ERR_INVALID_ARG, "batch: empty batch");
+  if (b.max_vis < 1 || b.max_rows_per_req < 1) return fail(DSA_ERR_INVALID_ARG, "batch: max_vis/max_rows_per_req < 1");
+  if (!b.tok_vis) return fail(DSA_ERR_INVALID_ARG, "batch: tok_vis is null");
+  if (need_meta && !b.req_row_start) return fail(DSA_ERR_INVALID_ARG, "batch: req_row_start is null");
+  if (b.block_table) {
+    const int64_t pages = ((int64_t)b.max_vis + (int64_t(1) << plog2) - 1) >> plog2;
+    if (b.bt_stride < pages)
+      return fail(DSA_ERR_INVALID_ARG, "batch: bt_stride %d below the %lld pages max_vis needs", b.bt_stride,
+                  (long long)pages);
+  } else if ((int64_t)b.max_vis > (int64_t(1) << plog2)) {
+    return fail(DSA_ERR_INVALID_ARG, "batch: non-paged cache needs page size >= max_vis");
+  }
+  return DSA_OK;
+}
+
+// ---- top-k plan
+struct TopkPlan {
+  int cand_cap, slice, nslices;
+  size_t off_hist, off_ctr, off_def, off_cand, total;
+};
+TopkPlan plan_topk(int T, int max_vis, int k) {
+  TopkPlan pl;
+  pl.cand_cap = std::min(max_vis, 8192);
+  pl.slice = 8192;
+  pl.nslices = (max_vis + pl.slice - 1) / pl.slice;
+  size_t off = 0;
+  pl.off_hist = off;
+  off = align_up(off + (size_t)T * 4096 * 4, 256);
+  pl.off_ctr = off;
+  off = align_up(off + (size_t)T * 16, 256);
+  pl.off_def = off;
+  off = align_up(off + (size_t)T * k * 4, 256);
+  pl.off_cand = off;
+  off = align_up(off + (size_t)T * pl.cand_cap * 8, 256);
+  pl.total = off;
+  return pl;
+}
+
+// ---- MLA plan
+struct MlaPlan {
+  int Hpad, ntiles, nsplit, split_len;
+  size_t off_po, off_pl, total;
+};
+MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
+  MlaPlan pl;
+  pl.Hpad = (a.num_heads + 15) / 16 * 16;
+  pl.ntiles = pl.Hpad / 16;
+  int want;
+  if (prefill) {
+    want = 1;
+  } else if (a.num_splits > 0) {
+    want = a.num_splits;
+  } else {
+    const int64_t waves = (int64_t)a.num_rows * pl.ntiles;
+    want = (int)std::min<int64_t>(16, std::max<int64_t>(1, (2048 + waves - 1) / waves));
+  }
+  want = std::max(1, std::min(want, (a.k + 31) / 32));
+  pl.split_len = ((a.k + want - 1) / want + 31) / 32 * 32;
+  pl.nsplit = (a.k + pl.split_len - 1) / pl.split_len;
+  size_t off = 0;
+  pl.off_po = 0;
+  pl.off_pl = 0;
+  if (pl.nsplit > 1) {
+    off = align_up((size_t)a.num_rows * pl.nsplit * a.num_heads * 512 * 4, 256);
+    pl.off_pl = off;
+    off = align_up(off + (size_t)a.num_rows * pl.nsplit * a.num_heads * 4, 256);
+  }
+  pl.total = off;
+  return pl;
+}
+
+dsa_status check_mla(const dsa_mla_args* a) {
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "mla: null args");
+  if (a->num_rows < 1) return fail(DSA_ERR_INVALID_ARG, "mla: num_rows < 1");
+  if (a->num_heads < 1 || a->num_heads > DSA_MAX_HEADS) return fail(DSA_ERR_INVALID_ARG, "mla: num_heads %d", a->num_heads);
+  if (a->k < 1 || a->k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "mla: k %d outside [1, 2048]", a->k);
+  if (!a->q || !aligned(a->q, 16)) return fail(DSA_ERR_INVALID_ARG, "mla: q null or not 16-byte aligned");
+  if (!a->rows) return fail(DSA_ERR_INVALID_ARG, "mla: rows is null");
+  if (!a->out || !aligned(a->out, 16)) return fail(DSA_ERR_INVALID_ARG, "mla: out null or not 16-byte aligned");
+  if (!(std::isfinite(a->sm_scale) && a->sm_scale > 0.f)) return fail(DSA_ERR_INVALID_ARG, "mla: sm_scale");
+  if (a->num_splits < 0 || a->num_splits > DSA_MAX_TOPK / 16) return fail(DSA_ERR_INVALID_ARG, "mla: num_splits");
+  return check_cache(a->latents, lat_token_bytes(a->latents.fmt), "mla latents");
+}
+
+dsa_status run_mla(const dsa_mla_args* a, hipStream_t stream, bool prefill) {
+  dsa_status st = check_mla(a);
+  if (st != DSA_OK) return st;
+  const MlaPlan pl = plan_mla(*a, prefill);
+  if (pl.total > 0) {
+    if (!a->workspace || !aligned(a->workspace, 256))
+      return fail(DSA_ERR_WORKSPACE, "mla: workspace null or not 256-byte aligned (%zu bytes needed)", pl.total);
+    if (a->workspace_bytes < pl.total)
+      return fail(DSA_ERR_WORKSPACE, "mla: workspace %zu bytes, %zu needed", a->workspace_bytes, pl.total);
+  }
+  dsa::MlaParams p{};
+  p.T = a->num_rows;
+  p.H = a->num_heads;
+  p.Hpad = pl.Hpad;
+  p.ntiles = pl.ntiles;
+  p.q = static_cast<const __bf16*>(a->q);
+  p.lat = static_cast<const uint8_t*>(a->latents.base);
+  p.page_bytes = a->latents.page_bytes;
+  p.plog2 = a->latents.page_size_log2;
+  p.num_pages = a->latents.num_pages;
+  p.fmt = a->latents.fmt;
+  p.rows = a->rows;
+  p.k = a->k;
+  p.sm_log2 = a->sm_scale * 1.4426950408889634f;
+  p.nsplit = pl.nsplit;
+  p.split_len = pl.split_len;
+  p.out = a->out;
+  p.lse = a->lse;
+  char* ws = static_cast<char*>(a->workspace);
+  p.part_o = pl.nsplit > 1 ? reinterpret_cast<float*>(ws + pl.off_po) : nullptr;
+  p.part_lse = pl.nsplit > 1 ? reinterpret_cast<float*>(ws + pl.off_pl) : nullptr;
+  st = dsa::launch_mla(p, stream);
+  if (st != DSA_OK) return fail(st, "mla: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return g_err; }
+
+const char* dsa_status_str(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "indexer: null args");
+  dsa_status st = check_cache(a->keys, key_token_bytes(a->keys.fmt), "indexer keys");
+  if (st != DSA_OK) return st;
+  st = check_batch(a->batch, a->keys.page_size_log2, true);
+  if (st != DSA_OK) return st;
+  if (!a->q || !aligned(a->q, 16)) return fail(DSA_ERR_INVALID_ARG, "indexer: q null or not 16-byte aligned");
+  if (!a->w || !aligned(a->w, 16)) return fail(DSA_ERR_INVALID_ARG, "indexer: w null or not 16-byte aligned");
+  if (!a->scores || !aligned(a->scores, 16)) return fail(DSA_ERR_INVALID_ARG, "indexer: scores null or not 16-byte aligned");
+  if (a->ld < a->batch.max_vis || a->ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "indexer: ld %lld", (long long)a->ld);
+  if (a->batch.num_requests > 65535) return fail(DSA_ERR_INVALID_ARG, "indexer: more than 65535 requests");
+  if (a->q_fmt != DSA_Q_BF16 && a->q_fmt != DSA_Q_FP8) return fail(DSA_ERR_UNSUPPORTED, "indexer: q_fmt %d", a->q_fmt);
+  if (a->q_fmt == DSA_Q_FP8 && !a->q_scale) return fail(DSA_ERR_INVALID_ARG, "indexer: FP8 q needs q_scale");
+
+  dsa::IndexerParams p{};
+  const dsa_batch& b = a->batch;
+  p.R = b.num_requests;
+  p.T = b.num_rows;
+  p.req_row_start = b.req_row_start;
+  p.tok_req = b.tok_req;
+  p.tok_vis = b.tok_vis;
+  p.block_table = b.block_table;
+  p.bt_stride = b.bt_stride;
+  p.max_vis = b.max_vis;
+  p.keys = static_cast<const uint8_t*>(a->keys.base);
+  p.page_bytes = a->keys.page_bytes;
+  p.plog2 = a->keys.page_size_log2;
+  p.num_pages = a->keys.num_pages;
+  p.key_fmt = a->keys.fmt;
+  p.w = a->w;
+  p.scores = a->scores;
+  p.ld = a->ld;
+  if (a->q_fmt == DSA_Q_BF16) {
+    p.q = static_cast<const __bf16*>(a->q);
+    // keys per workgroup: enough workgroups to fill 256 CUs, at most 4096 keys
+    int64_t target = (int64_t)b.max_vis * b.num_requests / 2048;
+    int chunk = 256;
+    while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
+    p.chunk = chunk;
+    p.qrows = std::min(b.max_rows_per_req, 6);
+    st = dsa::launch_indexer_bf16(p, stream);
+  } else {
+    if (a->keys.fmt != DSA_KEY_FP8) return fail(DSA_ERR_UNSUPPORTED, "indexer: FP8 q runs against FP8 keys only");
+    p.q8 = static_cast<const uint8_t*>(a->q);
+    p.q_scale = a->q_scale;
+    st = dsa::launch_indexer_fp8(p, stream);
+  }
+  if (st != DSA_OK) return fail(st, "indexer: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
+dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "topk: null args");
+  const dsa_batch& b = a->batch;
+  if (a->k < 1 || a->k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "topk: k %d outside [1, 2048]", a->k);
+  if (b.num_rows < 1 || b.max_vis < 1 || !b.tok_vis) return fail(DSA_ERR_INVALID_ARG, "topk: bad batch");
+  if (!a->scores || !aligned(a->scores, 16)) return fail(DSA_ERR_INVALID_ARG, "topk: scores null or not 16-byte aligned");
+  if (a->ld < b.max_vis || a->ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "topk: ld %lld", (long long)a->ld);
+  if (!a->idx) return fail(DSA_ERR_INVALID_ARG, "topk: idx is null");
+  if (a->rows) {
+    if (a->page_size_log2 < 4 || a->page_size_log2 > 24) return fail(DSA_ERR_INVALID_ARG, "topk: page_size_log2");
+    if (!b.tok_req) return fail(DSA_ERR_INVALID_ARG, "topk: rows need tok_req");
+    dsa_status st = check_batch(b, a->page_size_log2, false);
+    if (st != DSA_OK) return st;
+  }
+  if (b.num_rows > 65535 * 64) return fail(DSA_ERR_INVALID_ARG, "topk: too many rows");
+  const TopkPlan pl = plan_topk(b.num_rows, b.max_vis, a->k);
+  if (!a->workspace || !aligned(a->workspace, 256))
+    return fail(DSA_ERR_WORKSPACE, "topk: workspace null or not 256-byte aligned (%zu bytes needed)", pl.total);
+  if (a->workspace_bytes < pl.total)
+    return fail(DSA_ERR_WORKSPACE, "topk: workspace %zu bytes, %zu needed", a->workspace_bytes, pl.total);
+  dsa::TopkParams p{};
+  p.T = b.num_rows;
+  p.scores = a->scores;
+  p.ld = a->ld;
+  p.tok_vis = b.tok_vis;
+  p.tok_req = b.tok_req;
+  p.max_vis = b.max_vis;
+  p.k = a->k;
+  p.block_table = b.block_table;
+  p.bt_stride = b.bt_stride;
+  p.plog2 = a->page_size_log2;
+  p.idx = a->idx;
+  p.rows = a->rows;
+  p.count = a->count;
+  char* ws = static_cast<char*>(a->workspace);
+  p.hist = reinterpret_cast<uint32_t*>(ws + pl.off_hist);
+  p.ctr = reinterpret_cast<uint32_t*>(ws + pl.off_ctr);
+  p.defbuf = reinterpret_cast<int32_t*>(ws + pl.off_def);
+  p.cand = reinterpret_cast<uint32_t*>(ws + pl.off_cand);
+  p.cand_cap = pl.cand_cap;
+  p.slice = pl.slice;
+  p.nslices = pl.nslices;
+  dsa_status st = dsa::launch_topk(p, stream);
+  if (st != DSA_OK) return fail(st, "topk: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
+dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* b, int32_t page_size_log2,
+                               int32_t* rows, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!idx || !rows || !b) return fail(DSA_ERR_INVALID_ARG, "translate: null pointer");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "translate: k %d", k);
+  if (b->num_rows < 1 || !b->tok_req) return fail(DSA_ERR_INVALID_ARG, "translate: bad batch");
+  if (page_size_log2 < 4 || page_size_log2 > 24) return fail(DSA_ERR_INVALID_ARG, "translate: page_size_log2");
+  if (b->block_table && b->bt_stride < 1) return fail(DSA_ERR_INVALID_ARG, "translate: bt_stride");
+  dsa_status st = dsa::launch_translate(idx, k, b->num_rows, b->tok_req, b->block_table, b->bt_stride,
+                                        page_size_log2, rows, stream);
+  if (st != DSA_OK) return fail(st, "translate: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
+dsa_status sparse_mla_decode(const dsa_mla_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  return run_mla(a, stream, false);
+}
+
+dsa_status sparse_mla_prefill(const dsa_mla_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  return run_mla(a, stream, true);
+}
+
+size_t dsa_workspace_size(int32_t op, const void* args) {
+  if (!args) return 0;
+  switch (op) {
+    case DSA_OP_INDEXER: return 0;
+    case DSA_OP_TOPK: {
+      const dsa_topk_args* a = static_cast<const dsa_topk_args*>(args);
+      if (a->k < 1 || a->k > DSA_MAX_TOPK || a->batch.num_rows < 1 || a->batch.max_vis < 1) return 0;
+      return plan_topk(a->batch.num_rows, a->batch.max_vis, a->k).total;
+    }
+    case DSA_OP_MLA_DECODE:
+    case DSA_OP_MLA_PREFILL: {
+      const dsa_mla_args* a = static_cast<const dsa_mla_args*>(args);
+      if (a->k < 1 || a->k > DSA_MAX_TOPK || a->num_rows < 1 || a->num_heads < 1 || a->num_splits < 0) return 0;
+      return plan_mla(*a, op == DSA_OP_MLA_PREFILL).total;
+    }
+  }
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// Shared device helpers for the gfx950 DSA kernels: MFMA wrappers, in-register
+// dequantisation of the cache formats, and paged-cache addressing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+constexpr int kWave = 64;
+constexpr int kIdxHeads = DSA_INDEX_HEADS;  // 32
+constexpr int kIdxDim = DSA_INDEX_DIM;      // 128
+constexpr int kLatDim = DSA_LATENT_DIM;     // 576
+constexpr int kValDim = DSA_VALUE_DIM;      // 512
+
+// ---------------------------------------------------------------- MFMA
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.  Lane l
+// supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16]; it receives
+// D[4*(l/16) + i][l%16], i < 4.  The order in which the 32 k-values are
+// assigned to (lane group, slot) is free as long as A and B agree.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x128) * B(128x16) with FP8 E4M3 inputs (unit block scales).
+// Lane l supplies 32 consecutive k-values A[l%16][32*(l/16) .. +32) and
+// B[32*(l/16) .. +32)[l%16]; D layout as above.
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  // cbsz = blgp = 0 selects FP8 E4M3 for both operands; E8M0 scale 127 = 1.0.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------- dequant
+// Two E4M3 values (bytes 0,1 or 2,3 of `w`) -> two bf16.  E4M3 has a 3-bit
+// mantissa and exponents 2^-9 .. 2^8, so the conversion is exact.
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+}
+
+// Four E4M3 bytes of `w` -> four bf16 packed in two dwords.
+__device__ __forceinline__ i32x2 e4m3x4_to_bf16(uint32_t w) {
+  bf16x2 lo = e4m3x2_to_bf16(w, false);
+  bf16x2 hi = e4m3x2_to_bf16(w, true);
+  i32x2 r;
+  r[0] = __builtin_bit_cast(int, lo);
+  r[1] = __builtin_bit_cast(int, hi);
+  return r;
+}
+
+// Eight E4M3 bytes -> one bf16x8 MFMA fragment.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  i32x2 a = e4m3x4_to_bf16(w0), b = e4m3x4_to_bf16(w1);
+  i32x4 r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Eight E2M1 codes (one dword, low nibble first) x a power-of-two scale ->
+// bf16x8.  The scaled convert applies only the exponent of its scale operand,
+// which is exact for E8M0 (MXFP4) scales.
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t w, float pow2_scale) {
+  i32x4 r;
+  r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, pow2_scale, 0));
+  r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, pow2_scale, 1));
+  r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, pow2_scale, 2));
+  r[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, pow2_scale, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// fp32 pair -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight E2M1 codes x an arbitrary (E4M3-valued) block scale -> bf16x8.  The
+// product of a 2-significant-bit E2M1 value and a 4-significant-bit E4M3 value
+// has at most 6 significant bits, so the fp32 product rounds to bf16 exactly.
+__device__ __forceinline__ bf16x8 e2m1x8_times(uint32_t w, float scale) {
+  i32x4 r;
+#define DSA_E2M1_PAIR(b)                                                          \
+  {                                                                               \
+    const bf16x2 v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, 1.0f, b); \
+    r[b] = (int)pack_bf16x2((float)v[0] * scale, (float)v[1] * scale);            \
+  }
+  DSA_E2M1_PAIR(0) DSA_E2M1_PAIR(1) DSA_E2M1_PAIR(2) DSA_E2M1_PAIR(3)
+#undef DSA_E2M1_PAIR
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// E8M0 code -> fp32 power of two 2^(code-127) (code 0 -> 2^-127, subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+  return code == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23);
+}
+
+// E4M3 code -> fp32 (exact); used for NVFP4 block scales.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  bf16x2 v = e4m3x2_to_bf16(code & 0xFFu, false);
+  return (float)v[0];
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ i32x4 ld16(const void* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+__device__ __forceinline__ i32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+
+// ---------------------------------------------------------------- paging
+// Physical page of logical page `lp` of request `r`, or -1 when the
+// block-table entry is outside the pool.
+__device__ __forceinline__ int phys_page(const int32_t* __restrict__ bt, int bt_stride, int r, int lp,
+                                         int num_pages) {
+  int pg = bt ? bt[(int64_t)r * bt_stride + lp] : r;
+  return (pg >= 0 && pg < num_pages) ? pg : -1;
+}
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key); -0.0 is
+// mapped as +0.0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_sum_xor_16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+}  // namespace dsa

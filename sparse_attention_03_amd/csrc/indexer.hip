@@ -1,0 +1,158 @@
+// Lightning indexer, decode shape: BF16 queries against FP8 or MXFP4 paged keys.
+//
+//   score(t, s) = sum_{h<32} w[t,h] * max(0, q[t,h,:] . k_s)
+//
+// (Kimi K3.1 Pro day-0 page, "Sparse attention in K3.1 Pro": 32 light heads
+// score every earlier token against a 132-byte FP8 key; AMD section "native
+// MXFP4 indexer": FP32 accumulation, weighted reduction across heads, keys
+// reused across the speculative query rows of a request.)
+//
+// Work split: one workgroup = one request x one chunk of keys.  The rows of
+// the request (q, 8 KiB each as bf16) are staged once in LDS; each wave streams
+// its share of the chunk's keys with 16-byte loads straight into MFMA
+// B-fragments (dequantised in registers, exactly, to bf16), and runs every row
+// against them on v_mfma_f32_16x16x32_bf16.  Keys are therefore read from HBM
+// once per request whatever the number of rows.
+//
+// Fragment layout (16 keys x 32 heads per MFMA pair): lane l = 16*g + c holds
+// key c of the tile and, for k-step kk (0..3), dims 32g + 8kk .. +7.  The A
+// operand (q) uses the same dim assignment for head c (+16 for the second
+// head tile), so the k-sum is the full 128-dim dot product.  The result lane
+// (g, c) holds heads 4g+i (i<4) for key c; the ReLU-weighted head sum is done
+// in-lane and across the four lane groups with two xor shuffles.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+constexpr int kIdxWaves = 4;
+constexpr int kIdxKT = 4;              // 16-key tiles per wave per round
+constexpr int kIdxRound = kIdxWaves * kIdxKT * 16;  // 256 keys per round
+constexpr int kQPad = 136;             // bf16 per head row in LDS (272 B: conflict-free reads)
+
+template <int KFMT>
+__global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
+  extern __shared__ __attribute__((aligned(16))) __bf16 qs[];  // [rows][32][kQPad]
+  __shared__ int s_vmax[kIdxWaves];
+
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int rs = p.req_row_start[r], re = p.req_row_start[r + 1];
+
+  // largest visible count among the request's rows
+  int vm = 0;
+  for (int t = rs + tid; t < re; t += 256) vm = max(vm, p.tok_vis[t]);
+  for (int o = 32; o > 0; o >>= 1) vm = max(vm, __shfl_xor(vm, o));
+  if (lane == 0) s_vmax[wave] = vm;
+  __syncthreads();
+  int vmax = max(max(s_vmax[0], s_vmax[1]), max(s_vmax[2], s_vmax[3]));
+  vmax = min(vmax, p.max_vis);
+  const int k0 = blockIdx.x * p.chunk;
+  if (k0 >= vmax) return;
+  const int kend = min(k0 + p.chunk, vmax);
+  const int P = 1 << p.plog2;
+  const int code_bytes = (KFMT == DSA_KEY_FP8) ? 128 : 64;
+
+  for (int t0 = rs; t0 < re; t0 += p.qrows) {
+    const int nr = min(p.qrows, re - t0);
+    __syncthreads();
+    for (int i = tid; i < nr * 512; i += 256) {
+      const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
+      i32x4 v = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
+      *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = v;
+    }
+    __syncthreads();
+
+    for (int base = k0; base < kend; base += kIdxRound) {
+      bf16x8 bfr[kIdxKT][4];
+      float ksc[kIdxKT];
+      int s0v[kIdxKT];
+#pragma unroll
+      for (int kt = 0; kt < kIdxKT; ++kt) {
+        const int s0 = base + (wave * kIdxKT + kt) * 16;
+        s0v[kt] = s0;
+        ksc[kt] = 0.f;
+        int pg = -1;
+        if (s0 < kend) pg = phys_page(p.block_table, p.bt_stride, r, s0 >> p.plog2, p.num_pages);
+        if (pg >= 0) {
+          const uint8_t* page = p.keys + (int64_t)pg * p.page_bytes;
+          const int slot = (s0 & (P - 1)) + c;
+          if (KFMT == DSA_KEY_FP8) {
+            const uint8_t* kp = page + slot * 128 + 32 * g;
+            i32x4 a = ld16_stream(kp), b = ld16_stream(kp + 16);
+            ksc[kt] = *reinterpret_cast<const float*>(page + P * 128 + slot * 4);
+            bfr[kt][0] = e4m3x8_to_bf16x8(a[0], a[1]);
+            bfr[kt][1] = e4m3x8_to_bf16x8(a[2], a[3]);
+            bfr[kt][2] = e4m3x8_to_bf16x8(b[0], b[1]);
+            bfr[kt][3] = e4m3x8_to_bf16x8(b[2], b[3]);
+          } else {
+            const uint8_t* kp = page + slot * 64 + 16 * g;
+            i32x4 a = ld16_stream(kp);
+            const float sc = e8m0_to_f32(page[P * 64 + slot * 4 + g]);
+            ksc[kt] = 1.f;
+            bfr[kt][0] = e2m1x8_to_bf16x8(a[0], sc);
+            bfr[kt][1] = e2m1x8_to_bf16x8(a[1], sc);
+            bfr[kt][2] = e2m1x8_to_bf16x8(a[2], sc);
+            bfr[kt][3] = e2m1x8_to_bf16x8(a[3], sc);
+          }
+        } else {
+          ksc[kt] = -__builtin_inff();  // absent page: never selected
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) bfr[kt][kk] = bf16x8{};
+        }
+      }
+      (void)code_bytes;
+
+      for (int j = 0; j < nr; ++j) {
+        const int t = t0 + j;
+        const int vis = min(p.tok_vis[t], p.max_vis);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
+        f32x4 acc[kIdxKT][2];
+#pragma unroll
+        for (int kt = 0; kt < kIdxKT; ++kt) acc[kt][0] = acc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const __bf16* qrow = &qs[(j * 32) * kQPad];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qrow[c * kQPad + 32 * g + 8 * kk]);
+          const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qrow[(16 + c) * kQPad + 32 * g + 8 * kk]);
+#pragma unroll
+          for (int kt = 0; kt < kIdxKT; ++kt) {
+            acc[kt][0] = mfma16x16x32(a0, bfr[kt][kk], acc[kt][0]);
+            acc[kt][1] = mfma16x16x32(a1, bfr[kt][kk], acc[kt][1]);
+          }
+        }
+        float* srow = p.scores + (int64_t)t * p.ld;
+#pragma unroll
+        for (int kt = 0; kt < kIdxKT; ++kt) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v += w0[i] * fmaxf(acc[kt][0][i], 0.f);
+            v += w1[i] * fmaxf(acc[kt][1][i], 0.f);
+          }
+          v = wave_sum_xor_16_32(v);
+          const int s = s0v[kt] + c;
+          if (g == (kt & 3) && s < vis && s0v[kt] < kend) {
+            const float ks = ksc[kt];
+            srow[s] = (ks == -__builtin_inff()) ? ks : v * ks;
+          }
+        }
+      }
+    }
+  }
+}
+
+dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
+  dim3 grid((p.max_vis + p.chunk - 1) / p.chunk, p.R);
+  const size_t lds = (size_t)p.qrows * 32 * kQPad * sizeof(__bf16);
+  if (p.key_fmt == DSA_KEY_FP8)
+    hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_FP8>, grid, dim3(256), lds, stream, p);
+  else
+    hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_MXFP4>, grid, dim3(256), lds, stream, p);
+  return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+}  // namespace dsa

@@ -1,0 +1,87 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+struct IndexerParams {
+  int R, T;
+  const int32_t* req_row_start;
+  const int32_t* tok_req;
+  const int32_t* tok_vis;
+  const int32_t* block_table;
+  int bt_stride;
+  int max_vis;
+  // key pool
+  const uint8_t* keys;
+  int64_t page_bytes;
+  int plog2;
+  int num_pages;
+  int key_fmt;
+  // queries
+  const __bf16* q;          // bf16 q (BF16 path)
+  const uint8_t* q8;        // E4M3 q (FP8 path)
+  const float* q_scale;     // [T,32] (FP8 path)
+  const float* w;           // [T,32]
+  float* scores;
+  int64_t ld;
+  int chunk;                // keys per workgroup (BF16 path)
+  int qrows;                // rows staged in LDS per pass (BF16 path)
+};
+
+struct TopkParams {
+  int T;
+  const float* scores;
+  int64_t ld;
+  const int32_t* tok_vis;
+  const int32_t* tok_req;
+  int max_vis;
+  int k;
+  const int32_t* block_table;
+  int bt_stride;
+  int plog2;
+  int32_t* idx;
+  int32_t* rows;
+  int32_t* count;
+  // workspace
+  uint32_t* hist;       // [T][4096]
+  uint32_t* ctr;        // [T][4]: n_def, n_cand, threshold bin, need
+  int32_t* defbuf;      // [T][k]
+  uint32_t* cand;       // [T][cand_cap][2]: order key, index
+  int cand_cap;
+  int slice;            // scores per workgroup in the histogram / filter passes
+  int nslices;
+};
+
+struct MlaParams {
+  int T, H, Hpad, ntiles;
+  const __bf16* q;
+  const uint8_t* lat;
+  int64_t page_bytes;
+  int plog2;
+  int num_pages;
+  int fmt;
+  const int32_t* rows;
+  int k;
+  float sm_log2;            // sm_scale * log2(e)
+  int nsplit;
+  int split_len;            // list entries per split (multiple of 32)
+  float* out;
+  float* lse;
+  float* part_o;            // [T][nsplit][H][512]
+  float* part_lse;          // [T][nsplit][H]
+};
+
+dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream);
+dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream);
+dsa_status launch_topk(const TopkParams& p, hipStream_t stream);
+dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req,
+                            const int32_t* block_table, int bt_stride, int plog2, int32_t* rows,
+                            hipStream_t stream);
+dsa_status launch_mla(const MlaParams& p, hipStream_t stream);
+
+}  // namespace dsa

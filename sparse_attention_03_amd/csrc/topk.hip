@@ -1,0 +1,332 @@
+// Per-row top-k with a lower-index tie-break, and block-table translation.
+//
+// Kimi K3.1 Pro day-0 page: "Sparse attention in K3.1 Pro" keeps the 2,048
+// best-scored tokens per query; "Exact top-k merge" selects by radix select;
+// AMD "Communication" asks for a consistent tie-break rule.  The set kept for
+// row t is unique: the K = min(k, vis) largest scores, equal scores ordered by
+// ascending index.  It is emitted in ascending index order.
+//
+// Three passes over the scores of a row, each spread over many workgroups:
+//   1. histogram of the top 12 bits of the order-preserving uint32 key;
+//   2. threshold bin b from the histogram; every slice appends keys above b
+//      ("definite", fewer than K in total) and keys inside b ("candidates")
+//      to per-row buffers with one atomic per wave;
+//   3. one workgroup per row refines the candidates with an exact radix
+//      select on the 56-bit composite (low 20 key bits, then inverted index),
+//      so ties resolve to the lower index, then sorts the K winners by index
+//      (bitonic, in LDS) and writes indices, physical rows and the count.
+// If a row's candidates overflow their buffer, pass 3 reads the candidates
+// straight from the score row instead (slower, same result).
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+constexpr int kBins = 4096;
+constexpr int kBinShift = 20;
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__device__ __forceinline__ int row_vis(const TopkParams& p, int t) {
+  return min(max(p.tok_vis[t], 0), p.max_vis);
+}
+
+__global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
+  __shared__ uint32_t h[kBins];
+  const int t = blockIdx.y;
+  const int vis = row_vis(p, t);
+  if (vis <= p.k) return;
+  const int s_begin = blockIdx.x * p.slice;
+  if (s_begin >= vis) return;
+  const int s_end = min(s_begin + p.slice, vis);
+  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
+  __syncthreads();
+  const float* row = p.scores + (int64_t)t * p.ld;
+  for (int s = s_begin + 4 * threadIdx.x; s < s_end; s += 1024) {
+    if (s + 3 < s_end) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&h[order_key(v[e]) >> kBinShift], 1u);
+    } else {
+      for (int e = 0; s + e < s_end; ++e) atomicAdd(&h[order_key(row[s + e]) >> kBinShift], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = p.hist + (int64_t)t * kBins;
+  for (int i = threadIdx.x; i < kBins; i += 256)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// Threshold bin of row t from its global histogram: the bin b with
+// count(bins > b) < k <= count(bins >= b).  Returns b and need = k - count(> b).
+// Must be called by all 256 threads of the block.
+__device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int k, int* out_bin, int* out_need) {
+  __shared__ uint32_t part[256];
+  __shared__ int s_bin, s_need;
+  const int tid = threadIdx.x;
+  uint32_t loc[16];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    loc[i] = gh[tid * 16 + i];
+    sum += loc[i];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  // inclusive suffix scan over threads (higher thread = higher bins)
+  for (int off = 1; off < 256; off <<= 1) {
+    uint32_t v = (tid + off < 256) ? part[tid + off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const uint32_t above = part[tid] - sum;  // bins owned by higher threads
+  if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
+    uint32_t acc = above;
+    for (int i = 15; i >= 0; --i) {
+      if (acc + loc[i] >= (uint32_t)k) {
+        s_bin = tid * 16 + i;
+        s_need = k - (int)acc;
+        break;
+      }
+      acc += loc[i];
+    }
+  }
+  __syncthreads();
+  *out_bin = s_bin;
+  *out_need = s_need;
+}
+
+// Append this lane's element (if pred) to buf at a position reserved with one
+// atomic per wave.  Returns the position or -1.
+__device__ __forceinline__ int wave_append(bool pred, uint32_t* counter) {
+  const uint64_t mask = __ballot(pred);
+  if (mask == 0) return -1;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)mask) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+  base = __shfl(base, leader);
+  if (!pred) return -1;
+  return (int)(base + __popcll(mask & ((1ull << lane) - 1ull)));
+}
+
+__global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
+  const int t = blockIdx.y;
+  const int vis = row_vis(p, t);
+  if (vis <= p.k) return;
+  const int s_begin = blockIdx.x * p.slice;
+  if (s_begin >= vis) return;
+  const int s_end = min(s_begin + p.slice, vis);
+  int bin, need;
+  find_threshold_bin(p.hist + (int64_t)t * kBins, p.k, &bin, &need);
+  uint32_t* ctr = p.ctr + (int64_t)t * 4;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ctr[2] = (uint32_t)bin;
+    ctr[3] = (uint32_t)need;
+  }
+  const float* row = p.scores + (int64_t)t * p.ld;
+  int32_t* defrow = p.defbuf + (int64_t)t * p.k;
+  uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
+  // every lane of a wave runs the same trip count so the ballots line up
+  for (int s0 = s_begin; s0 < s_end; s0 += 1024) {
+    const int s = s0 + 4 * threadIdx.x;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (s + 3 < s_end) {
+      v = *reinterpret_cast<const f32x4*>(row + s);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (s + e < s_end) v[e] = row[s + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = s + e < s_end;
+      const uint32_t key = order_key(v[e]);
+      const int d = (int)(key >> kBinShift);
+      const int pd = wave_append(in && d > bin, &ctr[0]);
+      if (pd >= 0 && pd < p.k) defrow[pd] = s + e;
+      const int pc = wave_append(in && d == bin, &ctr[1]);
+      if (pc >= 0 && pc < p.cand_cap) {
+        candrow[2 * pc] = key;
+        candrow[2 * pc + 1] = (uint32_t)(s + e);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
+  return ((uint64_t)(key & 0xFFFFFu) << 36) | ((uint64_t)(0xFFFFFFFFu - idx) << 4);
+}
+
+__device__ __forceinline__ int translate_one(int li, int r, const int32_t* __restrict__ bt, int bt_stride,
+                                             int plog2) {
+  if (li < 0) return -1;
+  const int lp = li >> plog2;
+  int pg;
+  if (bt) {
+    if (lp >= bt_stride) return -1;
+    pg = bt[(int64_t)r * bt_stride + lp];
+  } else {
+    pg = r;
+  }
+  if (pg < 0) return -1;
+  return (pg << plog2) | (li & ((1 << plog2) - 1));
+}
+
+__global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
+  __shared__ int out[DSA_MAX_TOPK];
+  __shared__ uint32_t h[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_need, s_done, s_cnt;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int vis = row_vis(p, t);
+  const int K = min(p.k, vis);
+  const int r = p.tok_req ? p.tok_req[t] : 0;
+  int32_t* idx = p.idx + (int64_t)t * p.k;
+  int32_t* rows = p.rows ? p.rows + (int64_t)t * p.k : nullptr;
+
+  if (vis <= p.k) {
+    for (int j = tid; j < p.k; j += blockDim.x) {
+      const int li = j < vis ? j : -1;
+      idx[j] = li;
+      if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+    }
+    if (p.count && tid == 0) p.count[t] = K;
+    return;
+  }
+
+  const uint32_t* ctr = p.ctr + (int64_t)t * 4;
+  const int ndef = (int)ctr[0];
+  const int ncand = (int)ctr[1];
+  const uint32_t bin = ctr[2];
+  const bool from_buf = ncand <= p.cand_cap;
+  const uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
+  const float* srow = p.scores + (int64_t)t * p.ld;
+  const int nsrc = from_buf ? ncand : vis;
+
+  if (tid == 0) {
+    s_prefix = 0;
+    s_need = (int)ctr[3];
+    s_done = 0;
+  }
+  int shift = 48;
+  for (;; shift -= 8) {
+    for (int i = tid; i < 256; i += blockDim.x) h[i] = 0;
+    __syncthreads();
+    const uint64_t prefix = s_prefix;
+    for (int i = tid; i < nsrc; i += blockDim.x) {
+      uint32_t key, li;
+      if (from_buf) {
+        key = candrow[2 * i];
+        li = candrow[2 * i + 1];
+      } else {
+        key = order_key(srow[i]);
+        li = (uint32_t)i;
+        if ((key >> kBinShift) != bin) continue;
+      }
+      const uint64_t v = composite(key, li);
+      if ((v >> (shift + 8)) == prefix) atomicAdd(&h[(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int need = s_need;
+      uint32_t acc = 0;
+      int sel = 0;
+      for (int b = 255; b >= 0; --b) {
+        if (acc + h[b] >= (uint32_t)need) {
+          sel = b;
+          break;
+        }
+        acc += h[b];
+      }
+      need -= (int)acc;
+      s_need = need;
+      s_prefix = (prefix << 8) | (uint64_t)sel;
+      s_done = (h[sel] == (uint32_t)need) || shift == 0;
+    }
+    __syncthreads();
+    if (s_done) break;
+  }
+  const uint64_t thr = s_prefix;
+
+  // winners: definite entries, then candidates at or above the threshold
+  for (int i = tid; i < ndef; i += blockDim.x) out[i] = p.defbuf[(int64_t)t * p.k + i];
+  if (tid == 0) s_cnt = ndef;
+  __syncthreads();
+  for (int i = tid; i < nsrc; i += blockDim.x) {
+    uint32_t key, li;
+    if (from_buf) {
+      key = candrow[2 * i];
+      li = candrow[2 * i + 1];
+    } else {
+      key = order_key(srow[i]);
+      li = (uint32_t)i;
+      if ((key >> kBinShift) != bin) continue;
+    }
+    if ((composite(key, li) >> shift) >= thr) {
+      const int pos = atomicAdd(&s_cnt, 1);
+      if (pos < DSA_MAX_TOPK) out[pos] = (int)li;
+    }
+  }
+  __syncthreads();
+  for (int i = K + tid; i < DSA_MAX_TOPK; i += blockDim.x) out[i] = 0x7FFFFFFF;
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int size = 2; size <= DSA_MAX_TOPK; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < DSA_MAX_TOPK / 2; i += blockDim.x) {
+        const int pos = 2 * i - (i & (stride - 1));
+        const int a = out[pos], b = out[pos + stride];
+        const bool up = (pos & size) == 0;
+        if ((a > b) == up) {
+          out[pos] = b;
+          out[pos + stride] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = tid; j < p.k; j += blockDim.x) {
+    const int li = j < K ? out[j] : -1;
+    idx[j] = li;
+    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+  }
+  if (p.count && tid == 0) p.count[t] = K;
+}
+
+__global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, const int32_t* __restrict__ tok_req,
+                                 const int32_t* __restrict__ bt, int bt_stride, int plog2, int32_t* __restrict__ rows) {
+  const int64_t n = (int64_t)T * k;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / k);
+    rows[i] = translate_one(idx[i], tok_req[t], bt, bt_stride, plog2);
+  }
+}
+
+dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
+  const int64_t nz = (int64_t)p.T * kBins;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0,
+                     stream, p.hist, nz, 0u);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>((p.T * 4 + 255) / 256, 4096)), dim3(256), 0,
+                     stream, p.ctr, (int64_t)p.T * 4, 0u);
+  dim3 grid(p.nslices, p.T);
+  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(topk_finalize_kernel, dim3(p.T), dim3(1024), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req, const int32_t* block_table,
+                            int bt_stride, int plog2, int32_t* rows, hipStream_t stream) {
+  const int64_t n = (int64_t)T * k;
+  hipLaunchKernelGGL(translate_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 8192)), dim3(256), 0,
+                     stream, idx, k, T, tok_req, block_table, bt_stride, plog2, rows);
+  return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+}  // namespace dsa
