@@ -37,7 +37,20 @@ def parse():
     ap.add_argument("--workload", default="tp8_spec_decode_64k")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle sample (0 disables the CPU baseline)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
+                         "the HBM byte counters of a profiler against a known size")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "repeats": 5}))
 
 
 def cpu_baseline(wl, seconds, bytes_of_rows):
@@ -69,6 +82,9 @@ def cpu_baseline(wl, seconds, bytes_of_rows):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the DSA layer path here runs on a single MI355X "

@@ -98,11 +98,12 @@ MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
   } else if (a.num_splits > 0) {
     want = a.num_splits;
   } else {
-    const int64_t waves = (int64_t)a.num_rows * pl.ntiles;
-    want = (int)std::min<int64_t>(16, std::max<int64_t>(1, (2048 + waves - 1) / waves));
+    // about one workgroup per resident slot (4 single-wave groups per CU)
+    const int64_t groups = (int64_t)a.num_rows * ((pl.ntiles + 3) / 4);
+    want = (int)std::min<int64_t>(16, std::max<int64_t>(1, (1024 + groups - 1) / groups));
   }
-  want = std::max(1, std::min(want, (a.k + 31) / 32));
-  pl.split_len = ((a.k + want - 1) / want + 31) / 32 * 32;
+  want = std::max(1, std::min(want, (a.k + 15) / 16));
+  pl.split_len = ((a.k + want - 1) / want + 15) / 16 * 16;
   pl.nsplit = (a.k + pl.split_len - 1) / pl.split_len;
   size_t off = 0;
   pl.off_po = 0;

@@ -32,6 +32,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16) += A(16x16) * B(16x16), bf16: lane l supplies A[l%16][4*(l/16) ..
+// +4) and B[4*(l/16) .. +4)[l%16]; D layout as above.
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // D(16x16) += A(16x128) * B(128x16) with FP8 E4M3 inputs (unit block scales).
 // Lane l supplies 32 consecutive k-values A[l%16][32*(l/16) .. +32) and
 // B[32*(l/16) .. +32)[l%16]; D layout as above.
@@ -137,6 +143,35 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) == 0) u = 0;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Lane-group exchanges (a row = 16 lanes).  permlane16_swap(x, y) swaps the odd
+// rows of x with the even rows of y; permlane32_swap(x, y) swaps the upper 32
+// lanes of x with the lower 32 lanes of y.  Both return (x', y').
+struct f32pair {
+  float x, y;
+};
+__device__ __forceinline__ f32pair swap_rows16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32pair swap_halves32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Reduce-scatter over the four 16-lane rows: lane (g, c) holds v[0..3]; on
+// return it holds sum over g' of v_{g'}[g] (its own row's share of the sum).
+__device__ __forceinline__ float rows_reduce_scatter4(const float (&v)[4], int g) {
+  const bool odd = g & 1, upper = g >> 1;
+  // x = v[0], y = v[1]: odd rows of x receive the even rows' v[1], even rows
+  // of y receive the odd rows' v[0]; each row then sums the tile of its parity
+  const f32pair a = swap_rows16(v[0], v[1]);
+  const float s01 = odd ? v[1] + a.x : v[0] + a.y;
+  const f32pair b = swap_rows16(v[2], v[3]);
+  const float s23 = odd ? v[3] + b.x : v[2] + b.y;
+  const f32pair h = swap_halves32(s01, s23);
+  return upper ? s23 + h.x : s01 + h.y;
 }
 
 __device__ __forceinline__ float wave_sum_xor_16_32(float v) {

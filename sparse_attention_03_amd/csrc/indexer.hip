@@ -19,7 +19,9 @@
 // operand (q) uses the same dim assignment for head c (+16 for the second
 // head tile), so the k-sum is the full 128-dim dot product.  The result lane
 // (g, c) holds heads 4g+i (i<4) for key c; the ReLU-weighted head sum is done
-// in-lane and across the four lane groups with two xor shuffles.
+// in-lane, then a reduce-scatter over the four lane groups (three cross-row
+// swaps for four tiles) leaves every lane with one finished score, and the
+// wave stores 64 consecutive scores.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,9 +32,78 @@ constexpr int kIdxKT = 4;              // 16-key tiles per wave per round
 constexpr int kIdxRound = kIdxWaves * kIdxKT * 16;  // 256 keys per round
 constexpr int kQPad = 136;             // bf16 per head row in LDS (272 B: conflict-free reads)
 
+// Raw bytes of one round (kIdxKT tiles of 16 keys) for one lane.
+template <int KFMT> struct RawKeys {
+  i32x4 v[kIdxKT][KFMT == DSA_KEY_FP8 ? 2 : 1];
+  uint32_t sc[kIdxKT];   // MXFP4: E8M0 code of the lane's 32 dims
+  bool ok[kIdxKT];       // page present and tile inside the chunk
+  float own_scale;       // FP8 scale of the key this lane scores (tile g, key c)
+};
+
+template <int KFMT>
+__device__ __forceinline__ void load_round(const IndexerParams& p, int r, int base, int kend, int wave, int g,
+                                           int c, int P, RawKeys<KFMT>& raw) {
+  raw.own_scale = 1.f;
+#pragma unroll
+  for (int kt = 0; kt < kIdxKT; ++kt) {
+    const int s0 = base + (wave * kIdxKT + kt) * 16;
+    int pg = -1;
+    if (s0 < kend) pg = phys_page(p.block_table, p.bt_stride, r, s0 >> p.plog2, p.num_pages);
+    raw.ok[kt] = pg >= 0;
+    if (pg >= 0) {
+      const uint8_t* page = p.keys + (int64_t)pg * p.page_bytes;
+      const int slot = (s0 & (P - 1)) + c;
+      if (KFMT == DSA_KEY_FP8) {
+        const uint8_t* kp = page + slot * 128 + 32 * g;
+        raw.v[kt][0] = ld16_stream(kp);
+        raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16_stream(kp + 16);
+        if (kt == g) raw.own_scale = *reinterpret_cast<const float*>(page + P * 128 + slot * 4);
+      } else {
+        raw.v[kt][0] = ld16_stream(page + slot * 64 + 16 * g);
+        raw.sc[kt] = page[P * 64 + slot * 4 + g];
+      }
+    }
+  }
+}
+
+// Dequantise a round into B fragments.  Returns the multiplier of the score
+// this lane stores (key c of tile g): the FP8 key scale, 1 for MXFP4 (whose
+// power-of-two block scales are applied exactly during dequantisation), or
+// -inf for an absent page so the key is never selected.
+template <int KFMT>
+__device__ __forceinline__ float dequant_round(const RawKeys<KFMT>& raw, int g, bf16x8 (&bfr)[kIdxKT][4]) {
+#pragma unroll
+  for (int kt = 0; kt < kIdxKT; ++kt) {
+    if (raw.ok[kt]) {
+      if (KFMT == DSA_KEY_FP8) {
+        const i32x4 a = raw.v[kt][0], b = raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0];
+        bfr[kt][0] = e4m3x8_to_bf16x8(a[0], a[1]);
+        bfr[kt][1] = e4m3x8_to_bf16x8(a[2], a[3]);
+        bfr[kt][2] = e4m3x8_to_bf16x8(b[0], b[1]);
+        bfr[kt][3] = e4m3x8_to_bf16x8(b[2], b[3]);
+      } else {
+        const i32x4 a = raw.v[kt][0];
+        const float sc = e8m0_to_f32(raw.sc[kt]);
+        bfr[kt][0] = e2m1x8_to_bf16x8(a[0], sc);
+        bfr[kt][1] = e2m1x8_to_bf16x8(a[1], sc);
+        bfr[kt][2] = e2m1x8_to_bf16x8(a[2], sc);
+        bfr[kt][3] = e2m1x8_to_bf16x8(a[3], sc);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bfr[kt][kk] = bf16x8{};
+    }
+  }
+  bool own_ok = raw.ok[0];
+#pragma unroll
+  for (int kt = 1; kt < kIdxKT; ++kt)
+    if (g == kt) own_ok = raw.ok[kt];
+  return own_ok ? (KFMT == DSA_KEY_FP8 ? raw.own_scale : 1.f) : -__builtin_inff();
+}
+
 template <int KFMT>
 __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
-  extern __shared__ __attribute__((aligned(16))) __bf16 qs[];  // [rows][32][kQPad]
+  extern __shared__ __attribute__((aligned(16))) __bf16 qs[];  // [rows][32][kQPad] bf16, then [rows][32] fp32 w
   __shared__ int s_vmax[kIdxWaves];
 
   const int r = blockIdx.y;
@@ -53,7 +124,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   if (k0 >= vmax) return;
   const int kend = min(k0 + p.chunk, vmax);
   const int P = 1 << p.plog2;
-  const int code_bytes = (KFMT == DSA_KEY_FP8) ? 128 : 64;
+  float* ws = reinterpret_cast<float*>(qs + p.qrows * 32 * kQPad);
 
   for (int t0 = rs; t0 < re; t0 += p.qrows) {
     const int nr = min(p.qrows, re - t0);
@@ -63,56 +134,25 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
       i32x4 v = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
       *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = v;
     }
+    for (int i = tid; i < nr * 32; i += 256) ws[i] = p.w[(int64_t)t0 * 32 + i];
     __syncthreads();
 
+    // Software pipeline: the raw key bytes of round i+1 are in flight while
+    // round i is dequantised and multiplied.
+    RawKeys<KFMT> raw;
+    load_round<KFMT>(p, r, k0, kend, wave, g, c, P, raw);
     for (int base = k0; base < kend; base += kIdxRound) {
       bf16x8 bfr[kIdxKT][4];
-      float ksc[kIdxKT];
-      int s0v[kIdxKT];
-#pragma unroll
-      for (int kt = 0; kt < kIdxKT; ++kt) {
-        const int s0 = base + (wave * kIdxKT + kt) * 16;
-        s0v[kt] = s0;
-        ksc[kt] = 0.f;
-        int pg = -1;
-        if (s0 < kend) pg = phys_page(p.block_table, p.bt_stride, r, s0 >> p.plog2, p.num_pages);
-        if (pg >= 0) {
-          const uint8_t* page = p.keys + (int64_t)pg * p.page_bytes;
-          const int slot = (s0 & (P - 1)) + c;
-          if (KFMT == DSA_KEY_FP8) {
-            const uint8_t* kp = page + slot * 128 + 32 * g;
-            i32x4 a = ld16_stream(kp), b = ld16_stream(kp + 16);
-            ksc[kt] = *reinterpret_cast<const float*>(page + P * 128 + slot * 4);
-            bfr[kt][0] = e4m3x8_to_bf16x8(a[0], a[1]);
-            bfr[kt][1] = e4m3x8_to_bf16x8(a[2], a[3]);
-            bfr[kt][2] = e4m3x8_to_bf16x8(b[0], b[1]);
-            bfr[kt][3] = e4m3x8_to_bf16x8(b[2], b[3]);
-          } else {
-            const uint8_t* kp = page + slot * 64 + 16 * g;
-            i32x4 a = ld16_stream(kp);
-            const float sc = e8m0_to_f32(page[P * 64 + slot * 4 + g]);
-            ksc[kt] = 1.f;
-            bfr[kt][0] = e2m1x8_to_bf16x8(a[0], sc);
-            bfr[kt][1] = e2m1x8_to_bf16x8(a[1], sc);
-            bfr[kt][2] = e2m1x8_to_bf16x8(a[2], sc);
-            bfr[kt][3] = e2m1x8_to_bf16x8(a[3], sc);
-          }
-        } else {
-          ksc[kt] = -__builtin_inff();  // absent page: never selected
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) bfr[kt][kk] = bf16x8{};
-        }
-      }
-      (void)code_bytes;
+      const float own_mul = dequant_round<KFMT>(raw, g, bfr);
+      if (base + kIdxRound < kend) load_round<KFMT>(p, r, base + kIdxRound, kend, wave, g, c, P, raw);
+      const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
 
       for (int j = 0; j < nr; ++j) {
         const int t = t0 + j;
         const int vis = min(p.tok_vis[t], p.max_vis);
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 4 * g]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 16 + 4 * g]);
         f32x4 acc[kIdxKT][2];
-#pragma unroll
-        for (int kt = 0; kt < kIdxKT; ++kt) acc[kt][0] = acc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         const __bf16* qrow = &qs[(j * 32) * kQPad];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -120,26 +160,31 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
           const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qrow[(16 + c) * kQPad + 32 * g + 8 * kk]);
 #pragma unroll
           for (int kt = 0; kt < kIdxKT; ++kt) {
-            acc[kt][0] = mfma16x16x32(a0, bfr[kt][kk], acc[kt][0]);
-            acc[kt][1] = mfma16x16x32(a1, bfr[kt][kk], acc[kt][1]);
+            if (kk == 0) {
+              acc[kt][0] = mfma16x16x32(a0, bfr[kt][0], f32x4{0.f, 0.f, 0.f, 0.f});
+              acc[kt][1] = mfma16x16x32(a1, bfr[kt][0], f32x4{0.f, 0.f, 0.f, 0.f});
+            } else {
+              acc[kt][0] = mfma16x16x32(a0, bfr[kt][kk], acc[kt][0]);
+              acc[kt][1] = mfma16x16x32(a1, bfr[kt][kk], acc[kt][1]);
+            }
           }
         }
-        float* srow = p.scores + (int64_t)t * p.ld;
+        // ReLU-weighted head sum: 8 heads in-lane, then a reduce-scatter over
+        // the four lane groups leaves lane (g, c) with key c of tile g
+        float v[kIdxKT];
 #pragma unroll
         for (int kt = 0; kt < kIdxKT; ++kt) {
-          float v = 0.f;
+          float x = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v += w0[i] * fmaxf(acc[kt][0][i], 0.f);
-            v += w1[i] * fmaxf(acc[kt][1][i], 0.f);
+            x += w0[i] * fmaxf(acc[kt][0][i], 0.f);
+            x += w1[i] * fmaxf(acc[kt][1][i], 0.f);
           }
-          v = wave_sum_xor_16_32(v);
-          const int s = s0v[kt] + c;
-          if (g == (kt & 3) && s < vis && s0v[kt] < kend) {
-            const float ks = ksc[kt];
-            srow[s] = (ks == -__builtin_inff()) ? ks : v * ks;
-          }
+          v[kt] = x;
         }
+        const float tot = rows_reduce_scatter4(v, g);
+        if (s_own < kend && s_own < vis)
+          p.scores[(int64_t)t * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
       }
     }
   }
@@ -147,7 +192,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
 
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
   dim3 grid((p.max_vis + p.chunk - 1) / p.chunk, p.R);
-  const size_t lds = (size_t)p.qrows * 32 * kQPad * sizeof(__bf16);
+  const size_t lds = (size_t)p.qrows * 32 * (kQPad * sizeof(__bf16) + sizeof(float));
   if (p.key_fmt == DSA_KEY_FP8)
     hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_FP8>, grid, dim3(256), lds, stream, p);
   else

@@ -12,11 +12,17 @@
 // four 16-head tiles, one wave each (heads padded to a multiple of 16
 // in-kernel; padded heads get zero queries and are never written).  With one
 // wave per SIMD a wave may hold its 128 accumulator registers, the 72
-// registers of its query fragments and the tile temporaries without spills.  For every 32 selected rows:
-//   gather   all waves load the rows with 16-byte loads, dequantise them
-//            exactly to bf16 (FP8 codes; NVFP4 codes x E4M3 block scale; BF16
-//            copied) and store a [32 x 576] tile in LDS.  A per-row FP8 scale
+// registers of its query fragments and the tile temporaries without spills.
+// For every 16 selected rows:
+//   gather   all waves load the rows with 16-byte loads (four lanes per row,
+//            64 contiguous bytes per load instruction per row), dequantise
+//            them exactly to bf16 (FP8 codes; NVFP4 codes x E4M3 block scale;
+//            BF16 copied) and store a [16 x 576] tile in LDS.  A per-row FP8 scale
 //            is kept aside and folded into the logits and softmax weights.
+//            Software pipeline: the loads of tile i+1 are issued into
+//            registers before tile i computes, and the row ids of tile i+2
+//            are fetched a step earlier still, so HBM latency overlaps the
+//            MFMA work instead of stalling every tile.
 //   QK       S^T[rows x heads] = Lat . Q^T on v_mfma_f32_16x16x32_bf16: lane
 //            (g, c) supplies latent row c and head c over the same dims
 //            (k-step kk < 16: nope dims 128g + 8kk..; kk = 16, 17: rope dims
@@ -24,120 +30,148 @@
 //            holding rows 4g+i of head c -- exactly the A operand the value
 //            product needs, so the softmax weights never leave registers.
 //   softmax  online, base 2, per head; the head max/sum reduce over the four
-//            lane groups with two xor shuffles.
-//   PV       O[heads x 512] += P[heads x 32 rows] . V[32 rows x 512]: the V
-//            operand needs 8 rows of one column per lane, read as 4x4 bf16
-//            blocks (ds_read_b64) and transposed with v_perm_b32.  Lane (g, c)
-//            accumulates heads 4g+i at dims 64a + 4c + u.
+//            lane groups with two xor shuffles.  The running max only moves
+//            when a tile exceeds it by 2^8, so the 128 accumulators are
+//            rescaled rarely instead of on almost every tile.
+//   PV       O[heads x 512] += P[heads x 16 rows] . V[16 rows x 512] on
+//            v_mfma_f32_16x16x16_bf16: the V operand needs 4 rows of one
+//            column per lane, read as 4x4 bf16 blocks (ds_read_b64) and
+//            transposed with v_perm_b32.  Lane (g, c) accumulates heads 4g+i
+//            at dims 64a + 4c + u.
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 
-constexpr int kRT = 32;      // selected rows per tile
+constexpr int kRT = 16;      // selected rows per tile
 constexpr int kLPad = 584;   // bf16 per LDS latent row (1168 B: conflict-free row reads)
 
 __device__ __forceinline__ int dim_of(int kk, int g) {
   return kk < 16 ? 128 * g + 8 * kk : 512 + 16 * g + 8 * (kk - 16);
 }
 
+constexpr float kRescaleLog2 = 8.f;  // running max moves only when it grows by 2^8
+
+// Gather geometry: a row is cut into 64-byte segments; lane l of every wave
+// owns row (l >> 2) of the 16-row tile and chunk (l & 3) of each segment, and
+// wave w takes segments w, w + NW, ...  The row address is therefore computed
+// once per tile and every chunk is an immediate offset from it.
+template <int FMT> struct Geo;
+template <> struct Geo<DSA_LAT_FP8> { static constexpr int SEGS = 9; };    // 576 E4M3
+template <> struct Geo<DSA_LAT_BF16> { static constexpr int SEGS = 18; };  // 576 bf16
+template <> struct Geo<DSA_LAT_NVFP4> { static constexpr int SEGS = 5; };  // 4 x 128 E2M1, 64 rope
+
+struct RowPtr {
+  const uint8_t* data;   // FP8/BF16 row, NVFP4 codes
+  const uint8_t* aux;    // NVFP4 block scales
+  const uint8_t* rope;   // NVFP4 rope
+};
+
+__device__ __forceinline__ bool row_ok(int id, const MlaParams& p) {
+  return id >= 0 && (id >> p.plog2) < p.num_pages;
+}
+
 template <int FMT>
-__device__ __forceinline__ void gather_tile(const MlaParams& p, int t, int j0, int j_end, __bf16* lat,
-                                            float* rsc, int* rid) {
-  const int tid = threadIdx.x, nth = blockDim.x;
-  const int P = 1 << p.plog2;
-  if (tid < kRT) {
-    const int j = j0 + tid;
-    int id = (j < j_end) ? p.rows[(int64_t)t * p.k + j] : -1;
-    if (id >= 0 && (id >> p.plog2) >= p.num_pages) id = -1;
-    rid[tid] = id;
-    float sc = id >= 0 ? 1.f : 0.f;
-    if (FMT == DSA_LAT_FP8 && id >= 0) {
-      const uint8_t* page = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
-      sc = *reinterpret_cast<const float*>(page + P * 576 + (id & (P - 1)) * 4);
-    }
-    rsc[tid] = sc;
+__device__ __forceinline__ RowPtr row_ptr(const MlaParams& p, int id, int P) {
+  RowPtr r{nullptr, nullptr, nullptr};
+  if (!row_ok(id, p)) return r;
+  const uint8_t* page = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
+  const int slot = id & (P - 1);
+  if (FMT == DSA_LAT_FP8) r.data = page + slot * 576;
+  if (FMT == DSA_LAT_BF16) r.data = page + (int64_t)slot * 1152;
+  if (FMT == DSA_LAT_NVFP4) {
+    r.data = page + slot * 256;
+    r.aux = page + 256 * P + slot * 32;
+    r.rope = page + 288 * P + slot * 64;
   }
-  __syncthreads();
-  if (FMT == DSA_LAT_FP8) {
-    for (int i = tid; i < kRT * 36; i += nth) {
-      const int row = i / 36, part = i - row * 36;
-      const int id = rid[row];
-      i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-      if (id >= 0) {
-        const uint8_t* src = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes + (id & (P - 1)) * 576 + part * 16;
-        const i32x4 v = ld16(src);
-        const i32x2 a = e4m3x4_to_bf16(v[0]), b = e4m3x4_to_bf16(v[1]);
-        const i32x2 c2 = e4m3x4_to_bf16(v[2]), d = e4m3x4_to_bf16(v[3]);
-        lo = i32x4{a[0], a[1], b[0], b[1]};
-        hi = i32x4{c2[0], c2[1], d[0], d[1]};
-      }
-      i32x4* dst = reinterpret_cast<i32x4*>(&lat[row * kLPad + part * 16]);
-      dst[0] = lo;
-      dst[1] = hi;
-    }
-  } else if (FMT == DSA_LAT_BF16) {
-    for (int i = tid; i < kRT * 72; i += nth) {
-      const int row = i / 72, part = i - row * 72;
-      const int id = rid[row];
-      i32x4 v = {0, 0, 0, 0};
-      if (id >= 0)
-        v = ld16(p.lat + (int64_t)(id >> p.plog2) * p.page_bytes + (int64_t)(id & (P - 1)) * 1152 + part * 16);
-      *reinterpret_cast<i32x4*>(&lat[row * kLPad + part * 8]) = v;
-    }
-  } else {  // NVFP4: 16 code chunks (32 dims each) + 4 rope chunks (16 dims each) per row
-    for (int i = tid; i < kRT * 20; i += nth) {
-      const int row = i / 20, part = i - row * 20;
-      const int id = rid[row];
-      i32x4* dst;
-      if (part < 16) {
-        dst = reinterpret_cast<i32x4*>(&lat[row * kLPad + part * 32]);
-        i32x4 o0 = {0, 0, 0, 0}, o1 = o0, o2 = o0, o3 = o0;
-        if (id >= 0) {
-          const uint8_t* page = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
-          const int slot = id & (P - 1);
-          const i32x4 v = ld16(page + slot * 256 + part * 16);
-          const uint32_t s2 = *reinterpret_cast<const uint16_t*>(page + 256 * P + slot * 32 + part * 2);
-          const float sa = e4m3_to_f32(s2 & 0xFFu), sb = e4m3_to_f32(s2 >> 8);
-          o0 = __builtin_bit_cast(i32x4, e2m1x8_times(v[0], sa));
-          o1 = __builtin_bit_cast(i32x4, e2m1x8_times(v[1], sa));
-          o2 = __builtin_bit_cast(i32x4, e2m1x8_times(v[2], sb));
-          o3 = __builtin_bit_cast(i32x4, e2m1x8_times(v[3], sb));
+  return r;
+}
+
+// Load segments sp = s0, s0 + NW, ... (SPT of them) of this lane's row.
+template <int FMT, int NW, int SPT>
+__device__ __forceinline__ void seg_load(const RowPtr& rp, int s0, int q, i32x4 (&raw)[SPT], uint32_t (&aux)[SPT]) {
+  constexpr int SEGS = Geo<FMT>::SEGS;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int sp = s0 + i * NW;
+    raw[i] = i32x4{0, 0, 0, 0};
+    aux[i] = 0;
+    if (sp < SEGS && rp.data) {
+      if (FMT == DSA_LAT_NVFP4) {
+        if (sp < 4) {
+          raw[i] = ld16(rp.data + sp * 64 + q * 16);
+          aux[i] = *reinterpret_cast<const uint16_t*>(rp.aux + (sp * 4 + q) * 2);
+        } else {
+          raw[i] = ld16(rp.rope + q * 16);
         }
-        dst[0] = o0;
-        dst[1] = o1;
-        dst[2] = o2;
-        dst[3] = o3;
       } else {
-        const int q4 = part - 16;
-        dst = reinterpret_cast<i32x4*>(&lat[row * kLPad + 512 + q4 * 16]);
-        i32x4 lo = {0, 0, 0, 0}, hi = lo;
-        if (id >= 0) {
-          const uint8_t* page = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
-          const i32x4 v = ld16(page + 288 * P + (id & (P - 1)) * 64 + q4 * 16);
-          const i32x2 a = e4m3x4_to_bf16(v[0]), b = e4m3x4_to_bf16(v[1]);
-          const i32x2 c2 = e4m3x4_to_bf16(v[2]), d = e4m3x4_to_bf16(v[3]);
-          lo = i32x4{a[0], a[1], b[0], b[1]};
-          hi = i32x4{c2[0], c2[1], d[0], d[1]};
-        }
-        dst[0] = lo;
-        dst[1] = hi;
+        raw[i] = ld16(rp.data + sp * 64 + q * 16);
       }
     }
   }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256) void mla_kernel(MlaParams p) {
+// Dequantise the loaded segments into this lane's LDS row.
+template <int FMT, int NW, int SPT>
+__device__ __forceinline__ void seg_store(__bf16* lrow, int s0, int q, const i32x4 (&raw)[SPT],
+                                          const uint32_t (&aux)[SPT]) {
+  constexpr int SEGS = Geo<FMT>::SEGS;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int sp = s0 + i * NW;
+    if (sp >= SEGS) continue;
+    const i32x4 v = raw[i];
+    if (FMT == DSA_LAT_BF16) {
+      *reinterpret_cast<i32x4*>(lrow + (sp * 4 + q) * 8) = v;
+    } else if (FMT == DSA_LAT_FP8 || sp == 4) {
+      const i32x2 a = e4m3x4_to_bf16(v[0]), b = e4m3x4_to_bf16(v[1]);
+      const i32x2 c2 = e4m3x4_to_bf16(v[2]), d = e4m3x4_to_bf16(v[3]);
+      i32x4* dst = reinterpret_cast<i32x4*>(lrow + (FMT == DSA_LAT_FP8 ? (sp * 4 + q) * 16 : 512 + q * 16));
+      dst[0] = i32x4{a[0], a[1], b[0], b[1]};
+      dst[1] = i32x4{c2[0], c2[1], d[0], d[1]};
+    } else {  // NVFP4 codes: 32 dims, two E4M3 block scales
+      const float sa = e4m3_to_f32(aux[i] & 0xFFu), sb = e4m3_to_f32((aux[i] >> 8) & 0xFFu);
+      i32x4* dst = reinterpret_cast<i32x4*>(lrow + (sp * 4 + q) * 32);
+      dst[0] = __builtin_bit_cast(i32x4, e2m1x8_times(v[0], sa));
+      dst[1] = __builtin_bit_cast(i32x4, e2m1x8_times(v[1], sa));
+      dst[2] = __builtin_bit_cast(i32x4, e2m1x8_times(v[2], sb));
+      dst[3] = __builtin_bit_cast(i32x4, e2m1x8_times(v[3], sb));
+    }
+  }
+}
+
+template <int FMT, int NW>
+__global__ __launch_bounds__(64 * NW) void mla_kernel(MlaParams p) {
+  constexpr int SEGS = Geo<FMT>::SEGS;
+  // BF16 rows are twice as wide: a single wave gathers them in two register
+  // batches at tile time instead of prefetching them
+  constexpr int NB = (FMT == DSA_LAT_BF16 && NW == 1) ? 2 : 1;
+  constexpr int SPT = (SEGS + NW * NB - 1) / (NW * NB);
   __shared__ __attribute__((aligned(16))) __bf16 lat[kRT * kLPad];
   __shared__ float rsc[kRT];
-  __shared__ int rid[kRT];
+  __shared__ int rv[kRT];          // row id of the tile in LDS, -1 = absent
+  __shared__ int ridbuf[2][kRT];   // row ids of the next two tiles
 
   const int split = blockIdx.x, t = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, ht = blockIdx.z * 4 + (tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ht = blockIdx.z * NW + wave;
   const int g = lane >> 4, c = lane & 15;
+  const int my_row = lane >> 2, q = lane & 3;
   const int j_begin = split * p.split_len;
   const int j_end = min(j_begin + p.split_len, p.k);
+  const int ntile = (j_end - j_begin + kRT - 1) / kRT;
+  const int P = 1 << p.plog2;
+  const int32_t* rlist = p.rows + (int64_t)t * p.k;
+  auto load_id = [&](int tile) -> int {
+    const int j = j_begin + tile * kRT + tid;
+    return (tid < kRT && tile < ntile && j < j_end) ? rlist[j] : -1;
+  };
+  // FP8 row scale, fetched by the lane that owns chunk 0 of the row in wave 0
+  const bool scale_lane = (FMT == DSA_LAT_FP8) && wave == 0 && q == 0;
+  auto load_scale = [&](int id) -> float {
+    if (!row_ok(id, p)) return 0.f;
+    const uint8_t* page = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
+    return *reinterpret_cast<const float*>(page + P * 576 + (id & (P - 1)) * 4);
+  };
 
   // queries of head 16*ht + c as B fragments (zero for padded heads)
   const int head = 16 * ht + c;
@@ -156,55 +190,93 @@ __global__ __launch_bounds__(256) void mla_kernel(MlaParams p) {
   for (int x = 0; x < 32; ++x) O[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), l = 0.f;  // running max (log2 units) and sum, head c
 
-  for (int j0 = j_begin; j0 < j_end; j0 += kRT) {
-    __syncthreads();
-    gather_tile<FMT>(p, t, j0, j_end, lat, rsc, rid);
-    __syncthreads();
+  // pipeline prologue: ids of tiles 0 and 1, loads of tile 0, ids of tile 2
+  if (tid < kRT) {
+    ridbuf[0][tid] = load_id(0);
+    ridbuf[1][tid] = load_id(1);
+  }
+  __syncthreads();
+  i32x4 raw[SPT];
+  uint32_t aux[SPT];
+  float sc_next = 0.f;
+  if (NB == 1) {
+    const int id = ridbuf[0][my_row];
+    seg_load<FMT, NW, SPT>(row_ptr<FMT>(p, id, P), wave, q, raw, aux);
+    if (scale_lane) sc_next = load_scale(id);
+  }
+  int id_next = load_id(2);
+  __bf16* lrow = lat + my_row * kLPad;
 
-    // ---- QK: S^T tile, rows 16*nt + 4g + i of head c
-    f32x4 s[2];
+  for (int it = 0; it < ntile; ++it) {
+    __syncthreads();  // the previous tile's readers are done with lat/rsc/rv
+    // stage A: tile `it` (in registers) -> LDS
+    if (NB == 1) {
+      seg_store<FMT, NW, SPT>(lrow, wave, q, raw, aux);
+    } else {
+      const RowPtr rp = row_ptr<FMT>(p, ridbuf[it & 1][my_row], P);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const __bf16* lrow = &lat[(16 * nt + c) * kLPad];
+      for (int b = 0; b < NB; ++b) {
+        seg_load<FMT, NW * NB, SPT>(rp, wave + b * NW, q, raw, aux);
+        seg_store<FMT, NW * NB, SPT>(lrow, wave + b * NW, q, raw, aux);
+      }
+    }
+    if (tid < kRT) {
+      const int id = ridbuf[it & 1][tid];
+      rv[tid] = row_ok(id, p) ? id : -1;
+      if (FMT != DSA_LAT_FP8) rsc[tid] = row_ok(id, p) ? 1.f : 0.f;
+    }
+    if (scale_lane) rsc[my_row] = sc_next;
+    __syncthreads();
+    if (tid < kRT) ridbuf[it & 1][tid] = id_next;  // ids of tile it+2 (tile it's ids are consumed)
+    // stage B: loads of tile it+1 stay in flight while tile `it` computes
+    if (NB == 1 && it + 1 < ntile) {
+      const int id = ridbuf[(it + 1) & 1][my_row];
+      seg_load<FMT, NW, SPT>(row_ptr<FMT>(p, id, P), wave, q, raw, aux);
+      if (scale_lane) sc_next = load_scale(id);
+    }
+    id_next = load_id(it + 3);
+    // ---- QK: S^T tile, rows 4g + i of head c
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    {
+      const __bf16* lrow = &lat[c * kLPad];
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(lrow + dim_of(kk, g));
-        s[nt] = mfma16x16x32(a, qf[kk], s[nt]);
+        s = mfma16x16x32(a, qf[kk], s);
       }
     }
     // ---- online softmax for head c
-    float lg[8], rs[8];
+    float lg[4], rs[4];
     float tmax = -__builtin_inff();
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * nt + 4 * g + i;
-        const float sc = rsc[row];
-        rs[nt * 4 + i] = sc;
-        const float v = rid[row] >= 0 ? s[nt][i] * p.sm_log2 * sc : -__builtin_inff();
-        lg[nt * 4 + i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i;
+      const float sc = rsc[row];
+      rs[i] = sc;
+      const float v = rv[row] >= 0 ? s[i] * p.sm_log2 * sc : -__builtin_inff();
+      lg[i] = v;
+      tmax = fmaxf(tmax, v);
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = (mnew == -__builtin_inff()) ? 1.f : exp2f(m - mnew);
+    // lazy rescaling: keep a stale max while the tile stays within 2^8 of it
+    // (weights stay <= 256); both O and l use the same max, so the final
+    // normalisation is exact
+    const float mnew = (m == -__builtin_inff() || tmax > m + kRescaleLog2) ? tmax : m;
+    const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - mnew);
     float psum = 0.f;
-    float pw[8];
+    float pw[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const float e = (lg[x] == -__builtin_inff()) ? 0.f : exp2f(lg[x] - mnew);
+    for (int x = 0; x < 4; ++x) {
+      const float e = (lg[x] == -__builtin_inff() || mnew == -__builtin_inff()) ? 0.f : exp2f(lg[x] - mnew);
       psum += e;
       pw[x] = e * rs[x];  // FP8 row scale enters the value product here
     }
     psum = wave_sum_xor_16_32(psum);
     l = l * alpha + psum;
     m = mnew;
-    const i32x4 pa4 = {(int)pack_bf16x2(pw[0], pw[1]), (int)pack_bf16x2(pw[2], pw[3]),
-                       (int)pack_bf16x2(pw[4], pw[5]), (int)pack_bf16x2(pw[6], pw[7])};
-    const bf16x8 pa = __builtin_bit_cast(bf16x8, pa4);
+    const i32x2 pa2 = {(int)pack_bf16x2(pw[0], pw[1]), (int)pack_bf16x2(pw[2], pw[3])};
+    const bf16x4 pa = __builtin_bit_cast(bf16x4, pa2);
 
     // ---- rescale accumulators (heads 4g+i) when any running max moved
     if (__ballot(alpha != 1.f)) {
@@ -217,24 +289,19 @@ __global__ __launch_bounds__(256) void mla_kernel(MlaParams p) {
         for (int i = 0; i < 4; ++i) O[x][i] *= ai[i];
     }
 
-    // ---- PV
-    int rr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rr[j] = (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4);
+    // ---- PV: O[heads 4g+i][dims 64a + 4c + u] += P . V over the 16 rows
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      i32x2 rv[8];
+      i32x2 vb[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const i32x2*>(&lat[rr[j] * kLPad + 64 * a + 4 * c]);
+      for (int j = 0; j < 4; ++j) vb[j] = *reinterpret_cast<const i32x2*>(&lat[(4 * g + j) * kLPad + 64 * a + 4 * c]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int half = u >> 1;
         const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-        i32x4 f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          f[d] = (int)__builtin_amdgcn_perm((uint32_t)rv[2 * d + 1][half], (uint32_t)rv[2 * d][half], sel);
-        O[a * 4 + u] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, f), O[a * 4 + u]);
+        const i32x2 f = {(int)__builtin_amdgcn_perm((uint32_t)vb[1][half], (uint32_t)vb[0][half], sel),
+                         (int)__builtin_amdgcn_perm((uint32_t)vb[3][half], (uint32_t)vb[2][half], sel)};
+        O[a * 4 + u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, f), O[a * 4 + u]);
       }
     }
   }
@@ -295,13 +362,24 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
 }
 
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
-  // at most four head tiles (one wave each) per workgroup; more go to grid.z
-  dim3 grid(p.nsplit, p.T, (p.ntiles + 3) / 4), block(64 * (p.ntiles < 4 ? p.ntiles : 4));
-  switch (p.fmt) {
-    case DSA_LAT_BF16: hipLaunchKernelGGL(mla_kernel<DSA_LAT_BF16>, grid, block, 0, stream, p); break;
-    case DSA_LAT_FP8: hipLaunchKernelGGL(mla_kernel<DSA_LAT_FP8>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(mla_kernel<DSA_LAT_NVFP4>, grid, block, 0, stream, p); break;
+  // at most four head tiles (one wave each) per workgroup; the tiles of a row
+  // are spread evenly over grid.z
+  const int groups = (p.ntiles + 3) / 4;
+  const int nw = (p.ntiles + groups - 1) / groups;
+  dim3 grid(p.nsplit, p.T, groups), block(64 * nw);
+#define DSA_MLA_LAUNCH(F)                                                                   \
+  switch (nw) {                                                                            \
+    case 1: hipLaunchKernelGGL((mla_kernel<F, 1>), grid, block, 0, stream, p); break;      \
+    case 2: hipLaunchKernelGGL((mla_kernel<F, 2>), grid, block, 0, stream, p); break;      \
+    case 3: hipLaunchKernelGGL((mla_kernel<F, 3>), grid, block, 0, stream, p); break;      \
+    default: hipLaunchKernelGGL((mla_kernel<F, 4>), grid, block, 0, stream, p); break;     \
   }
+  switch (p.fmt) {
+    case DSA_LAT_BF16: DSA_MLA_LAUNCH(DSA_LAT_BF16) break;
+    case DSA_LAT_FP8: DSA_MLA_LAUNCH(DSA_LAT_FP8) break;
+    default: DSA_MLA_LAUNCH(DSA_LAT_NVFP4) break;
+  }
+#undef DSA_MLA_LAUNCH
   if (p.nsplit > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(p.H, p.T), dim3(128), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

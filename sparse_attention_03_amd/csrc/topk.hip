@@ -6,17 +6,19 @@
 // row t is unique: the K = min(k, vis) largest scores, equal scores ordered by
 // ascending index.  It is emitted in ascending index order.
 //
-// Three passes over the scores of a row, each spread over many workgroups:
-//   1. histogram of the top 12 bits of the order-preserving uint32 key;
-//   2. threshold bin b from the histogram; every slice appends keys above b
-//      ("definite", fewer than K in total) and keys inside b ("candidates")
-//      to per-row buffers with one atomic per wave;
-//   3. one workgroup per row refines the candidates with an exact radix
-//      select on the 56-bit composite (low 20 key bits, then inverted index),
-//      so ties resolve to the lower index, then sorts the K winners by index
-//      (bitonic, in LDS) and writes indices, physical rows and the count.
-// If a row's candidates overflow their buffer, pass 3 reads the candidates
-// straight from the score row instead (slower, same result).
+// Two passes over the scores of a row, each spread over many workgroups:
+//   1. histogram of the top 12 bits of the order-preserving uint32 key, then
+//      (one small workgroup per row) the threshold bin b holding rank K;
+//   2. every slice gathers keys above b ("definite", fewer than K in total)
+//      and keys inside b ("candidates") in LDS and appends them to per-row
+//      buffers behind one global atomic per list;
+//   3. one workgroup per row refines the candidates (in LDS) with an exact
+//      radix select on the 56-bit composite (low 20 key bits, then inverted
+//      index), so ties resolve to the lower index, then sorts the K winners
+//      by index (bitonic, in LDS) and writes indices, physical rows and the
+//      count.
+// If a row's candidates overflow their buffer, step 3 reads them straight
+// from the score row instead (slower, same result).
 #include "common.h"
 #include "kernels.h"
 
@@ -61,13 +63,15 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Threshold bin of row t from its global histogram: the bin b with
-// count(bins > b) < k <= count(bins >= b).  Returns b and need = k - count(> b).
-// Must be called by all 256 threads of the block.
-__device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int k, int* out_bin, int* out_need) {
+// Threshold bin of each row from its global histogram: the bin b with
+// count(bins > b) < k <= count(bins >= b); stores b and need = k - count(> b)
+// in ctr[2], ctr[3].  One 256-thread workgroup per row.
+__global__ __launch_bounds__(256) void topk_threshold_kernel(TopkParams p) {
   __shared__ uint32_t part[256];
-  __shared__ int s_bin, s_need;
+  const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  if (row_vis(p, t) <= p.k) return;
+  const uint32_t* gh = p.hist + (int64_t)t * kBins;
   uint32_t loc[16];
   uint32_t sum = 0;
 #pragma unroll
@@ -77,82 +81,106 @@ __device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int k, int* 
   }
   part[tid] = sum;
   __syncthreads();
-  // inclusive suffix scan over threads (higher thread = higher bins)
-  for (int off = 1; off < 256; off <<= 1) {
-    uint32_t v = (tid + off < 256) ? part[tid + off] : 0u;
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive suffix scan over threads
+    const uint32_t v = (tid + off < 256) ? part[tid + off] : 0u;
     __syncthreads();
     part[tid] += v;
     __syncthreads();
   }
-  const uint32_t above = part[tid] - sum;  // bins owned by higher threads
-  if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
+  const uint32_t above = part[tid] - sum;  // counts in bins owned by higher threads
+  const uint32_t k = (uint32_t)p.k;
+  if (above < k && above + sum >= k) {
     uint32_t acc = above;
     for (int i = 15; i >= 0; --i) {
-      if (acc + loc[i] >= (uint32_t)k) {
-        s_bin = tid * 16 + i;
-        s_need = k - (int)acc;
+      if (acc + loc[i] >= k) {
+        p.ctr[(int64_t)t * 4 + 2] = (uint32_t)(tid * 16 + i);
+        p.ctr[(int64_t)t * 4 + 3] = k - acc;
         break;
       }
       acc += loc[i];
     }
   }
-  __syncthreads();
-  *out_bin = s_bin;
-  *out_need = s_need;
 }
 
-// Append this lane's element (if pred) to buf at a position reserved with one
-// atomic per wave.  Returns the position or -1.
-__device__ __forceinline__ int wave_append(bool pred, uint32_t* counter) {
-  const uint64_t mask = __ballot(pred);
-  if (mask == 0) return -1;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)mask) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-  base = __shfl(base, leader);
-  if (!pred) return -1;
-  return (int)(base + __popcll(mask & ((1ull << lane) - 1ull)));
-}
+constexpr int kFilterCap = 2048;  // candidates a filter workgroup keeps in LDS
 
+// Keys above the threshold bin ("definite") and inside it ("candidates") are
+// gathered in LDS, then copied out behind one global atomic per list.
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
+  __shared__ int l_def[DSA_MAX_TOPK];
+  __shared__ uint32_t l_ck[kFilterCap];
+  __shared__ int l_ci[kFilterCap];
+  __shared__ int n_def, n_cand, n_cand2;
+  __shared__ uint32_t base_def, base_cand;
   const int t = blockIdx.y;
+  const int tid = threadIdx.x;
   const int vis = row_vis(p, t);
   if (vis <= p.k) return;
   const int s_begin = blockIdx.x * p.slice;
   if (s_begin >= vis) return;
   const int s_end = min(s_begin + p.slice, vis);
-  int bin, need;
-  find_threshold_bin(p.hist + (int64_t)t * kBins, p.k, &bin, &need);
   uint32_t* ctr = p.ctr + (int64_t)t * 4;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ctr[2] = (uint32_t)bin;
-    ctr[3] = (uint32_t)need;
+  const uint32_t bin = ctr[2];
+  if (tid == 0) {
+    n_def = 0;
+    n_cand = 0;
+    n_cand2 = 0;
   }
+  __syncthreads();
   const float* row = p.scores + (int64_t)t * p.ld;
-  int32_t* defrow = p.defbuf + (int64_t)t * p.k;
-  uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
-  // every lane of a wave runs the same trip count so the ballots line up
-  for (int s0 = s_begin; s0 < s_end; s0 += 1024) {
-    const int s = s0 + 4 * threadIdx.x;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s_begin + 4 * tid; s < s_end; s += 1024) {
+    f32x4 v;
     if (s + 3 < s_end) {
       v = *reinterpret_cast<const f32x4*>(row + s);
     } else {
-      for (int e = 0; e < 4; ++e)
-        if (s + e < s_end) v[e] = row[s + e];
+      for (int e = 0; e < 4; ++e) v[e] = (s + e < s_end) ? row[s + e] : -__builtin_inff();
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool in = s + e < s_end;
+      if (s + e >= s_end) break;
       const uint32_t key = order_key(v[e]);
-      const int d = (int)(key >> kBinShift);
-      const int pd = wave_append(in && d > bin, &ctr[0]);
-      if (pd >= 0 && pd < p.k) defrow[pd] = s + e;
-      const int pc = wave_append(in && d == bin, &ctr[1]);
-      if (pc >= 0 && pc < p.cand_cap) {
-        candrow[2 * pc] = key;
-        candrow[2 * pc + 1] = (uint32_t)(s + e);
+      const uint32_t d = key >> kBinShift;
+      if (d > bin) {
+        const int pos = atomicAdd(&n_def, 1);
+        if (pos < DSA_MAX_TOPK) l_def[pos] = s + e;
+      } else if (d == bin) {
+        const int pos = atomicAdd(&n_cand, 1);
+        if (pos < kFilterCap) {
+          l_ck[pos] = key;
+          l_ci[pos] = s + e;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    base_def = atomicAdd(&ctr[0], (uint32_t)n_def);
+    base_cand = atomicAdd(&ctr[1], (uint32_t)n_cand);
+  }
+  __syncthreads();
+  int32_t* defrow = p.defbuf + (int64_t)t * p.k;
+  for (int i = tid; i < n_def; i += 256)
+    if (base_def + i < (uint32_t)p.k) defrow[base_def + i] = l_def[i];
+  uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
+  const int nc = n_cand;
+  if (nc <= kFilterCap) {
+    for (int i = tid; i < nc; i += 256) {
+      const uint32_t pos = base_cand + i;
+      if (pos < (uint32_t)p.cand_cap) {
+        candrow[2 * pos] = l_ck[i];
+        candrow[2 * pos + 1] = (uint32_t)l_ci[i];
+      }
+    }
+  } else {
+    // more candidates than LDS holds: write them all straight from a rescan
+    for (int s = s_begin + tid; s < s_end; s += 256) {
+      const uint32_t key = order_key(row[s]);
+      if ((key >> kBinShift) == bin) {
+        const uint32_t pos = base_cand + (uint32_t)atomicAdd(&n_cand2, 1);
+        if (pos < (uint32_t)p.cand_cap) {
+          candrow[2 * pos] = key;
+          candrow[2 * pos + 1] = (uint32_t)s;
+        }
       }
     }
   }
@@ -177,9 +205,14 @@ __device__ __forceinline__ int translate_one(int li, int r, const int32_t* __res
   return (pg << plog2) | (li & ((1 << plog2) - 1));
 }
 
+constexpr int kFinalCap = 4096;  // candidates the finalize workgroup refines in LDS
+
 __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   __shared__ int out[DSA_MAX_TOPK];
+  __shared__ uint32_t ck[kFinalCap];
+  __shared__ uint32_t ci[kFinalCap];
   __shared__ uint32_t h[256];
+  __shared__ uint32_t wsum[4];
   __shared__ uint64_t s_prefix;
   __shared__ int s_need, s_done, s_cnt;
   const int t = blockIdx.x;
@@ -204,10 +237,31 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   const int ndef = (int)ctr[0];
   const int ncand = (int)ctr[1];
   const uint32_t bin = ctr[2];
-  const bool from_buf = ncand <= p.cand_cap;
   const uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
   const float* srow = p.scores + (int64_t)t * p.ld;
-  const int nsrc = from_buf ? ncand : vis;
+  // candidate source: LDS copy, the global candidate buffer, or the score row
+  const int mode = (ncand <= kFinalCap) ? 0 : (ncand <= p.cand_cap ? 1 : 2);
+  const int nsrc = mode == 2 ? vis : ncand;
+  if (mode == 0)
+    for (int i = tid; i < ncand; i += blockDim.x) {
+      ck[i] = candrow[2 * i];
+      ci[i] = candrow[2 * i + 1];
+    }
+  auto fetch = [&](int i, uint32_t& key, uint32_t& li) -> bool {
+    if (mode == 0) {
+      key = ck[i];
+      li = ci[i];
+      return true;
+    }
+    if (mode == 1) {
+      key = candrow[2 * i];
+      li = candrow[2 * i + 1];
+      return true;
+    }
+    key = order_key(srow[i]);
+    li = (uint32_t)i;
+    return (key >> kBinShift) == bin;
+  };
 
   if (tid == 0) {
     s_prefix = 0;
@@ -216,38 +270,39 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   }
   int shift = 48;
   for (;; shift -= 8) {
-    for (int i = tid; i < 256; i += blockDim.x) h[i] = 0;
+    if (tid < 256) h[tid] = 0;
     __syncthreads();
     const uint64_t prefix = s_prefix;
+    const uint32_t need = (uint32_t)s_need;  // read by all before the update below
     for (int i = tid; i < nsrc; i += blockDim.x) {
       uint32_t key, li;
-      if (from_buf) {
-        key = candrow[2 * i];
-        li = candrow[2 * i + 1];
-      } else {
-        key = order_key(srow[i]);
-        li = (uint32_t)i;
-        if ((key >> kBinShift) != bin) continue;
-      }
+      if (!fetch(i, key, li)) continue;
       const uint64_t v = composite(key, li);
       if ((v >> (shift + 8)) == prefix) atomicAdd(&h[(v >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int need = s_need;
-      uint32_t acc = 0;
-      int sel = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (acc + h[b] >= (uint32_t)need) {
-          sel = b;
-          break;
-        }
-        acc += h[b];
+    // suffix sums of the 256 bins: waves 0..3, one bin per lane
+    uint32_t hv = 0, suf = 0;
+    if (tid < 256) {
+      hv = h[tid];
+      suf = hv;
+      const int lane = tid & 63;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(suf, off);
+        if (lane + off < 64) suf += o;
       }
-      need -= (int)acc;
-      s_need = need;
-      s_prefix = (prefix << 8) | (uint64_t)sel;
-      s_done = (h[sel] == (uint32_t)need) || shift == 0;
+      if (lane == 0) wsum[tid >> 6] = suf;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = (tid >> 6) + 1; w < 4; ++w) suf += wsum[w];
+      const uint32_t above = suf - hv;       // count in higher bins
+      if (above < need && suf >= need) {     // exactly one bin qualifies
+        const uint32_t nn = need - above;
+        s_need = (int)nn;
+        s_prefix = (prefix << 8) | (uint64_t)tid;
+        s_done = (hv == nn) || shift == 0;
+      }
     }
     __syncthreads();
     if (s_done) break;
@@ -260,14 +315,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   __syncthreads();
   for (int i = tid; i < nsrc; i += blockDim.x) {
     uint32_t key, li;
-    if (from_buf) {
-      key = candrow[2 * i];
-      li = candrow[2 * i + 1];
-    } else {
-      key = order_key(srow[i]);
-      li = (uint32_t)i;
-      if ((key >> kBinShift) != bin) continue;
-    }
+    if (!fetch(i, key, li)) continue;
     if ((composite(key, li) >> shift) >= thr) {
       const int pos = atomicAdd(&s_cnt, 1);
       if (pos < DSA_MAX_TOPK) out[pos] = (int)li;
@@ -316,6 +364,7 @@ dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
                      stream, p.ctr, (int64_t)p.T * 4, 0u);
   dim3 grid(p.nslices, p.T);
   hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.T), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(256), 0, stream, p);
   hipLaunchKernelGGL(topk_finalize_kernel, dim3(p.T), dim3(1024), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
