@@ -98,9 +98,14 @@ MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
   } else if (a.num_splits > 0) {
     want = a.num_splits;
   } else {
-    // about one workgroup per resident slot (4 single-wave groups per CU)
-    const int64_t groups = (int64_t)a.num_rows * ((pl.ntiles + 3) / 4);
-    want = (int)std::min<int64_t>(16, std::max<int64_t>(1, (1024 + groups - 1) / groups));
+    // Fill the resident slots in one round: the kernel holds one wave per SIMD
+    // (four per CU), a workgroup has nw waves, so 256 * (4 / nw) workgroups are
+    // resident at once; a second, partial round would cost a whole extra pass.
+    const int groups = (pl.ntiles + 3) / 4;
+    const int nw = (pl.ntiles + groups - 1) / groups;
+    const int64_t resident = 256 * (4 / nw);
+    const int64_t per_split = (int64_t)a.num_rows * groups;
+    want = (int)std::min<int64_t>(64, std::max<int64_t>(1, resident / per_split));
   }
   want = std::max(1, std::min(want, (a.k + 15) / 16));
   pl.split_len = ((a.k + want - 1) / want + 15) / 16 * 16;
@@ -197,8 +202,11 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
   if (!a->scores || !aligned(a->scores, 16)) return fail(DSA_ERR_INVALID_ARG, "indexer: scores null or not 16-byte aligned");
   if (a->ld < a->batch.max_vis || a->ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "indexer: ld %lld", (long long)a->ld);
   if (a->batch.num_requests > 65535) return fail(DSA_ERR_INVALID_ARG, "indexer: more than 65535 requests");
+  if (a->q_fmt == DSA_Q_FP8 && (int64_t)a->batch.max_rows_per_req > 16 * 65535)
+    return fail(DSA_ERR_INVALID_ARG, "indexer: too many rows per request");
   if (a->q_fmt != DSA_Q_BF16 && a->q_fmt != DSA_Q_FP8) return fail(DSA_ERR_UNSUPPORTED, "indexer: q_fmt %d", a->q_fmt);
-  if (a->q_fmt == DSA_Q_FP8 && !a->q_scale) return fail(DSA_ERR_INVALID_ARG, "indexer: FP8 q needs q_scale");
+  if (a->q_fmt == DSA_Q_FP8 && (!a->q_scale || !aligned(a->q_scale, 16)))
+    return fail(DSA_ERR_INVALID_ARG, "indexer: FP8 q needs a 16-byte aligned q_scale");
 
   dsa::IndexerParams p{};
   const dsa_batch& b = a->batch;
@@ -226,11 +234,18 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
     p.chunk = chunk;
     p.qrows = std::min(b.max_rows_per_req, 6);
+    p.max_rows_per_req = b.max_rows_per_req;
     st = dsa::launch_indexer_bf16(p, stream);
   } else {
     if (a->keys.fmt != DSA_KEY_FP8) return fail(DSA_ERR_UNSUPPORTED, "indexer: FP8 q runs against FP8 keys only");
     p.q8 = static_cast<const uint8_t*>(a->q);
     p.q_scale = a->q_scale;
+    p.max_rows_per_req = b.max_rows_per_req;
+    // key segment per workgroup: about 2048 workgroups over rows x keys
+    const int64_t row_groups = (int64_t)b.num_requests * ((b.max_rows_per_req + 15) / 16);
+    int chunk = 256;
+    while (chunk < 16384 && row_groups * (((int64_t)b.max_vis + 2 * chunk - 1) / (2 * chunk)) >= 2048) chunk *= 2;
+    p.chunk = chunk;
     st = dsa::launch_indexer_fp8(p, stream);
   }
   if (st != DSA_OK) return fail(st, "indexer: launch failed: %s", hipGetErrorString(hipGetLastError()));

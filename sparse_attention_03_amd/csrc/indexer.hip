@@ -40,26 +40,30 @@ template <int KFMT> struct RawKeys {
   float own_scale;       // FP8 scale of the key this lane scores (tile g, key c)
 };
 
+// Page ids of the chunk's logical pages, staged in LDS once per workgroup so a
+// round's key loads never wait on a block-table load.
+constexpr int kIdxMaxChunkPages = 4096 / 16 + 1;
+
 template <int KFMT>
-__device__ __forceinline__ void load_round(const IndexerParams& p, int r, int base, int kend, int wave, int g,
-                                           int c, int P, RawKeys<KFMT>& raw) {
+__device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg_lds, int lp0, int base, int kend,
+                                           int wave, int g, int c, int P, RawKeys<KFMT>& raw) {
   raw.own_scale = 1.f;
 #pragma unroll
   for (int kt = 0; kt < kIdxKT; ++kt) {
     const int s0 = base + (wave * kIdxKT + kt) * 16;
     int pg = -1;
-    if (s0 < kend) pg = phys_page(p.block_table, p.bt_stride, r, s0 >> p.plog2, p.num_pages);
+    if (s0 < kend) pg = pg_lds[(s0 >> p.plog2) - lp0];
     raw.ok[kt] = pg >= 0;
     if (pg >= 0) {
       const uint8_t* page = p.keys + (int64_t)pg * p.page_bytes;
       const int slot = (s0 & (P - 1)) + c;
       if (KFMT == DSA_KEY_FP8) {
         const uint8_t* kp = page + slot * 128 + 32 * g;
-        raw.v[kt][0] = ld16_stream(kp);
-        raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16_stream(kp + 16);
+        raw.v[kt][0] = ld16(kp);
+        raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16(kp + 16);
         if (kt == g) raw.own_scale = *reinterpret_cast<const float*>(page + P * 128 + slot * 4);
       } else {
-        raw.v[kt][0] = ld16_stream(page + slot * 64 + 16 * g);
+        raw.v[kt][0] = ld16(page + slot * 64 + 16 * g);
         raw.sc[kt] = page[P * 64 + slot * 4 + g];
       }
     }
@@ -105,6 +109,7 @@ template <int KFMT>
 __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   extern __shared__ __attribute__((aligned(16))) __bf16 qs[];  // [rows][32][kQPad] bf16, then [rows][32] fp32 w
   __shared__ int s_vmax[kIdxWaves];
+  __shared__ int pg_lds[kIdxMaxChunkPages];
 
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
@@ -124,6 +129,9 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   if (k0 >= vmax) return;
   const int kend = min(k0 + p.chunk, vmax);
   const int P = 1 << p.plog2;
+  const int lp0 = k0 >> p.plog2;
+  for (int i = tid; i <= ((kend - 1) >> p.plog2) - lp0; i += 256)
+    pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
   float* ws = reinterpret_cast<float*>(qs + p.qrows * 32 * kQPad);
 
   for (int t0 = rs; t0 < re; t0 += p.qrows) {
@@ -139,64 +147,166 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
 
     // Software pipeline: the raw key bytes of round i+1 are in flight while
     // round i is dequantised and multiplied.
-    RawKeys<KFMT> raw;
-    load_round<KFMT>(p, r, k0, kend, wave, g, c, P, raw);
-    for (int base = k0; base < kend; base += kIdxRound) {
-      bf16x8 bfr[kIdxKT][4];
-      const float own_mul = dequant_round<KFMT>(raw, g, bfr);
-      if (base + kIdxRound < kend) load_round<KFMT>(p, r, base + kIdxRound, kend, wave, g, c, P, raw);
-      const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
-
-      for (int j = 0; j < nr; ++j) {
-        const int t = t0 + j;
-        const int vis = min(p.tok_vis[t], p.max_vis);
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 4 * g]);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 16 + 4 * g]);
-        f32x4 acc[kIdxKT][2];
-        const __bf16* qrow = &qs[(j * 32) * kQPad];
+    auto mfma_row = [&](int j, const bf16x8 (&bfr)[kIdxKT][4], f32x4 (&acc)[kIdxKT][2]) {
+      const __bf16* qrow = &qs[(j * 32) * kQPad];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qrow[c * kQPad + 32 * g + 8 * kk]);
-          const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qrow[(16 + c) * kQPad + 32 * g + 8 * kk]);
-#pragma unroll
-          for (int kt = 0; kt < kIdxKT; ++kt) {
-            if (kk == 0) {
-              acc[kt][0] = mfma16x16x32(a0, bfr[kt][0], f32x4{0.f, 0.f, 0.f, 0.f});
-              acc[kt][1] = mfma16x16x32(a1, bfr[kt][0], f32x4{0.f, 0.f, 0.f, 0.f});
-            } else {
-              acc[kt][0] = mfma16x16x32(a0, bfr[kt][kk], acc[kt][0]);
-              acc[kt][1] = mfma16x16x32(a1, bfr[kt][kk], acc[kt][1]);
-            }
-          }
-        }
-        // ReLU-weighted head sum: 8 heads in-lane, then a reduce-scatter over
-        // the four lane groups leaves lane (g, c) with key c of tile g
-        float v[kIdxKT];
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qrow[c * kQPad + 32 * g + 8 * kk]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qrow[(16 + c) * kQPad + 32 * g + 8 * kk]);
 #pragma unroll
         for (int kt = 0; kt < kIdxKT; ++kt) {
-          float x = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x += w0[i] * fmaxf(acc[kt][0][i], 0.f);
-            x += w1[i] * fmaxf(acc[kt][1][i], 0.f);
+          if (kk == 0) {
+            acc[kt][0] = mfma16x16x32(a0, bfr[kt][0], f32x4{0.f, 0.f, 0.f, 0.f});
+            acc[kt][1] = mfma16x16x32(a1, bfr[kt][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          } else {
+            acc[kt][0] = mfma16x16x32(a0, bfr[kt][kk], acc[kt][0]);
+            acc[kt][1] = mfma16x16x32(a1, bfr[kt][kk], acc[kt][1]);
           }
-          v[kt] = x;
         }
-        const float tot = rows_reduce_scatter4(v, g);
-        if (s_own < kend && s_own < vis)
-          p.scores[(int64_t)t * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
       }
+    };
+    // ReLU-weighted head sum: 8 heads in-lane, then a reduce-scatter over the
+    // four lane groups leaves lane (g, c) with key c of tile g
+    auto epi_row = [&](int j, const f32x4 (&acc)[kIdxKT][2], int s_own, float own_mul) {
+      const int t = t0 + j;
+      const int vis = min(p.tok_vis[t], p.max_vis);
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 4 * g]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 16 + 4 * g]);
+      float v[kIdxKT];
+#pragma unroll
+      for (int kt = 0; kt < kIdxKT; ++kt) {
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x += w0[i] * fmaxf(acc[kt][0][i], 0.f);
+          x += w1[i] * fmaxf(acc[kt][1][i], 0.f);
+        }
+        v[kt] = x;
+      }
+      const float tot = rows_reduce_scatter4(v, g);
+      if (s_own < kend && s_own < vis)
+        p.scores[(int64_t)t * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
+    };
+    auto do_round = [&](int base, RawKeys<KFMT>& raw, int next) {
+      bf16x8 bfr[kIdxKT][4];
+      const float own_mul = dequant_round<KFMT>(raw, g, bfr);
+      if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
+      const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
+      f32x4 acc[kIdxKT][2];
+      for (int j = 0; j < nr; ++j) {
+        mfma_row(j, bfr, acc);
+        epi_row(j, acc, s_own, own_mul);
+      }
+    };
+
+    // Software pipeline: the raw key bytes of round i+1 are in flight while
+    // round i is dequantised and multiplied.
+    RawKeys<KFMT> raw;
+    load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
+    for (int base = k0; base < kend; base += kIdxRound) do_round(base, raw, base + kIdxRound);
+  }
+}
+
+// One query row per request (long-context decode): the row's query fragments
+// stay in registers (no LDS traffic), each key tile is dequantised just before
+// its eight MFMAs, and the kernel is small enough for three to four waves per
+// SIMD -- enough HBM requests in flight to stream the keys at full rate.
+template <int KFMT>
+__global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) {
+  __shared__ int pg_lds[kIdxMaxChunkPages];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int t = p.req_row_start[r];
+  if (p.req_row_start[r + 1] <= t) return;
+  const int vis = min(p.tok_vis[t], p.max_vis);
+  const int k0 = blockIdx.x * p.chunk;
+  if (k0 >= vis) return;
+  const int kend = min(k0 + p.chunk, vis);
+  const int P = 1 << p.plog2;
+  const int lp0 = k0 >> p.plog2;
+  for (int i = tid; i <= ((kend - 1) >> p.plog2) - lp0; i += 256)
+    pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
+
+  bf16x8 qa[2][4];
+  const __bf16* qrow = p.q + (int64_t)t * 32 * 128;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + 32 * g + 8 * kk));
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
+  __syncthreads();
+
+  RawKeys<KFMT> raw;
+  load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
+  for (int base = k0; base < kend; base += kIdxRound) {
+    RawKeys<KFMT> cur = raw;
+    if (base + kIdxRound < kend) load_round<KFMT>(p, pg_lds, lp0, base + kIdxRound, kend, wave, g, c, P, raw);
+    float v[kIdxKT];
+#pragma unroll
+    for (int kt = 0; kt < kIdxKT; ++kt) {
+      bf16x8 b[4];
+      if (cur.ok[kt]) {
+        if (KFMT == DSA_KEY_FP8) {
+          const i32x4 x = cur.v[kt][0], y = cur.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0];
+          b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
+          b[1] = e4m3x8_to_bf16x8(x[2], x[3]);
+          b[2] = e4m3x8_to_bf16x8(y[0], y[1]);
+          b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
+        } else {
+          const i32x4 x = cur.v[kt][0];
+          const float sc = e8m0_to_f32(cur.sc[kt]);
+          b[0] = e2m1x8_to_bf16x8(x[0], sc);
+          b[1] = e2m1x8_to_bf16x8(x[1], sc);
+          b[2] = e2m1x8_to_bf16x8(x[2], sc);
+          b[3] = e2m1x8_to_bf16x8(x[3], sc);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b[kk] = bf16x8{};
+      }
+      f32x4 a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int kk = 1; kk < 4; ++kk) {
+        a0 = mfma16x16x32(qa[0][kk], b[kk], a0);
+        a1 = mfma16x16x32(qa[1][kk], b[kk], a1);
+      }
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x += w0[i] * fmaxf(a0[i], 0.f);
+        x += w1[i] * fmaxf(a1[i], 0.f);
+      }
+      v[kt] = x;
     }
+    bool own_ok = cur.ok[0];
+#pragma unroll
+    for (int kt = 1; kt < kIdxKT; ++kt)
+      if (g == kt) own_ok = cur.ok[kt];
+    const float own_mul = own_ok ? (KFMT == DSA_KEY_FP8 ? cur.own_scale : 1.f) : -__builtin_inff();
+    const float tot = rows_reduce_scatter4(v, g);
+    const int s_own = base + wave * (kIdxKT * 16) + lane;
+    if (s_own < kend) p.scores[(int64_t)t * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
   }
 }
 
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
   dim3 grid((p.max_vis + p.chunk - 1) / p.chunk, p.R);
   const size_t lds = (size_t)p.qrows * 32 * (kQPad * sizeof(__bf16) + sizeof(float));
-  if (p.key_fmt == DSA_KEY_FP8)
+  if (p.max_rows_per_req == 1) {
+    if (p.key_fmt == DSA_KEY_FP8)
+      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_FP8>, grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_MXFP4>, grid, dim3(256), 0, stream, p);
+  } else if (p.key_fmt == DSA_KEY_FP8) {
     hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_FP8>, grid, dim3(256), lds, stream, p);
-  else
+  } else {
     hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_MXFP4>, grid, dim3(256), lds, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

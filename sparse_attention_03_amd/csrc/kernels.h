@@ -29,8 +29,9 @@ struct IndexerParams {
   const float* w;           // [T,32]
   float* scores;
   int64_t ld;
-  int chunk;                // keys per workgroup (BF16 path)
+  int chunk;                // keys per workgroup (a multiple of 256)
   int qrows;                // rows staged in LDS per pass (BF16 path)
+  int max_rows_per_req;
 };
 
 struct TopkParams {
