@@ -183,7 +183,8 @@ typedef struct dsa_mla_args {
   const int32_t* rows;           /* device int32 [T, k] physical rows           */
   int32_t k;                     /* 1 .. 2048                                   */
   float sm_scale;                /* softmax scale (finite, > 0)                 */
-  int32_t num_splits;            /* 0 = automatic, else 1 .. k/16 (decode)      */
+  int32_t num_splits;            /* 0 = automatic, else 1 .. k/16; at most 64
+                                    are used (decode)                           */
   float* out;                    /* device fp32 [T, H, 512]                     */
   float* lse;                    /* device fp32 [T, H] or NULL                  */
   void* workspace;               /* device, 256-byte aligned                    */

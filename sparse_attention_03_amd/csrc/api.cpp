@@ -107,7 +107,7 @@ MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
     const int64_t per_split = (int64_t)a.num_rows * groups;
     want = (int)std::min<int64_t>(64, std::max<int64_t>(1, resident / per_split));
   }
-  want = std::max(1, std::min(want, (a.k + 15) / 16));
+  want = std::max(1, std::min({want, (a.k + 15) / 16, 64}));
   pl.split_len = ((a.k + want - 1) / want + 15) / 16 * 16;
   pl.nsplit = (a.k + pl.split_len - 1) / pl.split_len;
   size_t off = 0;

@@ -337,28 +337,41 @@ __global__ __launch_bounds__(64 * NW) void mla_kernel(MlaParams p) {
   }
 }
 
+// Merge of the split partials of one (row, head): all split LSEs are read in
+// parallel, and the weighted sum over splits issues its loads back to back.
 __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
+  __shared__ float wsh[64];
+  __shared__ float red[2];
   const int h = blockIdx.x, t = blockIdx.y;
-  const int tid = threadIdx.x;
-  const float* pl = p.part_lse + (int64_t)t * p.nsplit * p.H + h;
-  float mx = -__builtin_inff();
-  for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, pl[(int64_t)s * p.H]);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = p.nsplit;  // <= 64
+  const float* pl = p.part_lse + (int64_t)t * ns * p.H + h;
+  const float ls = tid < ns ? pl[(int64_t)tid * p.H] : -__builtin_inff();
+  float mx = ls;
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  const float w = (ls == -__builtin_inff()) ? 0.f : __expf(ls - mx);
+  if (tid < 64) wsh[tid] = w;
+  float ws = w;  // all ns <= 64 weights live in wave 0
+  for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+  __syncthreads();
+  if (tid == 0) red[0] = ws;
+  __syncthreads();
+  const float tot = red[0];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
   if (mx != -__builtin_inff()) {
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float ls = pl[(int64_t)s * p.H];
-      if (ls == -__builtin_inff()) continue;
-      const float w = __expf(ls - mx);
-      wsum += w;
-      const f32x4 v =
-          *reinterpret_cast<const f32x4*>(p.part_o + (((int64_t)t * p.nsplit + s) * p.H + h) * 512 + 4 * tid);
-      acc += w * v;
+    const float* po = p.part_o + ((int64_t)t * ns * p.H + h) * 512 + 4 * tid;
+#pragma unroll 8
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (int64_t)s2 * p.H * 512);
+      acc += wsh[s2] * v;
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
   *reinterpret_cast<f32x4*>(p.out + ((int64_t)t * p.H + h) * 512 + 4 * tid) = acc * inv;
-  if (tid == 0 && p.lse) p.lse[(int64_t)t * p.H + h] = wsum > 0.f ? mx + __logf(wsum) : -__builtin_inff();
+  if (tid == 0 && p.lse) p.lse[(int64_t)t * p.H + h] = tot > 0.f ? mx + __logf(tot) : -__builtin_inff();
 }
 
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {

@@ -7,16 +7,16 @@
 // ascending index.  It is emitted in ascending index order.
 //
 // Two passes over the scores of a row, each spread over many workgroups:
-//   1. histogram of the top 12 bits of the order-preserving uint32 key, then
-//      (one small workgroup per row) the threshold bin b holding rank K;
-//   2. every slice gathers keys above b ("definite", fewer than K in total)
+//   1. histogram of the top 12 bits of the order-preserving uint32 key;
+//   2. every slice finds the threshold bin b holding rank K from the row's
+//      histogram and gathers keys above b ("definite", fewer than K in total)
 //      and keys inside b ("candidates") in LDS and appends them to per-row
 //      buffers behind one global atomic per list;
 //   3. one workgroup per row refines the candidates (in LDS) with an exact
 //      radix select on the 56-bit composite (low 20 key bits, then inverted
-//      index), so ties resolve to the lower index, then sorts the K winners
-//      by index (bitonic, in LDS) and writes indices, physical rows and the
-//      count.
+//      index), so ties resolve to the lower index, then orders the K winners
+//      by index through an LDS bitmap (popcount prefix sums) and writes
+//      indices, physical rows and the count.
 // If a row's candidates overflow their buffer, step 3 reads them straight
 // from the score row instead (slower, same result).
 #include "common.h"
@@ -48,14 +48,21 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
   for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
   __syncthreads();
   const float* row = p.scores + (int64_t)t * p.ld;
-  for (int s = s_begin + 4 * threadIdx.x; s < s_end; s += 1024) {
-    if (s + 3 < s_end) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + s);
+  // the whole slice (8 float4 per thread) is loaded before any is binned
+  f32x4 v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&h[order_key(v[e]) >> kBinShift], 1u);
-    } else {
-      for (int e = 0; s + e < s_end; ++e) atomicAdd(&h[order_key(row[s + e]) >> kBinShift], 1u);
-    }
+  for (int b = 0; b < 8; ++b) {
+    const int s = s_begin + 4 * threadIdx.x + 1024 * b;
+    v[b] = (s + 3 < s_end) ? *reinterpret_cast<const f32x4*>(row + s) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s + 3 >= s_end)
+      for (int e = 0; e < 4; ++e) v[b][e] = (s + e < s_end) ? row[s + e] : 0.f;
+  }
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int s = s_begin + 4 * threadIdx.x + 1024 * b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (s + e < s_end) atomicAdd(&h[order_key(v[b][e]) >> kBinShift], 1u);
   }
   __syncthreads();
   uint32_t* gh = p.hist + (int64_t)t * kBins;
@@ -63,15 +70,16 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Threshold bin of each row from its global histogram: the bin b with
-// count(bins > b) < k <= count(bins >= b); stores b and need = k - count(> b)
-// in ctr[2], ctr[3].  One 256-thread workgroup per row.
-__global__ __launch_bounds__(256) void topk_threshold_kernel(TopkParams p) {
-  __shared__ uint32_t part[256];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (row_vis(p, t) <= p.k) return;
-  const uint32_t* gh = p.hist + (int64_t)t * kBins;
+// Threshold bin of a row from its global histogram: the bin b with
+// count(bins > b) < k <= count(bins >= b); returns b and need = k - count(> b).
+// Called by all 256 threads of a workgroup; 16 bins per thread, suffix sums
+// with wave shuffles and one LDS exchange.
+__device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, uint32_t k, int* out_bin,
+                                              uint32_t* out_need) {
+  __shared__ uint32_t wtot[4];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_need;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t loc[16];
   uint32_t sum = 0;
 #pragma unroll
@@ -79,27 +87,29 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(TopkParams p) {
     loc[i] = gh[tid * 16 + i];
     sum += loc[i];
   }
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive suffix scan over threads
-    const uint32_t v = (tid + off < 256) ? part[tid + off] : 0u;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  uint32_t suf = sum;  // inclusive suffix sum within the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off);
+    if (lane + off < 64) suf += o;
   }
-  const uint32_t above = part[tid] - sum;  // counts in bins owned by higher threads
-  const uint32_t k = (uint32_t)p.k;
-  if (above < k && above + sum >= k) {
+  if (lane == 0) wtot[wave] = suf;
+  __syncthreads();
+  for (int w = wave + 1; w < 4; ++w) suf += wtot[w];
+  const uint32_t above = suf - sum;  // bins owned by higher threads
+  if (above < k && suf >= k) {
     uint32_t acc = above;
     for (int i = 15; i >= 0; --i) {
       if (acc + loc[i] >= k) {
-        p.ctr[(int64_t)t * 4 + 2] = (uint32_t)(tid * 16 + i);
-        p.ctr[(int64_t)t * 4 + 3] = k - acc;
+        s_bin = tid * 16 + i;
+        s_need = k - acc;
         break;
       }
       acc += loc[i];
     }
   }
+  __syncthreads();
+  *out_bin = s_bin;
+  *out_need = s_need;
 }
 
 constexpr int kFilterCap = 2048;  // candidates a filter workgroup keeps in LDS
@@ -120,25 +130,36 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
   if (s_begin >= vis) return;
   const int s_end = min(s_begin + p.slice, vis);
   uint32_t* ctr = p.ctr + (int64_t)t * 4;
-  const uint32_t bin = ctr[2];
   if (tid == 0) {
     n_def = 0;
     n_cand = 0;
     n_cand2 = 0;
   }
-  __syncthreads();
+  int ibin;
+  uint32_t need;
+  threshold_bin(p.hist + (int64_t)t * kBins, (uint32_t)p.k, &ibin, &need);
+  const uint32_t bin = (uint32_t)ibin;
+  if (blockIdx.x == 0 && tid == 0) {
+    ctr[2] = bin;
+    ctr[3] = need;
+  }
   const float* row = p.scores + (int64_t)t * p.ld;
-  for (int s = s_begin + 4 * tid; s < s_end; s += 1024) {
-    f32x4 v;
-    if (s + 3 < s_end) {
-      v = *reinterpret_cast<const f32x4*>(row + s);
-    } else {
-      for (int e = 0; e < 4; ++e) v[e] = (s + e < s_end) ? row[s + e] : -__builtin_inff();
-    }
+  f32x4 v[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int s = s_begin + 4 * tid + 1024 * b;
+    v[b] = (s + 3 < s_end) ? *reinterpret_cast<const f32x4*>(row + s) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s + 3 >= s_end)
+      for (int e = 0; e < 4; ++e) v[b][e] = (s + e < s_end) ? row[s + e] : 0.f;
+  }
+  __syncthreads();  // counters initialised
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int s = s_begin + 4 * tid + 1024 * b;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (s + e >= s_end) break;
-      const uint32_t key = order_key(v[e]);
+      const uint32_t key = order_key(v[b][e]);
       const uint32_t d = key >> kBinShift;
       if (d > bin) {
         const int pos = atomicAdd(&n_def, 1);
@@ -206,12 +227,14 @@ __device__ __forceinline__ int translate_one(int li, int r, const int32_t* __res
 }
 
 constexpr int kFinalCap = 4096;  // candidates the finalize workgroup refines in LDS
+constexpr int kWinIdx = 1024 * 8 * 32;  // indices per bitmap window (8 words per thread)
 
 __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   __shared__ int out[DSA_MAX_TOPK];
-  __shared__ uint32_t ck[kFinalCap];
-  __shared__ uint32_t ci[kFinalCap];
-  __shared__ uint32_t h[256];
+  __shared__ uint32_t cand_lds[2 * kFinalCap];  // candidate keys, candidate indices; later the bitmap
+  uint32_t* ck = cand_lds;
+  uint32_t* ci = cand_lds + kFinalCap;
+  __shared__ uint32_t h[256];  // radix bins; later the 16 wave totals
   __shared__ uint32_t wsum[4];
   __shared__ uint64_t s_prefix;
   __shared__ int s_need, s_done, s_cnt;
@@ -322,27 +345,57 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
     }
   }
   __syncthreads();
-  for (int i = K + tid; i < DSA_MAX_TOPK; i += blockDim.x) out[i] = 0x7FFFFFFF;
-  __syncthreads();
-  // bitonic sort, ascending
-  for (int size = 2; size <= DSA_MAX_TOPK; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < DSA_MAX_TOPK / 2; i += blockDim.x) {
-        const int pos = 2 * i - (i & (stride - 1));
-        const int a = out[pos], b = out[pos + stride];
-        const bool up = (pos & size) == 0;
-        if ((a > b) == up) {
-          out[pos] = b;
-          out[pos + stride] = a;
-        }
-      }
-      __syncthreads();
+  // order the K winners by index: mark them in an LDS bitmap window by window
+  // (256K indices per window), then each thread emits the set bits of its 8
+  // words at its prefix-sum offset
+  uint32_t* bm = cand_lds;  // the candidate area (8192 words) is free now
+  int emitted = 0;
+  for (int w0 = 0; w0 < vis; w0 += kWinIdx) {
+    for (int i = tid; i < kWinIdx / 32; i += blockDim.x) bm[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < K; i += blockDim.x) {
+      const int li = out[i] - w0;
+      if (li >= 0 && li < kWinIdx) atomicOr(&bm[li >> 5], 1u << (li & 31));
     }
+    __syncthreads();
+    uint32_t words[8];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      words[i] = bm[tid * 8 + i];
+      cnt += __popc(words[i]);
+    }
+    // exclusive prefix over the 1024 threads: waves of 64, then 16 wave totals
+    const int lane = tid & 63, wave = tid >> 6;
+    int inc = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    if (lane == 63) h[wave] = (uint32_t)inc;
+    __syncthreads();
+    int before = emitted + inc - cnt;
+    for (int w = 0; w < wave; ++w) before += (int)h[w];
+    int tot = 0;
+    for (int w = 0; w < 16; ++w) tot += (int)h[w];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t x = words[i];
+      while (x) {
+        const int b = __ffs(x) - 1;
+        x &= x - 1;
+        const int li = w0 + (tid * 8 + i) * 32 + b;
+        idx[before] = li;
+        if (rows) rows[before] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+        ++before;
+      }
+    }
+    emitted += tot;
+    __syncthreads();
   }
-  for (int j = tid; j < p.k; j += blockDim.x) {
-    const int li = j < K ? out[j] : -1;
-    idx[j] = li;
-    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+  for (int j = K + tid; j < p.k; j += blockDim.x) {
+    idx[j] = -1;
+    if (rows) rows[j] = -1;
   }
   if (p.count && tid == 0) p.count[t] = K;
 }
@@ -357,14 +410,12 @@ __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, 
 }
 
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
-  const int64_t nz = (int64_t)p.T * kBins;
+  // histograms and counters are contiguous in the workspace: one fill
+  const int64_t nz = (int64_t)(p.ctr - p.hist) + (int64_t)p.T * 4;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0,
                      stream, p.hist, nz, 0u);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>((p.T * 4 + 255) / 256, 4096)), dim3(256), 0,
-                     stream, p.ctr, (int64_t)p.T * 4, 0u);
   dim3 grid(p.nslices, p.T);
   hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.T), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(256), 0, stream, p);
   hipLaunchKernelGGL(topk_finalize_kernel, dim3(p.T), dim3(1024), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
