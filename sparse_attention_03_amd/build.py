@@ -16,6 +16,8 @@ SOURCES = ["api.cpp", "indexer.hip", "indexer_fp8.hip", "topk.hip", "mla.hip"]
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results in ordinary VGPRs: no accvgpr copies before the VALU epilogues
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wno-unused-command-line-argument"]
 
 

@@ -139,6 +139,10 @@ __device__ __forceinline__ int phys_page(const int32_t* __restrict__ bt, int bt_
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0.0 is
 // mapped as +0.0.
+// max(x, 0) on the bit pattern: non-negative floats are the non-negative
+// int32 patterns, so one integer max is the ReLU (no NaN canonicalisation).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) == 0) u = 0;

@@ -43,30 +43,45 @@ template <int KFMT> struct RawKeys {
 // Page ids of the chunk's logical pages, staged in LDS once per workgroup so a
 // round's key loads never wait on a block-table load.
 constexpr int kIdxMaxChunkPages = 4096 / 16 + 1;
+constexpr int kIdxMaxRows = 8;  // rows staged in LDS per pass (qrows)
 
+// Every load is issued unconditionally (a tile past the chunk end or on an
+// absent page reads page 0 instead and its scores are masked afterwards):
+// loads under a branch would make the compiler wait for all of them before
+// any is used, so the next round's loads could not overlap this round.
 template <int KFMT>
 __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg_lds, int lp0, int base, int kend,
                                            int wave, int g, int c, int P, RawKeys<KFMT>& raw) {
-  raw.own_scale = 1.f;
+  const int last = ((kend - 1) >> p.plog2) - lp0;  // last staged page entry
+  int pgs[kIdxKT];
 #pragma unroll
   for (int kt = 0; kt < kIdxKT; ++kt) {
     const int s0 = base + (wave * kIdxKT + kt) * 16;
-    int pg = -1;
-    if (s0 < kend) pg = pg_lds[(s0 >> p.plog2) - lp0];
+    const int e = min((s0 >> p.plog2) - lp0, last);
+    const int pg = s0 < kend ? pg_lds[e] : -1;
+    pgs[kt] = pg;
     raw.ok[kt] = pg >= 0;
-    if (pg >= 0) {
-      const uint8_t* page = p.keys + (int64_t)pg * p.page_bytes;
-      const int slot = (s0 & (P - 1)) + c;
-      if (KFMT == DSA_KEY_FP8) {
-        const uint8_t* kp = page + slot * 128 + 32 * g;
-        raw.v[kt][0] = ld16(kp);
-        raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16(kp + 16);
-        if (kt == g) raw.own_scale = *reinterpret_cast<const float*>(page + P * 128 + slot * 4);
-      } else {
-        raw.v[kt][0] = ld16(page + slot * 64 + 16 * g);
-        raw.sc[kt] = page[P * 64 + slot * 4 + g];
-      }
+    const uint8_t* page = p.keys + (int64_t)max(pg, 0) * p.page_bytes;
+    const int slot = (s0 & (P - 1)) + c;
+    if (KFMT == DSA_KEY_FP8) {
+      const uint8_t* kp = page + slot * 128 + 32 * g;
+      raw.v[kt][0] = ld16(kp);
+      raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16(kp + 16);
+    } else {
+      raw.v[kt][0] = ld16(page + slot * 64 + 16 * g);
+      raw.sc[kt] = page[P * 64 + slot * 4 + g];
     }
+  }
+  if (KFMT == DSA_KEY_FP8) {
+    // the scale of the key this lane stores (tile g, key c)
+    int pg = pgs[0];
+#pragma unroll
+    for (int kt = 1; kt < kIdxKT; ++kt)
+      if (g == kt) pg = pgs[kt];
+    const int slot = ((base + (wave * kIdxKT + g) * 16) & (P - 1)) + c;
+    raw.own_scale = *reinterpret_cast<const float*>(p.keys + (int64_t)max(pg, 0) * p.page_bytes + P * 128 + slot * 4);
+  } else {
+    raw.own_scale = 1.f;
   }
 }
 
@@ -75,40 +90,42 @@ __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg
 // power-of-two block scales are applied exactly during dequantisation), or
 // -inf for an absent page so the key is never selected.
 template <int KFMT>
-__device__ __forceinline__ float dequant_round(const RawKeys<KFMT>& raw, int g, bf16x8 (&bfr)[kIdxKT][4]) {
-#pragma unroll
-  for (int kt = 0; kt < kIdxKT; ++kt) {
-    if (raw.ok[kt]) {
-      if (KFMT == DSA_KEY_FP8) {
-        const i32x4 a = raw.v[kt][0], b = raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0];
-        bfr[kt][0] = e4m3x8_to_bf16x8(a[0], a[1]);
-        bfr[kt][1] = e4m3x8_to_bf16x8(a[2], a[3]);
-        bfr[kt][2] = e4m3x8_to_bf16x8(b[0], b[1]);
-        bfr[kt][3] = e4m3x8_to_bf16x8(b[2], b[3]);
-      } else {
-        const i32x4 a = raw.v[kt][0];
-        const float sc = e8m0_to_f32(raw.sc[kt]);
-        bfr[kt][0] = e2m1x8_to_bf16x8(a[0], sc);
-        bfr[kt][1] = e2m1x8_to_bf16x8(a[1], sc);
-        bfr[kt][2] = e2m1x8_to_bf16x8(a[2], sc);
-        bfr[kt][3] = e2m1x8_to_bf16x8(a[3], sc);
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) bfr[kt][kk] = bf16x8{};
-    }
+__device__ __forceinline__ void dequant_tile(const RawKeys<KFMT>& raw, int kt, bf16x8 (&b)[4]) {
+  if (KFMT == DSA_KEY_FP8) {
+    const i32x4 x = raw.v[kt][0], y = raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0];
+    b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
+    b[1] = e4m3x8_to_bf16x8(x[2], x[3]);
+    b[2] = e4m3x8_to_bf16x8(y[0], y[1]);
+    b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
+  } else {
+    const i32x4 x = raw.v[kt][0];
+    const float sc = e8m0_to_f32(raw.sc[kt]);
+    b[0] = e2m1x8_to_bf16x8(x[0], sc);
+    b[1] = e2m1x8_to_bf16x8(x[1], sc);
+    b[2] = e2m1x8_to_bf16x8(x[2], sc);
+    b[3] = e2m1x8_to_bf16x8(x[3], sc);
   }
+}
+
+// Multiplier of the score this lane stores (key c of tile g): the FP8 key
+// scale, 1 for MXFP4 (whose power-of-two block scales are applied exactly
+// during dequantisation), or -inf for an absent page so the key is never
+// selected.  A tile on an absent page holds page 0's bytes; every score it
+// produces is replaced by this -inf.
+template <int KFMT>
+__device__ __forceinline__ float own_multiplier(const RawKeys<KFMT>& raw, int g) {
   bool own_ok = raw.ok[0];
 #pragma unroll
   for (int kt = 1; kt < kIdxKT; ++kt)
     if (g == kt) own_ok = raw.ok[kt];
-  return own_ok ? (KFMT == DSA_KEY_FP8 ? raw.own_scale : 1.f) : -__builtin_inff();
+  return own_ok ? raw.own_scale : -__builtin_inff();
 }
 
 template <int KFMT>
 __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   extern __shared__ __attribute__((aligned(16))) __bf16 qs[];  // [rows][32][kQPad] bf16, then [rows][32] fp32 w
   __shared__ int s_vmax[kIdxWaves];
+  __shared__ int s_vis[kIdxMaxRows];
   __shared__ int pg_lds[kIdxMaxChunkPages];
 
   const int r = blockIdx.y;
@@ -143,6 +160,9 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
       *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = v;
     }
     for (int i = tid; i < nr * 32; i += 256) ws[i] = p.w[(int64_t)t0 * 32 + i];
+    // visible counts of the pass's rows, read from LDS in the row loop: a
+    // global load there would make every row wait for the next round's keys
+    if (tid < nr) s_vis[tid] = min(p.tok_vis[t0 + tid], p.max_vis);
     __syncthreads();
 
     // Software pipeline: the raw key bytes of round i+1 are in flight while
@@ -169,7 +189,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
     // four lane groups leaves lane (g, c) with key c of tile g
     auto epi_row = [&](int j, const f32x4 (&acc)[kIdxKT][2], int s_own, float own_mul) {
       const int t = t0 + j;
-      const int vis = min(p.tok_vis[t], p.max_vis);
+      const int vis = s_vis[j];
       const f32x4 w0 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 4 * g]);
       const f32x4 w1 = *reinterpret_cast<const f32x4*>(&ws[j * 32 + 16 + 4 * g]);
       float v[kIdxKT];
@@ -178,8 +198,8 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
         float x = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x += w0[i] * fmaxf(acc[kt][0][i], 0.f);
-          x += w1[i] * fmaxf(acc[kt][1][i], 0.f);
+          x += w0[i] * relu(acc[kt][0][i]);
+          x += w1[i] * relu(acc[kt][1][i]);
         }
         v[kt] = x;
       }
@@ -189,7 +209,9 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
     };
     auto do_round = [&](int base, RawKeys<KFMT>& raw, int next) {
       bf16x8 bfr[kIdxKT][4];
-      const float own_mul = dequant_round<KFMT>(raw, g, bfr);
+#pragma unroll
+      for (int kt = 0; kt < kIdxKT; ++kt) dequant_tile<KFMT>(raw, kt, bfr[kt]);
+      const float own_mul = own_multiplier<KFMT>(raw, g);
       if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
       const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
       f32x4 acc[kIdxKT][2];
@@ -240,34 +262,13 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
   const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
   __syncthreads();
 
-  RawKeys<KFMT> raw;
-  load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
-  for (int base = k0; base < kend; base += kIdxRound) {
-    RawKeys<KFMT> cur = raw;
-    if (base + kIdxRound < kend) load_round<KFMT>(p, pg_lds, lp0, base + kIdxRound, kend, wave, g, c, P, raw);
+  // two raw buffers: the keys of the next round load while this one computes
+  auto round = [&](int base, const RawKeys<KFMT>& cur) {
     float v[kIdxKT];
 #pragma unroll
     for (int kt = 0; kt < kIdxKT; ++kt) {
       bf16x8 b[4];
-      if (cur.ok[kt]) {
-        if (KFMT == DSA_KEY_FP8) {
-          const i32x4 x = cur.v[kt][0], y = cur.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0];
-          b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
-          b[1] = e4m3x8_to_bf16x8(x[2], x[3]);
-          b[2] = e4m3x8_to_bf16x8(y[0], y[1]);
-          b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
-        } else {
-          const i32x4 x = cur.v[kt][0];
-          const float sc = e8m0_to_f32(cur.sc[kt]);
-          b[0] = e2m1x8_to_bf16x8(x[0], sc);
-          b[1] = e2m1x8_to_bf16x8(x[1], sc);
-          b[2] = e2m1x8_to_bf16x8(x[2], sc);
-          b[3] = e2m1x8_to_bf16x8(x[3], sc);
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b[kk] = bf16x8{};
-      }
+      dequant_tile<KFMT>(cur, kt, b);
       f32x4 a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -278,19 +279,29 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
       float x = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x += w0[i] * fmaxf(a0[i], 0.f);
-        x += w1[i] * fmaxf(a1[i], 0.f);
+        x += w0[i] * relu(a0[i]);
+        x += w1[i] * relu(a1[i]);
       }
       v[kt] = x;
     }
-    bool own_ok = cur.ok[0];
-#pragma unroll
-    for (int kt = 1; kt < kIdxKT; ++kt)
-      if (g == kt) own_ok = cur.ok[kt];
-    const float own_mul = own_ok ? (KFMT == DSA_KEY_FP8 ? cur.own_scale : 1.f) : -__builtin_inff();
+    const float own_mul = own_multiplier<KFMT>(cur, g);
     const float tot = rows_reduce_scatter4(v, g);
     const int s_own = base + wave * (kIdxKT * 16) + lane;
     if (s_own < kend) p.scores[(int64_t)t * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
+  };
+  // Loads past the last round re-read the last round (cache hits), so every
+  // iteration issues the same loads and the waits for a buffer never cover
+  // the other one.
+  const int last_base = k0 + (kend - 1 - k0) / kIdxRound * kIdxRound;
+  RawKeys<KFMT> ra, rb;
+  load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, ra);
+  for (int base = k0; base < kend; base += 2 * kIdxRound) {
+    const int b1 = base + kIdxRound, b2 = base + 2 * kIdxRound;
+    load_round<KFMT>(p, pg_lds, lp0, min(b1, last_base), kend, wave, g, c, P, rb);
+    round(base, ra);
+    if (b1 >= kend) break;
+    load_round<KFMT>(p, pg_lds, lp0, min(b2, last_base), kend, wave, g, c, P, ra);
+    round(b1, rb);
   }
 }
 

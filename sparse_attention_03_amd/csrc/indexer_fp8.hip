@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
           float x = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            x += wv[j][0][i] * fmaxf(acc[kt][0][i], 0.f);
-            x += wv[j][1][i] * fmaxf(acc[kt][1][i], 0.f);
+            x += wv[j][0][i] * relu(acc[kt][0][i]);
+            x += wv[j][1][i] * relu(acc[kt][1][i]);
           }
           v[kt] = x;
         }
