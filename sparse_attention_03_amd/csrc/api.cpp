@@ -228,12 +228,15 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
   p.ld = a->ld;
   if (a->q_fmt == DSA_Q_BF16) {
     p.q = static_cast<const __bf16*>(a->q);
-    // keys per workgroup: enough workgroups to fill 256 CUs, at most 4096 keys
-    int64_t target = (int64_t)b.max_vis * b.num_requests / 2048;
+    // keys per workgroup, at most 4096.  Single-row requests stream keys and
+    // want many workgroups in flight (about 2048); multi-row requests stage
+    // their rows once per workgroup, so fewer, longer workgroups (about 512,
+    // two per CU) amortise that.
+    int64_t target = (int64_t)b.max_vis * b.num_requests / (b.max_rows_per_req == 1 ? 2048 : 512);
     int chunk = 256;
     while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
     p.chunk = chunk;
-    p.qrows = std::min(b.max_rows_per_req, 6);
+    p.qrows = std::min(b.max_rows_per_req, dsa::kIndexerMaxRowsPerPass);
     p.max_rows_per_req = b.max_rows_per_req;
     st = dsa::launch_indexer_bf16(p, stream);
   } else {

@@ -43,7 +43,7 @@ template <int KFMT> struct RawKeys {
 // Page ids of the chunk's logical pages, staged in LDS once per workgroup so a
 // round's key loads never wait on a block-table load.
 constexpr int kIdxMaxChunkPages = 4096 / 16 + 1;
-constexpr int kIdxMaxRows = 8;  // rows staged in LDS per pass (qrows)
+constexpr int kIdxMaxRows = kIndexerMaxRowsPerPass;  // rows staged in LDS per pass (qrows)
 
 // Every load is issued unconditionally (a tile past the chunk end or on an
 // absent page reads page 0 instead and its scores are masked afterwards):
@@ -133,6 +133,39 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int rs = p.req_row_start[r], re = p.req_row_start[r + 1];
+  float* ws = reinterpret_cast<float*>(qs + p.qrows * 32 * kQPad);
+
+  // Rows of a pass are staged with every load issued before the first LDS
+  // store (one memory round trip, not one per load); the first pass's loads
+  // are issued before the visible-range and page-table reads they do not
+  // depend on.
+  constexpr int kQLoads = kIdxMaxRows * 512 / 256;
+  i32x4 qv[kQLoads];
+  float wv = 0.f;
+  int vv = 0;
+  auto load_rows = [&](int t0, int nr) {
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+      const int i = tid + 256 * u;
+      const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
+      if (i < nr * 512) qv[u] = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
+    }
+    if (tid < nr * 32) wv = p.w[(int64_t)t0 * 32 + tid];
+    if (tid < nr) vv = min(p.tok_vis[t0 + tid], p.max_vis);
+  };
+  auto store_rows = [&](int nr) {
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+      const int i = tid + 256 * u;
+      const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
+      if (i < nr * 512) *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = qv[u];
+    }
+    if (tid < nr * 32) ws[tid] = wv;
+    // visible counts of the pass's rows, read from LDS in the row loop: a
+    // global load there would make every row wait for the next round's keys
+    if (tid < nr) s_vis[tid] = vv;
+  };
+  load_rows(rs, min(p.qrows, re - rs));
 
   // largest visible count among the request's rows
   int vm = 0;
@@ -149,20 +182,10 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   const int lp0 = k0 >> p.plog2;
   for (int i = tid; i <= ((kend - 1) >> p.plog2) - lp0; i += 256)
     pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
-  float* ws = reinterpret_cast<float*>(qs + p.qrows * 32 * kQPad);
 
-  for (int t0 = rs; t0 < re; t0 += p.qrows) {
+  store_rows(min(p.qrows, re - rs));
+  for (int t0 = rs;;) {
     const int nr = min(p.qrows, re - t0);
-    __syncthreads();
-    for (int i = tid; i < nr * 512; i += 256) {
-      const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
-      i32x4 v = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
-      *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = v;
-    }
-    for (int i = tid; i < nr * 32; i += 256) ws[i] = p.w[(int64_t)t0 * 32 + i];
-    // visible counts of the pass's rows, read from LDS in the row loop: a
-    // global load there would make every row wait for the next round's keys
-    if (tid < nr) s_vis[tid] = min(p.tok_vis[t0 + tid], p.max_vis);
     __syncthreads();
 
     // Software pipeline: the raw key bytes of round i+1 are in flight while
@@ -226,6 +249,30 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
     RawKeys<KFMT> raw;
     load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
     for (int base = k0; base < kend; base += kIdxRound) do_round(base, raw, base + kIdxRound);
+
+    t0 += p.qrows;
+    if (t0 >= re) break;
+    __syncthreads();  // every wave is done with this pass's rows
+    // later passes (more rows than one pass holds): batches of four loads,
+    // which keeps the registers of the round loop free
+    const int nr2 = min(p.qrows, re - t0);
+    for (int u0 = 0; u0 < kQLoads; u0 += 4) {
+      i32x4 b4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * (u0 + u);
+        const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
+        if (i < nr2 * 512) b4[u] = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * (u0 + u);
+        const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
+        if (i < nr2 * 512) *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = b4[u];
+      }
+    }
+    if (tid < nr2 * 32) ws[tid] = p.w[(int64_t)t0 * 32 + tid];
+    if (tid < nr2) s_vis[tid] = min(p.tok_vis[t0 + tid], p.max_vis);
   }
 }
 

@@ -8,6 +8,9 @@
 
 namespace dsa {
 
+// Query rows of a request the BF16 indexer stages in LDS per pass.
+constexpr int kIndexerMaxRowsPerPass = 6;
+
 struct IndexerParams {
   int R, T;
   const int32_t* req_row_start;
