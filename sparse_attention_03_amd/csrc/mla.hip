@@ -140,6 +140,116 @@ __device__ __forceinline__ void seg_store(__bf16* lrow, int s0, int q, const i32
   }
 }
 
+// One 16-row tile for one 16-head tile: QK from the LDS tile, online softmax
+// (lazy rescale), PV into the accumulators.  rv/rsc: row ids (-1 = absent)
+// and per-row value multipliers of the tile.
+__device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, const float* rsc, const int* rv,
+                                         const bf16x8 (&qf)[18], f32x4 (&O)[32], float& m, float& l, int g, int c) {
+  // ---- QK: S^T tile, rows 4g + i of head c
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  {
+    const __bf16* lrow = &lat[c * kLPad];
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lrow + dim_of(kk, g));
+      s = mfma16x16x32(a, qf[kk], s);
+    }
+  }
+  // ---- online softmax for head c
+  float lg[4], rs[4];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i;
+    const float sc = rsc[row];
+    rs[i] = sc;
+    const float v = rv[row] >= 0 ? s[i] * p.sm_log2 * sc : -__builtin_inff();
+    lg[i] = v;
+    tmax = fmaxf(tmax, v);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  // lazy rescaling: keep a stale max while the tile stays within 2^8 of it
+  // (weights stay <= 256); both O and l use the same max, so the final
+  // normalisation is exact
+  const float mnew = (m == -__builtin_inff() || tmax > m + kRescaleLog2) ? tmax : m;
+  const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - mnew);
+  float psum = 0.f;
+  float pw[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const float e = (lg[x] == -__builtin_inff() || mnew == -__builtin_inff()) ? 0.f : exp2f(lg[x] - mnew);
+    psum += e;
+    pw[x] = e * rs[x];  // FP8 row scale enters the value product here
+  }
+  psum = wave_sum_xor_16_32(psum);
+  l = l * alpha + psum;
+  m = mnew;
+  const i32x2 pa2 = {(int)pack_bf16x2(pw[0], pw[1]), (int)pack_bf16x2(pw[2], pw[3])};
+  const bf16x4 pa = __builtin_bit_cast(bf16x4, pa2);
+
+  // ---- rescale accumulators (heads 4g+i) when any running max moved
+  if (__ballot(alpha != 1.f)) {
+    float ai[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+    for (int x = 0; x < 32; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[x][i] *= ai[i];
+  }
+
+  // ---- PV: O[heads 4g+i][dims 64a + 4c + u] += P . V over the 16 rows
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    i32x2 vb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vb[j] = *reinterpret_cast<const i32x2*>(&lat[(4 * g + j) * kLPad + 64 * a + 4 * c]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int half = u >> 1;
+      const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
+      const i32x2 f = {(int)__builtin_amdgcn_perm((uint32_t)vb[1][half], (uint32_t)vb[0][half], sel),
+                       (int)__builtin_amdgcn_perm((uint32_t)vb[3][half], (uint32_t)vb[2][half], sel)};
+      O[a * 4 + u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, f), O[a * 4 + u]);
+    }
+  }
+}
+
+// Normalise the accumulators of heads 4g+i and write the output row (one
+// split) or the split's partial output and LSE.
+__device__ __forceinline__ void mla_finish(const MlaParams& p, const f32x4 (&O)[32], float m, float l, int t,
+                                           int split, int ht, int g, int c) {
+  float li[4], mi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    li[i] = __shfl(l, 4 * g + i);
+    mi[i] = __shfl(m, 4 * g + i);
+  }
+  const bool final_out = p.nsplit == 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 16 * ht + 4 * g + i;
+    if (h >= p.H) continue;
+    const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
+    float* dst = final_out ? p.out + ((int64_t)t * p.H + h) * 512
+                           : p.part_o + (((int64_t)t * p.nsplit + split) * p.H + h) * 512;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      f32x4 v = {O[a * 4 + 0][i] * inv, O[a * 4 + 1][i] * inv, O[a * 4 + 2][i] * inv, O[a * 4 + 3][i] * inv};
+      *reinterpret_cast<f32x4*>(dst + 64 * a + 4 * c) = v;
+    }
+    if (c == 0) {
+      const float lse = li[i] > 0.f ? (mi[i] + __log2f(li[i])) * 0.69314718055994531f : -__builtin_inff();
+      if (final_out) {
+        if (p.lse) p.lse[(int64_t)t * p.H + h] = lse;
+      } else {
+        p.part_lse[((int64_t)t * p.nsplit + split) * p.H + h] = lse;
+      }
+    }
+  }
+}
+
 template <int FMT, int NW>
 __global__ __launch_bounds__(64 * NW) void mla_kernel(MlaParams p) {
   constexpr int SEGS = Geo<FMT>::SEGS;
@@ -235,106 +345,207 @@ __global__ __launch_bounds__(64 * NW) void mla_kernel(MlaParams p) {
       if (scale_lane) sc_next = load_scale(id);
     }
     id_next = load_id(it + 3);
-    // ---- QK: S^T tile, rows 4g + i of head c
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    {
-      const __bf16* lrow = &lat[c * kLPad];
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lrow + dim_of(kk, g));
-        s = mfma16x16x32(a, qf[kk], s);
-      }
-    }
-    // ---- online softmax for head c
-    float lg[4], rs[4];
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * g + i;
-      const float sc = rsc[row];
-      rs[i] = sc;
-      const float v = rv[row] >= 0 ? s[i] * p.sm_log2 * sc : -__builtin_inff();
-      lg[i] = v;
-      tmax = fmaxf(tmax, v);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // lazy rescaling: keep a stale max while the tile stays within 2^8 of it
-    // (weights stay <= 256); both O and l use the same max, so the final
-    // normalisation is exact
-    const float mnew = (m == -__builtin_inff() || tmax > m + kRescaleLog2) ? tmax : m;
-    const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - mnew);
-    float psum = 0.f;
-    float pw[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float e = (lg[x] == -__builtin_inff() || mnew == -__builtin_inff()) ? 0.f : exp2f(lg[x] - mnew);
-      psum += e;
-      pw[x] = e * rs[x];  // FP8 row scale enters the value product here
-    }
-    psum = wave_sum_xor_16_32(psum);
-    l = l * alpha + psum;
-    m = mnew;
-    const i32x2 pa2 = {(int)pack_bf16x2(pw[0], pw[1]), (int)pack_bf16x2(pw[2], pw[3])};
-    const bf16x4 pa = __builtin_bit_cast(bf16x4, pa2);
-
-    // ---- rescale accumulators (heads 4g+i) when any running max moved
-    if (__ballot(alpha != 1.f)) {
-      float ai[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int x = 0; x < 32; ++x)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[x][i] *= ai[i];
-    }
-
-    // ---- PV: O[heads 4g+i][dims 64a + 4c + u] += P . V over the 16 rows
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      i32x2 vb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vb[j] = *reinterpret_cast<const i32x2*>(&lat[(4 * g + j) * kLPad + 64 * a + 4 * c]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int half = u >> 1;
-        const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-        const i32x2 f = {(int)__builtin_amdgcn_perm((uint32_t)vb[1][half], (uint32_t)vb[0][half], sel),
-                         (int)__builtin_amdgcn_perm((uint32_t)vb[3][half], (uint32_t)vb[2][half], sel)};
-        O[a * 4 + u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, f), O[a * 4 + u]);
-      }
-    }
+    mla_tile(p, lat, rsc, rv, qf, O, m, l, g, c);
   }
 
-  // ---- epilogue: normalise heads 4g+i
-  float li[4], mi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    li[i] = __shfl(l, 4 * g + i);
-    mi[i] = __shfl(m, 4 * g + i);
-  }
-  const bool final_out = p.nsplit == 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 16 * ht + 4 * g + i;
-    if (h >= p.H) continue;
-    const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
-    float* dst = final_out ? p.out + ((int64_t)t * p.H + h) * 512
-                           : p.part_o + (((int64_t)t * p.nsplit + split) * p.H + h) * 512;
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      f32x4 v = {O[a * 4 + 0][i] * inv, O[a * 4 + 1][i] * inv, O[a * 4 + 2][i] * inv, O[a * 4 + 3][i] * inv};
-      *reinterpret_cast<f32x4*>(dst + 64 * a + 4 * c) = v;
+  mla_finish(p, O, m, l, t, split, ht, g, c);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 and NVFP4 latents: gather by direct HBM -> LDS copies.
+//
+// global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS (64
+// lanes = 16 rows x 64 bytes per instruction), so two tiles can be in flight
+// behind the one being computed without holding a single register.  The
+// copies are issued from inline assembly and waited for with explicit
+// vmcnt counts: every wave issues the same sequence per tile (one id copy,
+// one side copy -- FP8 row scales or NVFP4 block scales -- and its segment
+// copies), always, even past the end of the list (ids clamped in range, rows
+// on the zero row), so one constant count is exact in every iteration.
+//
+// Per iteration `it`, for every wave:
+//   wait   copies of tile it (rows, side) and ids of tile it+2 have landed
+//   A      dequantise this wave's segments of tile it into the bf16 tile
+//   B      copy ids of tile it+3, then side and rows of tile it+2 (into the
+//          ring slots tile it just vacated)
+//   C      QK / softmax / PV of tile it
+// LDS: bf16 tile [16][kLPad] | raw [2][SEGS][1 KB] | side [2][1 KB] | ids [4][64]
+static __device__ __attribute__((aligned(64))) uint8_t g_zero_row[1280] = {0};
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int FMT> struct DmaGeo;
+template <> struct DmaGeo<DSA_LAT_FP8> { static constexpr int SEGS = 9; };    // 576 B of E4M3
+template <> struct DmaGeo<DSA_LAT_NVFP4> { static constexpr int SEGS = 5; };  // 256 B codes, 64 B rope
+
+template <int FMT, int NW>
+__global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
+  constexpr int SEGS = DmaGeo<FMT>::SEGS;
+  constexpr int SPT = (SEGS + NW - 1) / NW;  // segment copies per wave per tile
+  constexpr int kRawBytes = SEGS * 1024;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  __bf16* lat = reinterpret_cast<__bf16*>(dsm);
+  uint8_t* raw = dsm + kRT * kLPad * 2;      // [2][SEGS][1024]
+  uint8_t* side = raw + 2 * kRawBytes;       // [2][1024]
+  int* ids = reinterpret_cast<int*>(side + 2 * 1024);  // [4][64]
+  __shared__ float rsc[kRT];
+  __shared__ int rv[kRT];
+
+  const int split = blockIdx.x, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ht = blockIdx.z * NW + wave;
+  const int g = lane >> 4, c = lane & 15;
+  const int my_row = lane >> 2, q = lane & 3;
+  const int j_begin = split * p.split_len;
+  const int j_end = min(j_begin + p.split_len, p.k);
+  const int ntile = (j_end - j_begin + kRT - 1) / kRT;
+  const int P = 1 << p.plog2;
+  const int32_t* rlist = p.rows + (int64_t)t * p.k;
+  const uint32_t raw_l = lds_addr(raw), side_l = lds_addr(side), ids_l = lds_addr(ids);
+
+  // id of row r of tile `tile` (-1 past the split's end), from the id ring
+  auto id_at = [&](int tile, int r) -> int {
+    return j_begin + tile * kRT + r < j_end ? ids[(tile & 3) * 64 + r] : -1;
+  };
+  auto page_of = [&](int id) -> const uint8_t* {
+    return p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
+  };
+  // copies of one tile's ids: lane l takes entry l & 15 (clamped in range)
+  auto copy_ids = [&](int tile) {
+    const int j = min(j_begin + tile * kRT + (lane & 15), p.k - 1);
+    dma4(rlist + j, ids_l + (tile & 3) * 256);
+  };
+  // side and row copies of one tile into ring slot `slot`
+  auto copy_tile = [&](int tile, int slot) {
+    if (FMT == DSA_LAT_FP8) {
+      // row scale of row lane >> 2 (lanes 4r .. 4r+3 carry row r's)
+      const int id = id_at(tile, my_row);
+      const uint8_t* src = row_ok(id, p) ? page_of(id) + P * 576 + (id & (P - 1)) * 4 : g_zero_row;
+      dma4(src, side_l + slot * 1024);
+    } else {
+      // 32 bytes of E4M3 block scales per row: lane l < 32 copies half l & 1
+      // of row l >> 1 (lanes 32..63 repeat rows 0..15 into the slot's tail)
+      const int r = (lane >> 1) & 15;
+      const int id = id_at(tile, r);
+      const uint8_t* src = row_ok(id, p) ? page_of(id) + 256 * P + (id & (P - 1)) * 32 + (lane & 1) * 16 : g_zero_row;
+      dma16(src, side_l + slot * 1024);
     }
-    if (c == 0) {
-      const float lse = li[i] > 0.f ? (mi[i] + __log2f(li[i])) * 0.69314718055994531f : -__builtin_inff();
-      if (final_out) {
-        if (p.lse) p.lse[(int64_t)t * p.H + h] = lse;
+    const int id = id_at(tile, my_row);
+    const bool ok = row_ok(id, p);
+    const uint8_t* page = ok ? page_of(id) : g_zero_row;
+    const int slot_i = ok ? (id & (P - 1)) : 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sp = min(wave + i * NW, SEGS - 1);
+      const uint8_t* src;
+      if (FMT == DSA_LAT_FP8) {
+        src = ok ? page + slot_i * 576 + sp * 64 + q * 16 : g_zero_row + sp * 64 + q * 16;
       } else {
-        p.part_lse[((int64_t)t * p.nsplit + split) * p.H + h] = lse;
+        src = !ok ? g_zero_row + q * 16
+                  : (sp < 4 ? page + slot_i * 256 + sp * 64 + q * 16 : page + 288 * P + slot_i * 64 + q * 16);
       }
+      dma16(src, raw_l + slot * kRawBytes + sp * 1024);
+    }
+  };
+  // copies outstanding behind the ids of tile it+2 when tile it is consumed
+  constexpr int kBehind = 1 + SPT;
+
+  bf16x8 qf[18];
+  {
+    const int head = 16 * ht + c;
+    if (head < p.H) {
+      const __bf16* qp = p.q + ((int64_t)t * p.H + head) * 576;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, ld16(qp + dim_of(kk, g)));
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qf[kk] = bf16x8{};
     }
   }
+  f32x4 O[32];
+#pragma unroll
+  for (int x = 0; x < 32; ++x) O[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), l = 0.f;
+
+  // The query loads must be complete (and known to the compiler to be) before
+  // the first copy: the compiler does not see the copies, and a query load
+  // still pending at the loop would make it wait for everything in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // prologue: ids of tiles 0, 1; tile 0; ids of tile 2; tile 1
+  copy_ids(0);
+  copy_ids(1);
+  wait_vmcnt<0>();
+  copy_tile(0, 0);
+  copy_ids(2);
+  copy_tile(1, 1);
+  __bf16* lrow = lat + my_row * kLPad;
+
+  for (int it = 0; it < ntile; ++it) {
+    const int slot = it & 1;
+    wait_vmcnt<kBehind>();
+    __syncthreads();  // the previous tile's readers are done with lat/rsc/rv
+    // A: this wave's segments of tile `it` -> bf16 tile (all LDS reads are
+    // issued before the first store, which the compiler could not reorder)
+    i32x4 rseg[SPT];
+    uint32_t rsc2[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sp = min(wave + i * NW, SEGS - 1);
+      rseg[i] = *reinterpret_cast<const i32x4*>(raw + slot * kRawBytes + sp * 1024 + lane * 16);
+      rsc2[i] = FMT == DSA_LAT_NVFP4
+                    ? *reinterpret_cast<const uint16_t*>(side + slot * 1024 + my_row * 32 + (min(sp, 3) * 4 + q) * 2)
+                    : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sp = wave + i * NW;
+      if (sp >= SEGS) continue;
+      const i32x4 v = rseg[i];
+      if (FMT == DSA_LAT_FP8 || sp == 4) {
+        const i32x2 a = e4m3x4_to_bf16(v[0]), b = e4m3x4_to_bf16(v[1]);
+        const i32x2 c2 = e4m3x4_to_bf16(v[2]), d = e4m3x4_to_bf16(v[3]);
+        i32x4* dst = reinterpret_cast<i32x4*>(lrow + (FMT == DSA_LAT_FP8 ? (sp * 4 + q) * 16 : 512 + q * 16));
+        dst[0] = i32x4{a[0], a[1], b[0], b[1]};
+        dst[1] = i32x4{c2[0], c2[1], d[0], d[1]};
+      } else {  // NVFP4 codes: 32 dims, two E4M3 block scales
+        const uint32_t sc2 = rsc2[i];
+        const float sa = e4m3_to_f32(sc2 & 0xFFu), sb = e4m3_to_f32((sc2 >> 8) & 0xFFu);
+        i32x4* dst = reinterpret_cast<i32x4*>(lrow + (sp * 4 + q) * 32);
+        dst[0] = __builtin_bit_cast(i32x4, e2m1x8_times(v[0], sa));
+        dst[1] = __builtin_bit_cast(i32x4, e2m1x8_times(v[1], sa));
+        dst[2] = __builtin_bit_cast(i32x4, e2m1x8_times(v[2], sb));
+        dst[3] = __builtin_bit_cast(i32x4, e2m1x8_times(v[3], sb));
+      }
+    }
+    if (wave == 0 && tid < kRT) {
+      const int id = id_at(it, tid);
+      const bool ok = row_ok(id, p);
+      rv[tid] = ok ? id : -1;
+      rsc[tid] = FMT == DSA_LAT_FP8 ? *reinterpret_cast<const float*>(side + slot * 1024 + tid * 16)
+                                    : (ok ? 1.f : 0.f);
+    }
+    __syncthreads();
+    // B: ids of tile it+3, then tile it+2 into the slot tile it vacated
+    copy_ids(it + 3);
+    copy_tile(it + 2, slot);
+    // C
+    mla_tile(p, lat, rsc, rv, qf, O, m, l, g, c);
+  }
+  wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
+  mla_finish(p, O, m, l, t, split, ht, g, c);
 }
 
 // Merge of the split partials of one (row, head): all split LSEs are read in
@@ -387,12 +598,23 @@ dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
     case 3: hipLaunchKernelGGL((mla_kernel<F, 3>), grid, block, 0, stream, p); break;      \
     default: hipLaunchKernelGGL((mla_kernel<F, 4>), grid, block, 0, stream, p); break;     \
   }
+#define DSA_MLA_DMA_LAUNCH(F)                                                                       \
+  {                                                                                                \
+    const size_t lds = (size_t)kRT * kLPad * 2 + 2 * DmaGeo<F>::SEGS * 1024 + 2 * 1024 + 4 * 256;  \
+    switch (nw) {                                                                                  \
+      case 1: hipLaunchKernelGGL((mla_dma_kernel<F, 1>), grid, block, lds, stream, p); break;      \
+      case 2: hipLaunchKernelGGL((mla_dma_kernel<F, 2>), grid, block, lds, stream, p); break;      \
+      case 3: hipLaunchKernelGGL((mla_dma_kernel<F, 3>), grid, block, lds, stream, p); break;      \
+      default: hipLaunchKernelGGL((mla_dma_kernel<F, 4>), grid, block, lds, stream, p); break;     \
+    }                                                                                              \
+  }
   switch (p.fmt) {
     case DSA_LAT_BF16: DSA_MLA_LAUNCH(DSA_LAT_BF16) break;
-    case DSA_LAT_FP8: DSA_MLA_LAUNCH(DSA_LAT_FP8) break;
-    default: DSA_MLA_LAUNCH(DSA_LAT_NVFP4) break;
+    case DSA_LAT_FP8: DSA_MLA_DMA_LAUNCH(DSA_LAT_FP8) break;
+    default: DSA_MLA_DMA_LAUNCH(DSA_LAT_NVFP4) break;
   }
 #undef DSA_MLA_LAUNCH
+#undef DSA_MLA_DMA_LAUNCH
   if (p.nsplit > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(p.H, p.T), dim3(128), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
