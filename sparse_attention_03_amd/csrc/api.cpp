@@ -63,20 +63,17 @@ dsa_status check_batch(const dsa_batch& b, int plog2, bool need_meta) {
 // ---- top-k plan
 struct TopkPlan {
   int cand_cap, slice, nslices;
-  size_t off_hist, off_ctr, off_def, off_cand, total;
+  size_t off_ctr, off_cand, total;
 };
 TopkPlan plan_topk(int T, int max_vis, int k) {
+  (void)k;
   TopkPlan pl;
-  pl.cand_cap = std::min(max_vis, 8192);
+  pl.cand_cap = std::min(max_vis, dsa::kTopkFinalCap);
   pl.slice = 8192;
   pl.nslices = (max_vis + pl.slice - 1) / pl.slice;
   size_t off = 0;
-  pl.off_hist = off;
-  off = align_up(off + (size_t)T * 4096 * 4, 256);
   pl.off_ctr = off;
   off = align_up(off + (size_t)T * 16, 256);
-  pl.off_def = off;
-  off = align_up(off + (size_t)T * k * 4, 256);
   pl.off_cand = off;
   off = align_up(off + (size_t)T * pl.cand_cap * 8, 256);
   pl.total = off;
@@ -291,9 +288,7 @@ dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   p.rows = a->rows;
   p.count = a->count;
   char* ws = static_cast<char*>(a->workspace);
-  p.hist = reinterpret_cast<uint32_t*>(ws + pl.off_hist);
   p.ctr = reinterpret_cast<uint32_t*>(ws + pl.off_ctr);
-  p.defbuf = reinterpret_cast<int32_t*>(ws + pl.off_def);
   p.cand = reinterpret_cast<uint32_t*>(ws + pl.off_cand);
   p.cand_cap = pl.cand_cap;
   p.slice = pl.slice;

@@ -37,6 +37,10 @@ struct IndexerParams {
   int max_rows_per_req;
 };
 
+// Candidates per row the top-k finalize holds in LDS (the candidate buffer
+// holds at most this many per row).
+constexpr int kTopkFinalCap = 8192;
+
 struct TopkParams {
   int T;
   const float* scores;
@@ -52,12 +56,10 @@ struct TopkParams {
   int32_t* rows;
   int32_t* count;
   // workspace
-  uint32_t* hist;       // [T][4096]
-  uint32_t* ctr;        // [T][4]: n_def, n_cand, threshold bin, need
-  int32_t* defbuf;      // [T][k]
+  uint32_t* ctr;        // [T][4]: candidates appended, -, threshold key, -
   uint32_t* cand;       // [T][cand_cap][2]: order key, index
   int cand_cap;
-  int slice;            // scores per workgroup in the histogram / filter passes
+  int slice;            // scores per workgroup in the filter pass
   int nslices;
 };
 

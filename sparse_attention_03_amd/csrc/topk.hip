@@ -6,122 +6,200 @@
 // row t is unique: the K = min(k, vis) largest scores, equal scores ordered by
 // ascending index.  It is emitted in ascending index order.
 //
-// Two passes over the scores of a row, each spread over many workgroups:
-//   1. histogram of the top 12 bits of the order-preserving uint32 key;
-//   2. every slice finds the threshold bin b holding rank K from the row's
-//      histogram and gathers keys above b ("definite", fewer than K in total)
-//      and keys inside b ("candidates") in LDS and appends them to per-row
-//      buffers behind one global atomic per list;
-//   3. one workgroup per row refines the candidates (in LDS) with an exact
-//      radix select on the 56-bit composite (low 20 key bits, then inverted
-//      index), so ties resolve to the lower index, then orders the K winners
-//      by index through an LDS bitmap (popcount prefix sums) and writes
-//      indices, physical rows and the count.
-// If a row's candidates overflow their buffer, step 3 reads them straight
-// from the score row instead (slower, same result).
+// One pass over the scores, bracketed by two small per-row kernels:
+//   1. threshold: one workgroup per row reads a sample of the row -- every
+//      score when the row is short, else the first 16 scores (one 64-byte
+//      line) of every block of B -- and finds, by two 12-bit histogram
+//      levels over the sample's key range, a key tau with about
+//      K * S / vis + 4 sqrt(.) + 8 sample keys at or above it (exactly the
+//      K-th largest key when the whole row is the sample).  So with
+//      overwhelming probability at least K and not many more than K scores
+//      of the row are >= tau.
+//   2. filter: the row is cut into slices; every slice gathers its keys >=
+//      tau in LDS and appends them to the row's candidate buffer behind one
+//      global atomic.
+//   3. finalize: one workgroup per row runs an exact radix select (12-bit
+//      digits) over the candidates' 64-bit composites (key, inverted index)
+//      -- ties go to the lower index -- then ranks the K winners by index
+//      through an LDS bitmap and writes indices and physical rows.
+// The estimate only decides speed: when fewer than K or more than the
+// buffer's capacity of candidates arrived, finalize selects from the whole
+// score row instead (same result).
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 
-constexpr int kBins = 4096;
-constexpr int kBinShift = 20;
-
-__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
+constexpr int kExactMax = 8192;     // rows up to this length are sampled completely
+constexpr int kMaxSamples = 16384;  // 16 per thread of the threshold workgroup
+constexpr int kRun = 16;            // consecutive scores per sampled block
+constexpr int kFilterCap = 4096;    // candidates a filter workgroup gathers in LDS
 
 __device__ __forceinline__ int row_vis(const TopkParams& p, int t) {
   return min(max(p.tok_vis[t], 0), p.max_vis);
 }
 
-__global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
-  __shared__ uint32_t h[kBins];
-  const int t = blockIdx.y;
-  const int vis = row_vis(p, t);
-  if (vis <= p.k) return;
-  const int s_begin = blockIdx.x * p.slice;
-  if (s_begin >= vis) return;
-  const int s_end = min(s_begin + p.slice, vis);
-  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
-  __syncthreads();
-  const float* row = p.scores + (int64_t)t * p.ld;
-  // the whole slice (8 float4 per thread) is loaded before any is binned
-  f32x4 v[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int s = s_begin + 4 * threadIdx.x + 1024 * b;
-    v[b] = (s + 3 < s_end) ? *reinterpret_cast<const f32x4*>(row + s) : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (s + 3 >= s_end)
-      for (int e = 0; e < 4; ++e) v[b][e] = (s + e < s_end) ? row[s + e] : 0.f;
-  }
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int s = s_begin + 4 * threadIdx.x + 1024 * b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (s + e < s_end) atomicAdd(&h[order_key(v[b][e]) >> kBinShift], 1u);
-  }
-  __syncthreads();
-  uint32_t* gh = p.hist + (int64_t)t * kBins;
-  for (int i = threadIdx.x; i < kBins; i += 256)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+// Sampling block of a row: B = kRun (every score) for short rows, else the
+// smallest power of two >= 256 with vis / B * kRun <= kMaxSamples.
+__device__ __forceinline__ int sample_block(int vis) {
+  if (vis <= kExactMax) return kRun;
+  int b = 256;
+  while ((int64_t)b * kMaxSamples < (int64_t)vis * kRun) b <<= 1;
+  return b;
 }
 
-// Threshold bin of a row from its global histogram: the bin b with
-// count(bins > b) < k <= count(bins >= b); returns b and need = k - count(> b).
-// Called by all 256 threads of a workgroup; 16 bins per thread, suffix sums
-// with wave shuffles and one LDS exchange.
-__device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, uint32_t k, int* out_bin,
-                                              uint32_t* out_need) {
-  __shared__ uint32_t wtot[4];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_need;
+// Block-wide inclusive suffix scan over nb = 4 * blockDim bins held 4 per
+// thread (bins 4*tid .. 4*tid+3), then the bin holding rank r from the top:
+// count(bins > b) < r <= count(bins >= b).  Every thread gets b and
+// need = r - count(bins > b).  wtot: 16 words of LDS.
+__device__ __forceinline__ void rank_bin_1024(const uint32_t* h, uint32_t r, uint32_t* wtot, int* s_bin,
+                                              uint32_t* s_need, int& bin, uint32_t& need,
+                                              uint32_t* s_count = nullptr, uint32_t* count = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t loc[16];
-  uint32_t sum = 0;
+  uint32_t loc[4], sum = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    loc[i] = gh[tid * 16 + i];
+  for (int i = 0; i < 4; ++i) {
+    loc[i] = h[4 * tid + i];
     sum += loc[i];
   }
-  uint32_t suf = sum;  // inclusive suffix sum within the wave
+  uint32_t suf = sum;
   for (int off = 1; off < 64; off <<= 1) {
     const uint32_t o = __shfl_down(suf, off);
     if (lane + off < 64) suf += o;
   }
   if (lane == 0) wtot[wave] = suf;
   __syncthreads();
-  for (int w = wave + 1; w < 4; ++w) suf += wtot[w];
-  const uint32_t above = suf - sum;  // bins owned by higher threads
-  if (above < k && suf >= k) {
+  for (int w = wave + 1; w < 16; ++w) suf += wtot[w];
+  const uint32_t above = suf - sum;
+  if (above < r && suf >= r) {
     uint32_t acc = above;
-    for (int i = 15; i >= 0; --i) {
-      if (acc + loc[i] >= k) {
-        s_bin = tid * 16 + i;
-        s_need = k - acc;
+    for (int i = 3; i >= 0; --i) {
+      if (acc + loc[i] >= r) {
+        *s_bin = 4 * tid + i;
+        *s_need = r - acc;
+        if (s_count) *s_count = loc[i];
         break;
       }
       acc += loc[i];
     }
   }
   __syncthreads();
-  *out_bin = s_bin;
-  *out_need = s_need;
+  bin = *s_bin;
+  need = *s_need;
+  if (s_count) *count = *s_count;
 }
 
-constexpr int kFilterCap = 2048;  // candidates a filter workgroup keeps in LDS
+__global__ __launch_bounds__(1024) void topk_threshold_kernel(TopkParams p) {
+  __shared__ uint32_t h[4096];
+  __shared__ uint32_t wtot[16];
+  __shared__ uint32_t s_lo[16], s_hi[16];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_need;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vis = row_vis(p, t);
+  uint32_t* ctr = p.ctr + (int64_t)t * 4;
+  if (vis <= p.k) {
+    if (tid < 4) ctr[tid] = 0;
+    return;
+  }
+  const int B = sample_block(vis);
+  const float* row = p.scores + (int64_t)t * p.ld;
+  // sample keys (16 per thread, all loads issued first); 0 marks "no sample"
+  // (below every finite or -inf score's key)
+  uint32_t key[16];
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = tid + 1024 * i;
+    const int64_t s = (int64_t)(e >> 4) * B + (e & 15);
+    v[i] = s < vis ? row[s] : 0.f;
+  }
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = tid + 1024 * i;
+    const int64_t s = (int64_t)(e >> 4) * B + (e & 15);
+    key[i] = s < vis ? order_key(v[i]) : 0u;
+    if (s < vis) {
+      lo = min(lo, key[i]);
+      hi = max(hi, key[i]);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+  }
+  if (lane == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+  }
+  for (int i = tid; i < 4096; i += 1024) h[i] = 0;
+  __syncthreads();
+  lo = s_lo[0];
+  hi = s_hi[0];
+  for (int w = 1; w < 16; ++w) {
+    lo = min(lo, s_lo[w]);
+    hi = max(hi, s_hi[w]);
+  }
+  // number of samples (blocks < kMaxSamples / kRun; the last may be partial)
+  // and the rank of the threshold among them
+  const int64_t nblk = ((int64_t)vis + B - 1) / B;
+  const int64_t cb = min<int64_t>(nblk, kMaxSamples / kRun);
+  const int64_t full = vis / B;  // blocks with all kRun samples present
+  const int64_t S = min(full, cb) * kRun + (cb > full ? min<int64_t>(kRun, vis - full * B) : 0);
+  uint32_t r;
+  if (B == kRun) {
+    r = (uint32_t)p.k;  // exact: the K-th largest key
+  } else {
+    const float mu = (float)p.k * (float)S / (float)vis;
+    r = (uint32_t)min<int64_t>(S, (int64_t)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
+  }
+  if (tid == 0) {  // a rank beyond the samples cannot happen; keep the result defined anyway
+    s_bin = 0;
+    s_need = 1;
+  }
+  // level 1: 12-bit bins over the sample's key range
+  const uint32_t diff = lo ^ hi;
+  const int nbits = diff ? 32 - __clz((int)diff) : 0;
+  const int sh1 = max(nbits - 12, 0);
+  const uint32_t base1 = lo >> sh1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (key[i] >= lo && key[i] != 0u) atomicAdd(&h[(key[i] >> sh1) - base1], 1u);
+  __syncthreads();
+  int b1;
+  uint32_t need1;
+  rank_bin_1024(h, r, wtot, &s_bin, &s_need, b1, need1);
+  uint32_t tau = (base1 + (uint32_t)b1) << sh1;
+  if (sh1 > 0) {
+    // level 2: the next (up to) 12 bits inside bin b1
+    const int sh2 = max(sh1 - 12, 0);
+    const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
+    for (int i = tid; i < 4096; i += 1024) h[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key[i] != 0u && (key[i] >> sh1) - base1 == (uint32_t)b1) atomicAdd(&h[(key[i] >> sh2) & mask2], 1u);
+    __syncthreads();
+    int b2;
+    uint32_t need2;
+    rank_bin_1024(h, need1, wtot, &s_bin, &s_need, b2, need2);
+    tau |= (uint32_t)b2 << sh2;
+  }
+  if (tid == 0) {
+    ctr[0] = 0;    // candidates appended by the filter
+    ctr[1] = 0;
+    ctr[2] = tau;  // keys >= tau are candidates
+    ctr[3] = 0;
+  }
+}
 
-// Keys above the threshold bin ("definite") and inside it ("candidates") are
-// gathered in LDS, then copied out behind one global atomic per list.
+// Keys >= tau are gathered in LDS, then copied out behind one global atomic.
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
-  __shared__ int l_def[DSA_MAX_TOPK];
   __shared__ uint32_t l_ck[kFilterCap];
   __shared__ int l_ci[kFilterCap];
-  __shared__ int n_def, n_cand, n_cand2;
-  __shared__ uint32_t base_def, base_cand;
+  __shared__ int n_cand, n_cand2;
+  __shared__ uint32_t base_cand;
   const int t = blockIdx.y;
   const int tid = threadIdx.x;
   const int vis = row_vis(p, t);
@@ -130,20 +208,8 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
   if (s_begin >= vis) return;
   const int s_end = min(s_begin + p.slice, vis);
   uint32_t* ctr = p.ctr + (int64_t)t * 4;
-  if (tid == 0) {
-    n_def = 0;
-    n_cand = 0;
-    n_cand2 = 0;
-  }
-  int ibin;
-  uint32_t need;
-  threshold_bin(p.hist + (int64_t)t * kBins, (uint32_t)p.k, &ibin, &need);
-  const uint32_t bin = (uint32_t)ibin;
-  if (blockIdx.x == 0 && tid == 0) {
-    ctr[2] = bin;
-    ctr[3] = need;
-  }
   const float* row = p.scores + (int64_t)t * p.ld;
+  // the whole slice (8 float4 per thread) is loaded before any is compared
   f32x4 v[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
@@ -152,7 +218,12 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
     if (s + 3 >= s_end)
       for (int e = 0; e < 4; ++e) v[b][e] = (s + e < s_end) ? row[s + e] : 0.f;
   }
-  __syncthreads();  // counters initialised
+  const uint32_t tau = ctr[2];
+  if (tid == 0) {
+    n_cand = 0;
+    n_cand2 = 0;
+  }
+  __syncthreads();
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int s = s_begin + 4 * tid + 1024 * b;
@@ -160,11 +231,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
     for (int e = 0; e < 4; ++e) {
       if (s + e >= s_end) break;
       const uint32_t key = order_key(v[b][e]);
-      const uint32_t d = key >> kBinShift;
-      if (d > bin) {
-        const int pos = atomicAdd(&n_def, 1);
-        if (pos < DSA_MAX_TOPK) l_def[pos] = s + e;
-      } else if (d == bin) {
+      if (key >= tau) {
         const int pos = atomicAdd(&n_cand, 1);
         if (pos < kFilterCap) {
           l_ck[pos] = key;
@@ -174,14 +241,8 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    base_def = atomicAdd(&ctr[0], (uint32_t)n_def);
-    base_cand = atomicAdd(&ctr[1], (uint32_t)n_cand);
-  }
+  if (tid == 0) base_cand = atomicAdd(&ctr[0], (uint32_t)n_cand);
   __syncthreads();
-  int32_t* defrow = p.defbuf + (int64_t)t * p.k;
-  for (int i = tid; i < n_def; i += 256)
-    if (base_def + i < (uint32_t)p.k) defrow[base_def + i] = l_def[i];
   uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
   const int nc = n_cand;
   if (nc <= kFilterCap) {
@@ -193,10 +254,10 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
       }
     }
   } else {
-    // more candidates than LDS holds: write them all straight from a rescan
+    // more candidates than LDS holds: write them straight from a rescan
     for (int s = s_begin + tid; s < s_end; s += 256) {
       const uint32_t key = order_key(row[s]);
-      if ((key >> kBinShift) == bin) {
+      if (key >= tau) {
         const uint32_t pos = base_cand + (uint32_t)atomicAdd(&n_cand2, 1);
         if (pos < (uint32_t)p.cand_cap) {
           candrow[2 * pos] = key;
@@ -208,7 +269,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
 }
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
-  return ((uint64_t)(key & 0xFFFFFu) << 36) | ((uint64_t)(0xFFFFFFFFu - idx) << 4);
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - idx);
 }
 
 __device__ __forceinline__ int translate_one(int li, int r, const int32_t* __restrict__ bt, int bt_stride,
@@ -226,18 +287,158 @@ __device__ __forceinline__ int translate_one(int li, int r, const int32_t* __res
   return (pg << plog2) | (li & ((1 << plog2) - 1));
 }
 
-constexpr int kFinalCap = 4096;  // candidates the finalize workgroup refines in LDS
-constexpr int kWinIdx = 1024 * 8 * 32;  // indices per bitmap window (8 words per thread)
+// Shared scratch of the 1024-thread selection and sort.
+struct SelectLds {
+  uint32_t h[4096];
+  uint32_t wtot[16];
+  uint64_t red[2][16];
+  int bin, cnt;
+  uint32_t need, hcount;
+};
+
+// Exact selection of the K largest among distinct 64-bit composites that the
+// workgroup's 1024 threads enumerate (each(f) calls f(v) for every composite
+// of the calling thread): radix select with 12-bit digits, starting at the
+// highest bit in which the composites differ.  On return, v is a winner iff
+// (v >> hi_sh) >= prefix; exactly K composites are.
+template <class Each>
+__device__ __forceinline__ void select_top(Each each, uint32_t K, SelectLds& sl, int& hi_sh_out,
+                                           uint64_t& prefix_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t mx = 0, mn = ~0ull;
+  each([&](uint64_t v) {
+    mx = v > mx ? v : mx;
+    mn = v < mn ? v : mn;
+  });
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t a = __shfl_xor(mx, o), b = __shfl_xor(mn, o);
+    mx = a > mx ? a : mx;
+    mn = b < mn ? b : mn;
+  }
+  if (lane == 0) {
+    sl.red[0][wave] = mx;
+    sl.red[1][wave] = mn;
+  }
+  __syncthreads();
+  mx = sl.red[0][0];
+  mn = sl.red[1][0];
+  for (int w = 1; w < 16; ++w) {
+    mx = sl.red[0][w] > mx ? sl.red[0][w] : mx;
+    mn = sl.red[1][w] < mn ? sl.red[1][w] : mn;
+  }
+  const uint64_t dif = mx ^ mn;
+  int hi_sh = dif ? 64 - __clzll((long long)dif) : 1;  // bits >= hi_sh: common prefix
+  uint64_t prefix = hi_sh >= 64 ? 0ull : (mx >> hi_sh);
+  uint32_t need = K;
+  for (;;) {
+    const int lo_sh = max(hi_sh - 12, 0);
+    const uint64_t dmask = (1ull << (hi_sh - lo_sh)) - 1ull;
+    for (int i = tid; i < 4096; i += 1024) sl.h[i] = 0;
+    if (tid == 0) {
+      sl.bin = 0;
+      sl.need = 1;
+      sl.hcount = 1;
+    }
+    __syncthreads();
+    each([&](uint64_t v) {
+      const uint64_t pre = hi_sh >= 64 ? 0ull : (v >> hi_sh);
+      if (pre == prefix) atomicAdd(&sl.h[(v >> lo_sh) & dmask], 1u);
+    });
+    __syncthreads();
+    int b;
+    uint32_t nn, hv;
+    rank_bin_1024(sl.h, need, sl.wtot, &sl.bin, &sl.need, b, nn, &sl.hcount, &hv);
+    prefix = (prefix << (hi_sh - lo_sh)) | (uint64_t)b;
+    hi_sh = lo_sh;
+    need = nn;
+    if (hv == nn || lo_sh == 0) break;
+  }
+  hi_sh_out = hi_sh;
+  prefix_out = prefix;
+}
+
+// Order the K winners in out[0..K) by index and write idx / physical rows of
+// row t.  An LDS bitmap (bm, bm_words words) covers a window of the index
+// range, W words per thread; a block prefix sum of the threads' popcounts
+// gives every winner its rank directly (rank = set bits before it), so no
+// thread walks its bits one by one.  Windows repeat until vis is covered.
+// ord: LDS int[2048] (the ordered list), tpre: LDS int[1024], wsum: 16 words.
+__device__ __forceinline__ void order_and_store(const TopkParams& p, const int* out, int K, int vis, uint32_t* bm,
+                                                int bm_words, int* ord, int* tpre, uint32_t* wsum, int t, int r,
+                                                int32_t* idx, int32_t* rows) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int need_words = (vis + 31) >> 5;
+  const int W = max(1, min(bm_words >> 10, (need_words + 1023) >> 10));
+  const int win = W * 1024 * 32;
+  int emitted = 0;
+  for (int w0 = 0; w0 < vis; w0 += win) {
+    for (int i = 0; i < W; ++i) bm[tid * W + i] = 0;
+    __syncthreads();
+    for (int j = tid; j < K; j += 1024) {
+      const int li = out[j] - w0;
+      if (li >= 0 && li < win) atomicOr(&bm[li >> 5], 1u << (li & 31));
+    }
+    __syncthreads();
+    int cnt = 0;
+    for (int i = 0; i < W; ++i) cnt += __popc(bm[tid * W + i]);
+    int inc = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    if (lane == 63) wsum[wave] = (uint32_t)inc;
+    __syncthreads();
+    int before = inc - cnt, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) before += (int)wsum[w];
+      tot += (int)wsum[w];
+    }
+    tpre[tid] = before;
+    __syncthreads();
+    for (int j = tid; j < K; j += 1024) {
+      const int li = out[j] - w0;
+      if (li >= 0 && li < win) {
+        const int w = li >> 5, own = w / W;
+        int rk = tpre[own] + __popc(bm[w] & ((1u << (li & 31)) - 1u));
+        for (int x = own * W; x < w; ++x) rk += __popc(bm[x]);
+        ord[emitted + rk] = out[j];
+      }
+    }
+    emitted += tot;
+    __syncthreads();
+  }
+  // coalesced stores; the block-table reads of all entries are in flight at once
+  for (int j = tid; j < p.k; j += 1024) {
+    const int li = j < K ? ord[j] : -1;
+    idx[j] = li;
+    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+  }
+  if (p.count && tid == 0) p.count[t] = K;
+}
+
+// A row with vis <= k keeps every position.
+__device__ __forceinline__ void store_all(const TopkParams& p, int vis, int t, int r, int32_t* idx, int32_t* rows) {
+  for (int j = threadIdx.x; j < p.k; j += blockDim.x) {
+    const int li = j < vis ? j : -1;
+    idx[j] = li;
+    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+  }
+  if (p.count && threadIdx.x == 0) p.count[t] = vis;
+}
+
+// Dynamic LDS of the finalize: candidate keys [kTopkFinalCap] and indices
+// [kTopkFinalCap] (later the ordering bitmap), the winners [2048], the
+// ordered winners [2048], per-thread prefix sums [1024].
+constexpr size_t kFinalLds = (size_t)2 * kTopkFinalCap * 4 + 2 * DSA_MAX_TOPK * 4 + 1024 * 4;
 
 __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
-  __shared__ int out[DSA_MAX_TOPK];
-  __shared__ uint32_t cand_lds[2 * kFinalCap];  // candidate keys, candidate indices; later the bitmap
-  uint32_t* ck = cand_lds;
-  uint32_t* ci = cand_lds + kFinalCap;
-  __shared__ uint32_t h[256];  // radix bins; later the 16 wave totals
-  __shared__ uint32_t wsum[4];
-  __shared__ uint64_t s_prefix;
-  __shared__ int s_need, s_done, s_cnt;
+  extern __shared__ uint32_t fsm[];
+  uint32_t* ck = fsm;
+  uint32_t* ci = fsm + kTopkFinalCap;
+  int* out = reinterpret_cast<int*>(fsm + 2 * kTopkFinalCap);
+  int* ord = out + DSA_MAX_TOPK;
+  int* tpre = ord + DSA_MAX_TOPK;
+  __shared__ SelectLds sl;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int vis = row_vis(p, t);
@@ -245,159 +446,228 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   const int r = p.tok_req ? p.tok_req[t] : 0;
   int32_t* idx = p.idx + (int64_t)t * p.k;
   int32_t* rows = p.rows ? p.rows + (int64_t)t * p.k : nullptr;
-
   if (vis <= p.k) {
-    for (int j = tid; j < p.k; j += blockDim.x) {
-      const int li = j < vis ? j : -1;
-      idx[j] = li;
-      if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
-    }
-    if (p.count && tid == 0) p.count[t] = K;
+    store_all(p, vis, t, r, idx, rows);
     return;
   }
 
   const uint32_t* ctr = p.ctr + (int64_t)t * 4;
-  const int ndef = (int)ctr[0];
-  const int ncand = (int)ctr[1];
-  const uint32_t bin = ctr[2];
+  const int ncand = (int)ctr[0];
   const uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
   const float* srow = p.scores + (int64_t)t * p.ld;
-  // candidate source: LDS copy, the global candidate buffer, or the score row
-  const int mode = (ncand <= kFinalCap) ? 0 : (ncand <= p.cand_cap ? 1 : 2);
-  const int nsrc = mode == 2 ? vis : ncand;
-  if (mode == 0)
+  // candidates in LDS, or (estimate missed) the whole score row
+  const bool from_row = ncand < K || ncand > p.cand_cap;
+  const int nsrc = from_row ? vis : ncand;
+  if (!from_row)
     for (int i = tid; i < ncand; i += blockDim.x) {
       ck[i] = candrow[2 * i];
       ci[i] = candrow[2 * i + 1];
     }
-  auto fetch = [&](int i, uint32_t& key, uint32_t& li) -> bool {
-    if (mode == 0) {
-      key = ck[i];
-      li = ci[i];
-      return true;
-    }
-    if (mode == 1) {
-      key = candrow[2 * i];
-      li = candrow[2 * i + 1];
-      return true;
-    }
-    key = order_key(srow[i]);
-    li = (uint32_t)i;
-    return (key >> kBinShift) == bin;
+  __syncthreads();
+  auto each = [&](auto f) {
+    for (int i = tid; i < nsrc; i += 1024)
+      f(from_row ? composite(order_key(srow[i]), (uint32_t)i) : composite(ck[i], ci[i]));
   };
+  int hi_sh;
+  uint64_t prefix;
+  select_top(each, (uint32_t)K, sl, hi_sh, prefix);
+  if (tid == 0) sl.cnt = 0;
+  __syncthreads();
+  each([&](uint64_t v) {
+    if ((v >> hi_sh) >= prefix) {
+      const int pos = atomicAdd(&sl.cnt, 1);
+      if (pos < DSA_MAX_TOPK) out[pos] = (int)(0xFFFFFFFFu - (uint32_t)v);
+    }
+  });
+  __syncthreads();
+  order_and_store(p, out, K, vis, fsm, 2 * kTopkFinalCap, ord, tpre, sl.wtot, t, r, idx, rows);
+}
 
+// Short rows: one workgroup per row does everything with the row held in
+// registers (up to 64 scores per thread, one read of the row, no workspace,
+// one launch): a threshold from every 16th group of four scores (or from all
+// of a row up to kExactMax), candidates compacted into LDS by a block prefix
+// sum, the exact select over them (over the row re-read from memory when the
+// estimate missed), the sort and the stores.  Used when no row is longer
+// than kFusedMax: a CU streams far less than its share of HBM bandwidth
+// alone, so long rows are spread over many workgroups (threshold / filter /
+// finalize) instead.
+constexpr int kFusedMax = 8192;
+constexpr int kFusedCap = 4096;
+
+__global__ __launch_bounds__(1024) void topk_fused_kernel(TopkParams p) {
+  __shared__ uint32_t cand[2 * kFusedCap];  // keys | indices; later the ordering bitmap
+  uint32_t* ck = cand;
+  uint32_t* ci = cand + kFusedCap;
+  __shared__ int out[DSA_MAX_TOPK];
+  __shared__ int ord[DSA_MAX_TOPK];
+  __shared__ int tpre[1024];
+  __shared__ SelectLds sl;
+  __shared__ uint32_t s_lo[16], s_hi[16];
+  __shared__ int s_wsum[16];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vis = row_vis(p, t);
+  const int K = min(p.k, vis);
+  const int r = p.tok_req ? p.tok_req[t] : 0;
+  int32_t* idx = p.idx + (int64_t)t * p.k;
+  int32_t* rows = p.rows ? p.rows + (int64_t)t * p.k : nullptr;
+  if (vis <= p.k) {
+    store_all(p, vis, t, r, idx, rows);
+    return;
+  }
+  // scores 4*tid + 4096*i + c (i < 16, c < 4); key 0 = past the row's end.
+  // Every float4 read is issued, unconditionally: a start past the row's ld
+  // columns (ld is a multiple of 4) is clamped to the last float4 and its
+  // values are masked, so no read waits behind a branch.
+  const float* row = p.scores + (int64_t)t * p.ld;
+  const int last4 = (int)min<int64_t>(p.ld - 4, 4 * 1024 * 16 - 4);
+  f32x4 x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = *reinterpret_cast<const f32x4*>(row + min(4 * tid + 4096 * i, last4));
+  uint32_t key[16][4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[i][c] = 4 * tid + 4096 * i + c < vis ? order_key(x[i][c]) : 0u;
+
+  // ---- threshold from the sample: all scores of a short row (groups 0 and
+  // 1 hold them), else group i = tid & 15 of every thread (vis / 16 scores
+  // spread over the row), picked by selects rather than a dynamic index
+  const bool exact = vis <= kExactMax;
+  static_assert(kExactMax == 2 * 4096, "a short row lives in groups 0 and 1");
+  uint32_t samp[8];
+  {
+    const int sel = tid & 15;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t x = key[0][c];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) x = sel == i ? key[i][c] : x;
+      samp[c] = exact ? key[0][c] : x;
+      samp[4 + c] = exact ? key[1][c] : 0u;
+    }
+  }
+  auto each_sample = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (samp[j] != 0u) f(samp[j]);
+  };
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  int ns = 0;
+  each_sample([&](uint32_t k2) {
+    lo = min(lo, k2);
+    hi = max(hi, k2);
+    ++ns;
+  });
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    ns += __shfl_xor(ns, o);
+  }
+  if (lane == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+    s_wsum[wave] = ns;
+  }
+  for (int i = tid; i < 4096; i += 1024) sl.h[i] = 0;
   if (tid == 0) {
-    s_prefix = 0;
-    s_need = (int)ctr[3];
-    s_done = 0;
+    sl.bin = 0;
+    sl.need = 1;
   }
-  int shift = 48;
-  for (;; shift -= 8) {
-    if (tid < 256) h[tid] = 0;
-    __syncthreads();
-    const uint64_t prefix = s_prefix;
-    const uint32_t need = (uint32_t)s_need;  // read by all before the update below
-    for (int i = tid; i < nsrc; i += blockDim.x) {
-      uint32_t key, li;
-      if (!fetch(i, key, li)) continue;
-      const uint64_t v = composite(key, li);
-      if ((v >> (shift + 8)) == prefix) atomicAdd(&h[(v >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    // suffix sums of the 256 bins: waves 0..3, one bin per lane
-    uint32_t hv = 0, suf = 0;
-    if (tid < 256) {
-      hv = h[tid];
-      suf = hv;
-      const int lane = tid & 63;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(suf, off);
-        if (lane + off < 64) suf += o;
-      }
-      if (lane == 0) wsum[tid >> 6] = suf;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = (tid >> 6) + 1; w < 4; ++w) suf += wsum[w];
-      const uint32_t above = suf - hv;       // count in higher bins
-      if (above < need && suf >= need) {     // exactly one bin qualifies
-        const uint32_t nn = need - above;
-        s_need = (int)nn;
-        s_prefix = (prefix << 8) | (uint64_t)tid;
-        s_done = (hv == nn) || shift == 0;
-      }
-    }
-    __syncthreads();
-    if (s_done) break;
+  __syncthreads();
+  lo = s_lo[0];
+  hi = s_hi[0];
+  int S = s_wsum[0];
+  for (int w = 1; w < 16; ++w) {
+    lo = min(lo, s_lo[w]);
+    hi = max(hi, s_hi[w]);
+    S += s_wsum[w];
   }
-  const uint64_t thr = s_prefix;
+  uint32_t rk;
+  if (exact) {
+    rk = (uint32_t)K;
+  } else {
+    const float mu = (float)K * (float)S / (float)vis;
+    rk = (uint32_t)min<int64_t>(S, (int64_t)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
+  }
+  const uint32_t diff = lo ^ hi;
+  const int nbits = diff ? 32 - __clz((int)diff) : 0;
+  const int sh1 = max(nbits - 12, 0);
+  const uint32_t base1 = lo >> sh1;
+  each_sample([&](uint32_t k2) { atomicAdd(&sl.h[(k2 >> sh1) - base1], 1u); });
+  __syncthreads();
+  int b1;
+  uint32_t need1;
+  rank_bin_1024(sl.h, rk, sl.wtot, &sl.bin, &sl.need, b1, need1);
+  uint32_t tau = (base1 + (uint32_t)b1) << sh1;
+  if (sh1 > 0) {
+    const int sh2 = max(sh1 - 12, 0);
+    const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
+    for (int i = tid; i < 4096; i += 1024) sl.h[i] = 0;
+    __syncthreads();
+    each_sample([&](uint32_t k2) {
+      if ((k2 >> sh1) - base1 == (uint32_t)b1) atomicAdd(&sl.h[(k2 >> sh2) & mask2], 1u);
+    });
+    __syncthreads();
+    int b2;
+    uint32_t need2;
+    rank_bin_1024(sl.h, need1, sl.wtot, &sl.bin, &sl.need, b2, need2);
+    tau |= (uint32_t)b2 << sh2;
+  }
 
-  // winners: definite entries, then candidates at or above the threshold
-  for (int i = tid; i < ndef; i += blockDim.x) out[i] = p.defbuf[(int64_t)t * p.k + i];
-  if (tid == 0) s_cnt = ndef;
-  __syncthreads();
-  for (int i = tid; i < nsrc; i += blockDim.x) {
-    uint32_t key, li;
-    if (!fetch(i, key, li)) continue;
-    if ((composite(key, li) >> shift) >= thr) {
-      const int pos = atomicAdd(&s_cnt, 1);
-      if (pos < DSA_MAX_TOPK) out[pos] = (int)li;
-    }
-  }
-  __syncthreads();
-  // order the K winners by index: mark them in an LDS bitmap window by window
-  // (256K indices per window), then each thread emits the set bits of its 8
-  // words at its prefix-sum offset
-  uint32_t* bm = cand_lds;  // the candidate area (8192 words) is free now
-  int emitted = 0;
-  for (int w0 = 0; w0 < vis; w0 += kWinIdx) {
-    for (int i = tid; i < kWinIdx / 32; i += blockDim.x) bm[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < K; i += blockDim.x) {
-      const int li = out[i] - w0;
-      if (li >= 0 && li < kWinIdx) atomicOr(&bm[li >> 5], 1u << (li & 31));
-    }
-    __syncthreads();
-    uint32_t words[8];
-    int cnt = 0;
+  // ---- candidates: keys >= tau, compacted by a block exclusive prefix sum
+  int mine = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      words[i] = bm[tid * 8 + i];
-      cnt += __popc(words[i]);
-    }
-    // exclusive prefix over the 1024 threads: waves of 64, then 16 wave totals
-    const int lane = tid & 63, wave = tid >> 6;
-    int inc = cnt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(inc, off);
-      if (lane >= off) inc += o;
-    }
-    if (lane == 63) h[wave] = (uint32_t)inc;
-    __syncthreads();
-    int before = emitted + inc - cnt;
-    for (int w = 0; w < wave; ++w) before += (int)h[w];
-    int tot = 0;
-    for (int w = 0; w < 16; ++w) tot += (int)h[w];
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t x = words[i];
-      while (x) {
-        const int b = __ffs(x) - 1;
-        x &= x - 1;
-        const int li = w0 + (tid * 8 + i) * 32 + b;
-        idx[before] = li;
-        if (rows) rows[before] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
-        ++before;
-      }
+    for (int c = 0; c < 4; ++c) mine += (key[i][c] >= tau && key[i][c] != 0u) ? 1 : 0;
+  int inc = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) s_wsum[wave] = inc;
+  __syncthreads();
+  int pos = inc - mine, ncand = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) pos += s_wsum[w];
+    ncand += s_wsum[w];
+  }
+  // estimate missed (rare): select over the row re-read from memory
+  const bool from_row = ncand < K || ncand > kFusedCap;
+  if (!from_row) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (key[i][c] >= tau && key[i][c] != 0u) {
+          ck[pos] = key[i][c];
+          ci[pos] = (uint32_t)(4 * tid + 4096 * i + c);
+          ++pos;
+        }
+  }
+  __syncthreads();
+  auto each = [&](auto f) {
+    if (from_row) {
+      for (int i = tid; i < vis; i += 1024) f(composite(order_key(row[i]), (uint32_t)i));
+    } else {
+      for (int i = tid; i < ncand; i += 1024) f(composite(ck[i], ci[i]));
     }
-    emitted += tot;
-    __syncthreads();
-  }
-  for (int j = K + tid; j < p.k; j += blockDim.x) {
-    idx[j] = -1;
-    if (rows) rows[j] = -1;
-  }
-  if (p.count && tid == 0) p.count[t] = K;
+  };
+  int hi_sh;
+  uint64_t prefix;
+  select_top(each, (uint32_t)K, sl, hi_sh, prefix);
+  if (tid == 0) sl.cnt = 0;
+  __syncthreads();
+  each([&](uint64_t v2) {
+    if ((v2 >> hi_sh) >= prefix) {
+      const int q = atomicAdd(&sl.cnt, 1);
+      if (q < DSA_MAX_TOPK) out[q] = (int)(0xFFFFFFFFu - (uint32_t)v2);
+    }
+  });
+  __syncthreads();
+  order_and_store(p, out, K, vis, cand, 2 * kFusedCap, ord, tpre, sl.wtot, t, r, idx, rows);
 }
 
 __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, const int32_t* __restrict__ tok_req,
@@ -410,14 +680,13 @@ __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, 
 }
 
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
-  // histograms and counters are contiguous in the workspace: one fill
-  const int64_t nz = (int64_t)(p.ctr - p.hist) + (int64_t)p.T * 4;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0,
-                     stream, p.hist, nz, 0u);
-  dim3 grid(p.nslices, p.T);
-  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(topk_finalize_kernel, dim3(p.T), dim3(1024), 0, stream, p);
+  if (p.max_vis <= kFusedMax) {
+    hipLaunchKernelGGL(topk_fused_kernel, dim3(p.T), dim3(1024), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+  }
+  hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.T), dim3(1024), 0, stream, p);
+  hipLaunchKernelGGL(topk_filter_kernel, dim3(p.nslices, p.T), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(topk_finalize_kernel, dim3(p.T), dim3(1024), kFinalLds, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

@@ -145,10 +145,15 @@ def _topk_alone(scores, vis, k, gpu):
     return idx.cpu().numpy(), cnt.cpu().numpy()
 
 
-@pytest.mark.parametrize("kind", ["random", "ties", "all_equal", "short_rows", "k1", "negative"])
-def test_topk_exact_on_same_scores(kind, gpu):
+@pytest.mark.parametrize("ld", [40000, 8000])
+@pytest.mark.parametrize("kind", ["random", "ties", "all_equal", "short_rows", "k1", "negative", "sampled_high"])
+def test_topk_exact_on_same_scores(kind, ld, gpu):
+    # ld 40000: threshold / filter / finalize kernels; ld 8000: the one-workgroup
+    # kernel for short rows.  "all_equal" overflows the candidate buffers and
+    # "sampled_high" (large scores only where the threshold sample looks) makes
+    # the sampled threshold too high: both take the whole-row fallback.
     g = np.random.default_rng(42)
-    T, ld, k = 6, 40000, 2048
+    T, k = 6, 2048
     if kind == "random":
         s = g.standard_normal((T, ld)).astype(np.float32) * 50 + 100
     elif kind == "ties":
@@ -160,11 +165,17 @@ def test_topk_exact_on_same_scores(kind, gpu):
     elif kind == "k1":
         s = g.integers(0, 5, (T, ld)).astype(np.float32)
         k = 1
-    else:
+    elif kind == "negative":
         s = -np.abs(g.standard_normal((T, ld)).astype(np.float32))
         s[:, ::7] = 0.0
         s[:, 3::7] = -0.0
-    vis = [ld, ld - 1, 30001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 40000, 12345, 8193, 4097]
+    else:
+        s = g.standard_normal((T, ld)).astype(np.float32)
+        s[:, (np.arange(ld) % 256) < 16] += 1000.0
+    if ld == 40000:
+        vis = [ld, ld - 1, 30001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 40000, 12345, 8193, 4097]
+    else:
+        vis = [ld, ld - 1, 5001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 8000, 6345, 4097, 2049]
     idx, cnt = _topk_alone(torch.from_numpy(s), vis, k, gpu)
     for t in range(T):
         ref, _ = O.topk(s[t, : vis[t]].astype(np.float64), k)
