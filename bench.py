@@ -53,6 +53,26 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "repeats": 5}))
 
 
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes (read + written) per launch of `stage`'s kernels on `workload`,
+    from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised in
+    profiles/traffic.json (already scaled by the copy calibration).  None when
+    no such run exists or the library sources changed since it was taken."""
+    from sparse_attention_03_amd import build as B
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256_16") != B.source_digest():
+        return None
+    st = rec.get("workloads", {}).get(workload, {}).get(stage)
+    if not st:
+        return None
+    return int(st["fetch_bytes"] + st["write_bytes"])
+
+
 def cpu_baseline(wl, seconds, bytes_of_rows):
     """Time the oracle, request by request, until `seconds` have elapsed."""
     from oracle import dsa as O
@@ -170,6 +190,7 @@ def main():
         roof = {"bound": "hbm", "achieved": nbytes / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "traffic": None}
     roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(spec.name, dom)
     roof["achieved"] = round(roof["achieved"], 2)
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
 

@@ -44,3 +44,17 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+
+
+def source_digest() -> str:
+    """First 16 hex digits of the sha256 of the library sources, the public
+    header and the compile flags: names the build a profile was taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(HERE)
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(root, "include", "dsa.h")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()[:16]
