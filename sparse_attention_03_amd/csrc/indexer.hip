@@ -32,13 +32,53 @@ constexpr int kIdxKT = 4;              // 16-key tiles per wave per round
 constexpr int kIdxRound = kIdxWaves * kIdxKT * 16;  // 256 keys per round
 constexpr int kQPad = 136;             // bf16 per head row in LDS (272 B: conflict-free reads)
 
-// Raw bytes of one round (kIdxKT tiles of 16 keys) for one lane.
+// Raw key codes of one round (kIdxKT tiles of 16 keys) for one lane.  The
+// per-key side data (FP8 scale, MXFP4 E8M0 codes) is staged in LDS for the
+// whole chunk up front, so the round loop issues nothing but these 16-byte
+// code loads.
 template <int KFMT> struct RawKeys {
   i32x4 v[kIdxKT][KFMT == DSA_KEY_FP8 ? 2 : 1];
-  uint32_t sc[kIdxKT];   // MXFP4: E8M0 code of the lane's 32 dims
   bool ok[kIdxKT];       // page present and tile inside the chunk
-  float own_scale;       // FP8 scale of the key this lane scores (tile g, key c)
+  uint32_t sc[kIdxKT];   // (side data read in the loop) MXFP4: E8M0 codes of key c of tile kt
+  float own_scale;       // (side data read in the loop) FP8 scale of the key this lane stores
 };
+
+// Side data of the chunk's keys in LDS, one word per key: the FP8 scale (-inf
+// on an absent page, so the key is never selected) or the four E8M0 codes of
+// an MXFP4 key.  Loaded with all of a thread's loads in flight at once.
+constexpr int kIdxMaxChunk = 4096;
+template <int KFMT>
+__device__ __forceinline__ void stage_side(const IndexerParams& p, const int* pg_lds, int lp0, int k0, int kend, int P,
+                                           uint32_t* side) {
+  constexpr int kPer = kIdxMaxChunk / 256;
+  uint32_t v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = k0 + (int)threadIdx.x + 256 * i;
+    const int pg_read = pg_lds[min(s, kend - 1) - (lp0 << p.plog2) >> p.plog2];
+    const int pg = s < kend ? pg_read : -1;
+    const uint8_t* page = p.keys + (int64_t)max(pg, 0) * p.page_bytes;
+    const int slot = s & (P - 1);
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(page + P * (KFMT == DSA_KEY_FP8 ? 128 : 64) + slot * 4);
+    v[i] = KFMT == DSA_KEY_FP8 ? (pg >= 0 ? x : __float_as_uint(-__builtin_inff())) : x;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) side[threadIdx.x + 256 * i] = v[i];
+}
+
+// The 8 dims lane group g supplies at k-step kk of the 128-dim dot product
+// (the same assignment for the query A and the key B fragments, so the
+// k-sum is the full dot product).  FP8 keys: the four lane groups of a key
+// read its first 64 bytes in one instruction and its last 64 in a second
+// (16 bytes each, contiguous per key); MXFP4: lane group g holds the 32
+// codes under E8M0 scale g.
+// (COAL = false: FP8 lane group g reads bytes 32g .. 32g+31 of each key, as
+// the multi-row kernel does, whose A fragments come from LDS.)
+template <int KFMT, bool COAL>
+__device__ __forceinline__ int kdim(int kk, int g) {
+  if (KFMT == DSA_KEY_FP8 && COAL) return kk < 2 ? 16 * g + 8 * kk : 64 + 16 * g + 8 * (kk - 2);
+  return 32 * g + 8 * kk;
+}
 
 // Page ids of the chunk's logical pages, staged in LDS once per workgroup so a
 // round's key loads never wait on a block-table load.
@@ -49,7 +89,9 @@ constexpr int kIdxMaxRows = kIndexerMaxRowsPerPass;  // rows staged in LDS per p
 // absent page reads page 0 instead and its scores are masked afterwards):
 // loads under a branch would make the compiler wait for all of them before
 // any is used, so the next round's loads could not overlap this round.
-template <int KFMT>
+// SIDE: the side data comes from the LDS copy (stage_side) instead of loads
+// issued with the round.
+template <int KFMT, bool SIDE>
 __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg_lds, int lp0, int base, int kend,
                                            int wave, int g, int c, int P, RawKeys<KFMT>& raw) {
   const int last = ((kend - 1) >> p.plog2) - lp0;  // last staged page entry
@@ -58,30 +100,35 @@ __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg
   for (int kt = 0; kt < kIdxKT; ++kt) {
     const int s0 = base + (wave * kIdxKT + kt) * 16;
     const int e = min((s0 >> p.plog2) - lp0, last);
-    const int pg = s0 < kend ? pg_lds[e] : -1;
+    int pg;
+    if (SIDE) {
+      const int pg_read = pg_lds[e];  // read unconditionally: no branch around the loads below
+      pg = s0 < kend ? pg_read : -1;
+    } else {
+      pg = s0 < kend ? pg_lds[e] : -1;
+    }
     pgs[kt] = pg;
     raw.ok[kt] = pg >= 0;
     const uint8_t* page = p.keys + (int64_t)max(pg, 0) * p.page_bytes;
     const int slot = (s0 & (P - 1)) + c;
     if (KFMT == DSA_KEY_FP8) {
-      const uint8_t* kp = page + slot * 128 + 32 * g;
+      // SIDE (single-row kernel): the coalesced lane-to-byte map of kdim<FP8, true>
+      const uint8_t* kp = page + slot * 128 + (SIDE ? 16 : 32) * g;
       raw.v[kt][0] = ld16(kp);
-      raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16(kp + 16);
+      raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16(kp + (SIDE ? 64 : 16));
     } else {
       raw.v[kt][0] = ld16(page + slot * 64 + 16 * g);
-      raw.sc[kt] = page[P * 64 + slot * 4 + g];
+      if (!SIDE) raw.sc[kt] = *reinterpret_cast<const uint32_t*>(page + P * 64 + slot * 4);
     }
   }
-  if (KFMT == DSA_KEY_FP8) {
-    // the scale of the key this lane stores (tile g, key c)
+  if (KFMT == DSA_KEY_FP8 && !SIDE) {
+    // one load for the scale of the key this lane stores (tile g, key c)
     int pg = pgs[0];
 #pragma unroll
     for (int kt = 1; kt < kIdxKT; ++kt)
       if (g == kt) pg = pgs[kt];
     const int slot = ((base + (wave * kIdxKT + g) * 16) & (P - 1)) + c;
     raw.own_scale = *reinterpret_cast<const float*>(p.keys + (int64_t)max(pg, 0) * p.page_bytes + P * 128 + slot * 4);
-  } else {
-    raw.own_scale = 1.f;
   }
 }
 
@@ -90,7 +137,8 @@ __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg
 // power-of-two block scales are applied exactly during dequantisation), or
 // -inf for an absent page so the key is never selected.
 template <int KFMT>
-__device__ __forceinline__ void dequant_tile(const RawKeys<KFMT>& raw, int kt, bf16x8 (&b)[4]) {
+__device__ __forceinline__ void dequant_tile(const RawKeys<KFMT>& raw, int kt, bf16x8 (&b)[4], uint32_t e8m0x4 = 0,
+                                             int g = 0) {
   if (KFMT == DSA_KEY_FP8) {
     const i32x4 x = raw.v[kt][0], y = raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0];
     b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
@@ -99,7 +147,7 @@ __device__ __forceinline__ void dequant_tile(const RawKeys<KFMT>& raw, int kt, b
     b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
   } else {
     const i32x4 x = raw.v[kt][0];
-    const float sc = e8m0_to_f32(raw.sc[kt]);
+    const float sc = e8m0_to_f32((e8m0x4 >> (8 * g)) & 0xFFu);
     b[0] = e2m1x8_to_bf16x8(x[0], sc);
     b[1] = e2m1x8_to_bf16x8(x[1], sc);
     b[2] = e2m1x8_to_bf16x8(x[2], sc);
@@ -107,18 +155,19 @@ __device__ __forceinline__ void dequant_tile(const RawKeys<KFMT>& raw, int kt, b
   }
 }
 
-// Multiplier of the score this lane stores (key c of tile g): the FP8 key
-// scale, 1 for MXFP4 (whose power-of-two block scales are applied exactly
-// during dequantisation), or -inf for an absent page so the key is never
-// selected.  A tile on an absent page holds page 0's bytes; every score it
-// produces is replaced by this -inf.
-template <int KFMT>
-__device__ __forceinline__ float own_multiplier(const RawKeys<KFMT>& raw, int g) {
+// Multiplier of the score this lane stores (key s_own = tile g, key c): the
+// FP8 key scale from the staged side data (-inf on an absent page), 1 for
+// MXFP4 (whose power-of-two block scales are applied exactly during
+// dequantisation) or -inf on an absent page.  A tile on an absent page holds
+// page 0's bytes; every score it produces is replaced by this -inf.
+template <int KFMT, bool SIDE>
+__device__ __forceinline__ float own_multiplier(const RawKeys<KFMT>& raw, int g, const uint32_t* side, int i_own) {
+  if (KFMT == DSA_KEY_FP8 && SIDE) return __uint_as_float(side[i_own]);
   bool own_ok = raw.ok[0];
 #pragma unroll
   for (int kt = 1; kt < kIdxKT; ++kt)
     if (g == kt) own_ok = raw.ok[kt];
-  return own_ok ? raw.own_scale : -__builtin_inff();
+  return own_ok ? (KFMT == DSA_KEY_FP8 ? raw.own_scale : 1.f) : -__builtin_inff();
 }
 
 template <int KFMT>
@@ -194,8 +243,8 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
       const __bf16* qrow = &qs[(j * 32) * kQPad];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qrow[c * kQPad + 32 * g + 8 * kk]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qrow[(16 + c) * kQPad + 32 * g + 8 * kk]);
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qrow[c * kQPad + kdim<KFMT, false>(kk, g)]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qrow[(16 + c) * kQPad + kdim<KFMT, false>(kk, g)]);
 #pragma unroll
         for (int kt = 0; kt < kIdxKT; ++kt) {
           if (kk == 0) {
@@ -233,10 +282,10 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
     auto do_round = [&](int base, RawKeys<KFMT>& raw, int next) {
       bf16x8 bfr[kIdxKT][4];
 #pragma unroll
-      for (int kt = 0; kt < kIdxKT; ++kt) dequant_tile<KFMT>(raw, kt, bfr[kt]);
-      const float own_mul = own_multiplier<KFMT>(raw, g);
-      if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
+      for (int kt = 0; kt < kIdxKT; ++kt) dequant_tile<KFMT>(raw, kt, bfr[kt], raw.sc[kt], g);
       const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
+      const float own_mul = own_multiplier<KFMT, false>(raw, g, nullptr, 0);
+      if (next < kend) load_round<KFMT, false>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
       f32x4 acc[kIdxKT][2];
       for (int j = 0; j < nr; ++j) {
         mfma_row(j, bfr, acc);
@@ -247,7 +296,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
     // Software pipeline: the raw key bytes of round i+1 are in flight while
     // round i is dequantised and multiplied.
     RawKeys<KFMT> raw;
-    load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
+    load_round<KFMT, false>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
     for (int base = k0; base < kend; base += kIdxRound) do_round(base, raw, base + kIdxRound);
 
     t0 += p.qrows;
@@ -281,8 +330,13 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
 // its eight MFMAs, and the kernel is small enough for three to four waves per
 // SIMD -- enough HBM requests in flight to stream the keys at full rate.
 template <int KFMT>
-__global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) {
+__global__ __launch_bounds__(256, 4) void indexer_bf16_row_kernel(IndexerParams p) {
   __shared__ int pg_lds[kIdxMaxChunkPages];
+  __shared__ uint32_t side[kIdxMaxChunk];
+  // the chunk's scores collect in LDS and leave in one coalesced pass at the
+  // end: the round loop then holds no global store, whose operand registers
+  // the compiler would otherwise wait on before reusing them
+  __shared__ float sc_out[kIdxMaxChunk];
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -304,9 +358,11 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + 32 * g + 8 * kk));
+      qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
   const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
   const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
+  __syncthreads();
+  stage_side<KFMT>(p, pg_lds, lp0, k0, kend, P, side);
   __syncthreads();
 
   // two raw buffers: the keys of the next round load while this one computes
@@ -315,7 +371,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
 #pragma unroll
     for (int kt = 0; kt < kIdxKT; ++kt) {
       bf16x8 b[4];
-      dequant_tile<KFMT>(cur, kt, b);
+      dequant_tile<KFMT>(cur, kt, b, side[base - k0 + (wave * kIdxKT + kt) * 16 + c], g);
       f32x4 a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -331,25 +387,33 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
       }
       v[kt] = x;
     }
-    const float own_mul = own_multiplier<KFMT>(cur, g);
-    const float tot = rows_reduce_scatter4(v, g);
     const int s_own = base + wave * (kIdxKT * 16) + lane;
-    if (s_own < kend) p.scores[(int64_t)t * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
+    const float own_mul = own_multiplier<KFMT, true>(cur, g, side, s_own - k0);
+    const float tot = rows_reduce_scatter4(v, g);
+    sc_out[s_own - k0] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
   };
-  // Loads past the last round re-read the last round (cache hits), so every
-  // iteration issues the same loads and the waits for a buffer never cover
-  // the other one.
+  // Three raw buffers in rotation: two rounds of keys are in flight while one
+  // computes (the compute is short; keeping HBM busy needs the bytes in
+  // flight).  Loads past the last round re-read the last round (cache hits),
+  // so every step issues the same loads and the waits stay exact.
   const int last_base = k0 + (kend - 1 - k0) / kIdxRound * kIdxRound;
-  RawKeys<KFMT> ra, rb;
-  load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, ra);
-  for (int base = k0; base < kend; base += 2 * kIdxRound) {
+  RawKeys<KFMT> ra, rb, rc;
+  load_round<KFMT, true>(p, pg_lds, lp0, k0, kend, wave, g, c, P, ra);
+  load_round<KFMT, true>(p, pg_lds, lp0, min(k0 + kIdxRound, last_base), kend, wave, g, c, P, rb);
+  for (int base = k0; base < kend; base += 3 * kIdxRound) {
     const int b1 = base + kIdxRound, b2 = base + 2 * kIdxRound;
-    load_round<KFMT>(p, pg_lds, lp0, min(b1, last_base), kend, wave, g, c, P, rb);
+    load_round<KFMT, true>(p, pg_lds, lp0, min(b2, last_base), kend, wave, g, c, P, rc);
     round(base, ra);
     if (b1 >= kend) break;
-    load_round<KFMT>(p, pg_lds, lp0, min(b2, last_base), kend, wave, g, c, P, ra);
+    load_round<KFMT, true>(p, pg_lds, lp0, min(b2 + kIdxRound, last_base), kend, wave, g, c, P, ra);
     round(b1, rb);
+    if (b2 >= kend) break;
+    load_round<KFMT, true>(p, pg_lds, lp0, min(b2 + 2 * kIdxRound, last_base), kend, wave, g, c, P, rb);
+    round(b2, rc);
   }
+  __syncthreads();
+  float* out = p.scores + (int64_t)t * p.ld;
+  for (int i = tid; i < kend - k0; i += 256) out[k0 + i] = sc_out[i];
 }
 
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
