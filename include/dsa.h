@@ -30,21 +30,27 @@
  *
  * Paged caches (same page, "One KV cache, three states": the engine turns the
  * block table into kernel page addresses before each step).  A pool is a
- * sequence of physical pages `page_bytes` apart; a page holds P = 2^p tokens,
- * structure-of-arrays inside the page, each region starting on a 16-byte
- * boundary:
+ * sequence of physical pages `page_bytes` apart; a page holds P = 2^p tokens.
+ * Index-key pages are scanned whole, so they are structure-of-arrays, each
+ * region starting on a 16-byte boundary:
  *     key   FP8    [P x 128 E4M3][P x fp32 scale]                     132 B/token
  *     key   MXFP4  [P x 64 B E2M1 pairs, low nibble first][P x 4 E8M0]  68 B/token
- *     lat   BF16   [P x 576 bf16]                                      1152 B/token
- *     lat   FP8    [P x 576 E4M3][P x fp32 scale]                       580 B/token
- *     lat   NVFP4  [P x 256 B E2M1 pairs (dims 0..511)]
- *                  [P x 32 E4M3 scales, one per 16 dims]
- *                  [P x 64 E4M3 rope dims 512..575, unscaled]           352 B/token
- * page_bytes may exceed P x (bytes per token): several layers' pages can share
- * one block row.  Logical token s of request r lives in physical page
- * block_table[r * bt_stride + (s >> p)], slot s & (P-1); with block_table ==
- * NULL the cache is non-paged and request r owns physical page r.  A physical
- * row id is page * P + slot.  Keys and latents of one token share page ids.
+ * Latent rows are gathered one by one, so a latent page is P rows, each row
+ * padded to whole 128-byte lines and holding all of its bytes (a gathered row
+ * then fetches only its own lines; page_bytes a multiple of 128 keeps rows
+ * line-aligned):
+ *     lat   BF16   row 1152 B: [576 bf16]                              1152 B/token
+ *     lat   FP8    row  640 B: [576 E4M3][fp32 scale][60 B unused]      580 B/token
+ *     lat   NVFP4  row  384 B: [256 B E2M1 pairs (dims 0..511)]
+ *                              [32 E4M3 scales, one per 16 dims]
+ *                              [64 E4M3 rope dims 512..575, unscaled]
+ *                              [32 B unused]                           352 B/token
+ * (B/token counts the data bytes.)  page_bytes may exceed P x (bytes per row
+ * or token): several layers' pages can share one block row.  Logical token s
+ * of request r lives in physical page block_table[r * bt_stride + (s >> p)],
+ * slot s & (P-1); with block_table == NULL the cache is non-paged and request
+ * r owns physical page r.  A physical row id is page * P + slot.  Keys and
+ * latents of one token share page ids.
  *
  * Latent rows are 576-d: 512 "nope" dims followed by 64 "rope" dims; the value
  * vector is the first 512 dims.  FP8 E4M3 is OCP E4M3FN (bias 7, max 448).

@@ -61,26 +61,32 @@ def key_pages(pool: np.ndarray, fmt: str, P: int, pages: np.ndarray) -> np.ndarr
     return vals.reshape(n * P, DI)
 
 
+LAT_ROW_STRIDE = {"bf16": 1152, "fp8": 640, "nvfp4": 384}   # bytes per latent row in a page
+
+
 def lat_rows(pool: np.ndarray, fmt: str, P: int, rows: np.ndarray) -> np.ndarray:
-    """Dequantise latent rows (physical ids page*P+slot) -> fp64 [m, 576]."""
+    """Dequantise latent rows (physical ids page*P+slot) -> fp64 [m, 576].
+
+    A latent page holds P rows of LAT_ROW_STRIDE[fmt] bytes: BF16 [576 bf16];
+    FP8 [576 E4M3][fp32 scale][pad]; NVFP4 [256 B E2M1 pairs][32 E4M3 block
+    scales][64 E4M3 rope][pad] ("One KV cache, three states": 576-byte FP8 and
+    352-byte NVFP4 latents; the padding is unused)."""
     rows = np.asarray(rows, dtype=np.int64)
     page, slot = rows // P, rows % P
+    stride = LAT_ROW_STRIDE[fmt]
 
-    def region(off, width):
-        cols = off + slot[:, None] * width + np.arange(width)[None, :]
+    def field(off, width):
+        cols = slot[:, None] * stride + off + np.arange(width)[None, :]
         return pool[page[:, None], cols]
 
     if fmt == "bf16":
-        raw = region(0, 1152)
-        return C.bf16(raw.view("<u2"))
+        return C.bf16(field(0, 1152).view("<u2"))
     if fmt == "fp8":
-        codes = region(0, 576)
-        scale = C.f32(region(576 * P, 4))
-        return C.e4m3(codes) * scale
+        return C.e4m3(field(0, 576)) * C.f32(field(576, 4))
     if fmt == "nvfp4":
-        nope = C.e2m1_packed(region(0, 256))                 # [m, 512]
-        sc = C.e4m3(region(256 * P, 32))                     # [m, 32]
-        rope = C.e4m3(region(288 * P, 64))                   # [m, 64]
+        nope = C.e2m1_packed(field(0, 256))                  # [m, 512]
+        sc = C.e4m3(field(256, 32))                          # [m, 32]
+        rope = C.e4m3(field(288, 64))                        # [m, 64]
         return np.concatenate([nope * np.repeat(sc, 16, axis=-1), rope], axis=-1)
     raise ValueError(fmt)
 

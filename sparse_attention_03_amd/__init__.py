@@ -31,7 +31,8 @@ KEY_FMT = {"fp8": KEY_FP8, "mxfp4": KEY_MXFP4}
 LAT_FMT = {"bf16": LAT_BF16, "fp8": LAT_FP8, "nvfp4": LAT_NVFP4}
 Q_FMT = {"bf16": Q_BF16, "fp8": Q_FP8}
 KEY_TOKEN_BYTES = {KEY_FP8: 132, KEY_MXFP4: 68}
-LAT_TOKEN_BYTES = {LAT_BF16: 1152, LAT_FP8: 580, LAT_NVFP4: 352}
+LAT_TOKEN_BYTES = {LAT_BF16: 1152, LAT_FP8: 580, LAT_NVFP4: 352}   # data bytes per token
+LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per latent row in a page
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
            "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",

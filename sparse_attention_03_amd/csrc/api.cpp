@@ -27,8 +27,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int key_token_bytes(int fmt) { return fmt == DSA_KEY_FP8 ? 132 : fmt == DSA_KEY_MXFP4 ? 68 : 0; }
-int lat_token_bytes(int fmt) {
-  return fmt == DSA_LAT_BF16 ? 1152 : fmt == DSA_LAT_FP8 ? 580 : fmt == DSA_LAT_NVFP4 ? 352 : 0;
+// bytes per latent row inside a page (the row's data padded to whole 128-byte lines)
+int lat_row_bytes(int fmt) {
+  return fmt == DSA_LAT_BF16 ? 1152 : fmt == DSA_LAT_FP8 ? 640 : fmt == DSA_LAT_NVFP4 ? 384 : 0;
 }
 
 dsa_status check_cache(const dsa_cache& c, int token_bytes, const char* what) {
@@ -95,13 +96,11 @@ MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
   } else if (a.num_splits > 0) {
     want = a.num_splits;
   } else {
-    // Fill the resident slots in one round: the kernel holds one wave per SIMD
-    // (four per CU), a workgroup has nw waves, so 256 * (4 / nw) workgroups are
-    // resident at once; a second, partial round would cost a whole extra pass.
-    const int groups = (pl.ntiles + 3) / 4;
-    const int nw = (pl.ntiles + groups - 1) / groups;
-    const int64_t resident = 256 * (4 / nw);
-    const int64_t per_split = (int64_t)a.num_rows * groups;
+    // Fill the resident workgroup slots in one round; a second, partial round
+    // would cost a whole extra pass.
+    const dsa::MlaShape sh = dsa::mla_shape(pl.ntiles);
+    const int64_t resident = 256 * sh.resident_per_cu;
+    const int64_t per_split = (int64_t)a.num_rows * sh.groups;
     want = (int)std::min<int64_t>(64, std::max<int64_t>(1, resident / per_split));
   }
   want = std::max(1, std::min({want, (a.k + 15) / 16, 64}));
@@ -129,7 +128,7 @@ dsa_status check_mla(const dsa_mla_args* a) {
   if (!a->out || !aligned(a->out, 16)) return fail(DSA_ERR_INVALID_ARG, "mla: out null or not 16-byte aligned");
   if (!(std::isfinite(a->sm_scale) && a->sm_scale > 0.f)) return fail(DSA_ERR_INVALID_ARG, "mla: sm_scale");
   if (a->num_splits < 0 || a->num_splits > DSA_MAX_TOPK / 16) return fail(DSA_ERR_INVALID_ARG, "mla: num_splits");
-  return check_cache(a->latents, lat_token_bytes(a->latents.fmt), "mla latents");
+  return check_cache(a->latents, lat_row_bytes(a->latents.fmt), "mla latents");
 }
 
 dsa_status run_mla(const dsa_mla_args* a, hipStream_t stream, bool prefill) {

@@ -82,6 +82,20 @@ struct MlaParams {
   float* part_lse;          // [T][nsplit][H]
 };
 
+// Workgroup shape of the sparse-MLA kernels: `groups` workgroups per (row,
+// split), each with nw head tiles of 16 heads, one wave per head tile; the
+// kernels hold one wave per SIMD, so 4 / nw workgroups share a CU.
+struct MlaShape {
+  int groups, nw, resident_per_cu;
+};
+inline MlaShape mla_shape(int ntiles) {
+  MlaShape s;
+  s.groups = (ntiles + 3) / 4;
+  s.nw = (ntiles + s.groups - 1) / s.groups;
+  s.resident_per_cu = 4 / s.nw;
+  return s;
+}
+
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream);

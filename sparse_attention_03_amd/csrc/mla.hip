@@ -61,6 +61,15 @@ template <> struct Geo<DSA_LAT_FP8> { static constexpr int SEGS = 9; };    // 57
 template <> struct Geo<DSA_LAT_BF16> { static constexpr int SEGS = 18; };  // 576 bf16
 template <> struct Geo<DSA_LAT_NVFP4> { static constexpr int SEGS = 5; };  // 4 x 128 E2M1, 64 rope
 
+// Row layout inside a latent page: every row padded to whole 128-byte lines
+// with all of its bytes inside, so a gathered row costs only its own lines.
+template <int FMT> struct LatRow {
+  static constexpr int kBytes = FMT == DSA_LAT_BF16 ? 1152 : FMT == DSA_LAT_FP8 ? 640 : 384;
+  static constexpr int kScale = 576;   // FP8 row: [576 E4M3][fp32 scale][pad]
+  static constexpr int kScales = 256;  // NVFP4 row: [256 B E2M1][32 E4M3 block scales]
+  static constexpr int kRope = 288;    //            [64 E4M3 rope][pad]
+};
+
 struct RowPtr {
   const uint8_t* data;   // FP8/BF16 row, NVFP4 codes
   const uint8_t* aux;    // NVFP4 block scales
@@ -75,14 +84,11 @@ template <int FMT>
 __device__ __forceinline__ RowPtr row_ptr(const MlaParams& p, int id, int P) {
   RowPtr r{nullptr, nullptr, nullptr};
   if (!row_ok(id, p)) return r;
-  const uint8_t* page = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
-  const int slot = id & (P - 1);
-  if (FMT == DSA_LAT_FP8) r.data = page + slot * 576;
-  if (FMT == DSA_LAT_BF16) r.data = page + (int64_t)slot * 1152;
+  const uint8_t* row = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes + (int64_t)(id & (P - 1)) * LatRow<FMT>::kBytes;
+  r.data = row;
   if (FMT == DSA_LAT_NVFP4) {
-    r.data = page + slot * 256;
-    r.aux = page + 256 * P + slot * 32;
-    r.rope = page + 288 * P + slot * 64;
+    r.aux = row + LatRow<FMT>::kScales;
+    r.rope = row + LatRow<FMT>::kRope;
   }
   return r;
 }
@@ -141,10 +147,13 @@ __device__ __forceinline__ void seg_store(__bf16* lrow, int s0, int q, const i32
 }
 
 // One 16-row tile for one 16-head tile: QK from the LDS tile, online softmax
-// (lazy rescale), PV into the accumulators.  rv/rsc: row ids (-1 = absent)
-// and per-row value multipliers of the tile.
+// (lazy rescale), PV into the accumulators of value dims 64*a0 .. 64*(a0+NA)
+// (NA = 8: all 512 dims; NA = 4: the half this wave owns).  rv/rsc: row ids
+// (-1 = absent) and per-row value multipliers of the tile.
+template <int NA>
 __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, const float* rsc, const int* rv,
-                                         const bf16x8 (&qf)[18], f32x4 (&O)[32], float& m, float& l, int g, int c) {
+                                         const bf16x8 (&qf)[18], f32x4 (&O)[NA * 4], float& m, float& l, int g, int c,
+                                         int a0) {
   // ---- QK: S^T tile, rows 4g + i of head c
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   {
@@ -194,14 +203,15 @@ __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
 #pragma unroll
-    for (int x = 0; x < 32; ++x)
+    for (int x = 0; x < NA * 4; ++x)
 #pragma unroll
       for (int i = 0; i < 4; ++i) O[x][i] *= ai[i];
   }
 
   // ---- PV: O[heads 4g+i][dims 64a + 4c + u] += P . V over the 16 rows
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
+  for (int aa = 0; aa < NA; ++aa) {
+    const int a = a0 + aa;
     i32x2 vb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) vb[j] = *reinterpret_cast<const i32x2*>(&lat[(4 * g + j) * kLPad + 64 * a + 4 * c]);
@@ -211,15 +221,17 @@ __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, 
       const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
       const i32x2 f = {(int)__builtin_amdgcn_perm((uint32_t)vb[1][half], (uint32_t)vb[0][half], sel),
                        (int)__builtin_amdgcn_perm((uint32_t)vb[3][half], (uint32_t)vb[2][half], sel)};
-      O[a * 4 + u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, f), O[a * 4 + u]);
+      O[aa * 4 + u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, f), O[aa * 4 + u]);
     }
   }
 }
 
-// Normalise the accumulators of heads 4g+i and write the output row (one
-// split) or the split's partial output and LSE.
-__device__ __forceinline__ void mla_finish(const MlaParams& p, const f32x4 (&O)[32], float m, float l, int t,
-                                           int split, int ht, int g, int c) {
+// Normalise the accumulators of heads 4g+i (value dims 64*a0 .. 64*(a0+NA))
+// and write the output row (one split) or the split's partial output; the
+// wave holding dims from 0 writes the LSE.
+template <int NA>
+__device__ __forceinline__ void mla_finish(const MlaParams& p, const f32x4 (&O)[NA * 4], float m, float l, int t,
+                                           int split, int ht, int g, int c, int a0) {
   float li[4], mi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -235,11 +247,11 @@ __device__ __forceinline__ void mla_finish(const MlaParams& p, const f32x4 (&O)[
     float* dst = final_out ? p.out + ((int64_t)t * p.H + h) * 512
                            : p.part_o + (((int64_t)t * p.nsplit + split) * p.H + h) * 512;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      f32x4 v = {O[a * 4 + 0][i] * inv, O[a * 4 + 1][i] * inv, O[a * 4 + 2][i] * inv, O[a * 4 + 3][i] * inv};
-      *reinterpret_cast<f32x4*>(dst + 64 * a + 4 * c) = v;
+    for (int aa = 0; aa < NA; ++aa) {
+      f32x4 v = {O[aa * 4 + 0][i] * inv, O[aa * 4 + 1][i] * inv, O[aa * 4 + 2][i] * inv, O[aa * 4 + 3][i] * inv};
+      *reinterpret_cast<f32x4*>(dst + 64 * (a0 + aa) + 4 * c) = v;
     }
-    if (c == 0) {
+    if (c == 0 && a0 == 0) {
       const float lse = li[i] > 0.f ? (mi[i] + __log2f(li[i])) * 0.69314718055994531f : -__builtin_inff();
       if (final_out) {
         if (p.lse) p.lse[(int64_t)t * p.H + h] = lse;
@@ -279,8 +291,7 @@ __global__ __launch_bounds__(64 * NW) void mla_kernel(MlaParams p) {
   const bool scale_lane = (FMT == DSA_LAT_FP8) && wave == 0 && q == 0;
   auto load_scale = [&](int id) -> float {
     if (!row_ok(id, p)) return 0.f;
-    const uint8_t* page = p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
-    return *reinterpret_cast<const float*>(page + P * 576 + (id & (P - 1)) * 4);
+    return *reinterpret_cast<const float*>(row_ptr<FMT>(p, id, P).data + LatRow<DSA_LAT_FP8>::kScale);
   };
 
   // queries of head 16*ht + c as B fragments (zero for padded heads)
@@ -345,32 +356,37 @@ __global__ __launch_bounds__(64 * NW) void mla_kernel(MlaParams p) {
       if (scale_lane) sc_next = load_scale(id);
     }
     id_next = load_id(it + 3);
-    mla_tile(p, lat, rsc, rv, qf, O, m, l, g, c);
+    mla_tile<8>(p, lat, rsc, rv, qf, O, m, l, g, c, 0);
   }
 
-  mla_finish(p, O, m, l, t, split, ht, g, c);
+  mla_finish<8>(p, O, m, l, t, split, ht, g, c, 0);
 }
 
 // ---------------------------------------------------------------------------
 // FP8 and NVFP4 latents: gather by direct HBM -> LDS copies.
 //
 // global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS (64
-// lanes = 16 rows x 64 bytes per instruction), so two tiles can be in flight
+// lanes = 16 rows x 64 bytes per instruction), so DP tiles can be in flight
 // behind the one being computed without holding a single register.  The
-// copies are issued from inline assembly and waited for with explicit
-// vmcnt counts: every wave issues the same sequence per tile (one id copy,
-// one side copy -- FP8 row scales or NVFP4 block scales -- and its segment
-// copies), always, even past the end of the list (ids clamped in range, rows
-// on the zero row), so one constant count is exact in every iteration.
+// split's row ids are read into LDS once, up front, so no copy ever waits on
+// an id load.  The copies are issued from inline assembly and waited for with
+// explicit vmcnt counts: every wave issues the same sequence per tile (one
+// side copy -- FP8 row scales or NVFP4 block scales -- and its segment
+// copies), always, even past the end of the list (rows on the zero row), so
+// one constant count is exact in every iteration.
 //
 // Per iteration `it`, for every wave:
-//   wait   copies of tile it (rows, side) and ids of tile it+2 have landed
+//   wait   copies of tile it (rows, side) have landed
 //   A      dequantise this wave's segments of tile it into the bf16 tile
-//   B      copy ids of tile it+3, then side and rows of tile it+2 (into the
-//          ring slots tile it just vacated)
+//   B      copy side and rows of tile it+DP into the ring slot tile it vacated
 //   C      QK / softmax / PV of tile it
-// LDS: bf16 tile [16][kLPad] | raw [2][SEGS][1 KB] | side [2][1 KB] | ids [4][64]
+// LDS: bf16 tile [16][kLPad] | raw [DP][SEGS][1 KB] | side [DP][1 KB] | ids [split_len]
 static __device__ __attribute__((aligned(64))) uint8_t g_zero_row[1280] = {0};
+
+constexpr int kMlaDepth = 2;  // tiles in flight behind the one being computed
+inline size_t mla_dma_lds_bytes(int segs, int depth, int split_len) {
+  return (size_t)kRT * kLPad * 2 + (size_t)depth * (segs * 1024 + 1024) + ((size_t)split_len * 4 + 15) / 16 * 16;
+}
 
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
@@ -390,16 +406,18 @@ template <int FMT> struct DmaGeo;
 template <> struct DmaGeo<DSA_LAT_FP8> { static constexpr int SEGS = 9; };    // 576 B of E4M3
 template <> struct DmaGeo<DSA_LAT_NVFP4> { static constexpr int SEGS = 5; };  // 256 B codes, 64 B rope
 
-template <int FMT, int NW>
+// Workgroup = NW head tiles, one wave each; DP tiles of rows in flight.
+template <int FMT, int NW, int DP>
 __global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
+  constexpr int NA = 8;  // 64-dim value blocks per wave (all 512 dims)
   constexpr int SEGS = DmaGeo<FMT>::SEGS;
   constexpr int SPT = (SEGS + NW - 1) / NW;  // segment copies per wave per tile
   constexpr int kRawBytes = SEGS * 1024;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __bf16* lat = reinterpret_cast<__bf16*>(dsm);
-  uint8_t* raw = dsm + kRT * kLPad * 2;      // [2][SEGS][1024]
-  uint8_t* side = raw + 2 * kRawBytes;       // [2][1024]
-  int* ids = reinterpret_cast<int*>(side + 2 * 1024);  // [4][64]
+  uint8_t* raw = dsm + kRT * kLPad * 2;      // [DP][SEGS][1024]
+  uint8_t* side = raw + DP * kRawBytes;      // [DP][1024]
+  int* ids = reinterpret_cast<int*>(side + DP * 1024);  // [split_len]
   __shared__ float rsc[kRT];
   __shared__ int rv[kRT];
 
@@ -407,6 +425,7 @@ __global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ht = blockIdx.z * NW + wave;
+  constexpr int a0 = 0;
   const int g = lane >> 4, c = lane & 15;
   const int my_row = lane >> 2, q = lane & 3;
   const int j_begin = split * p.split_len;
@@ -414,54 +433,50 @@ __global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
   const int ntile = (j_end - j_begin + kRT - 1) / kRT;
   const int P = 1 << p.plog2;
   const int32_t* rlist = p.rows + (int64_t)t * p.k;
-  const uint32_t raw_l = lds_addr(raw), side_l = lds_addr(side), ids_l = lds_addr(ids);
+  const int n_ids = j_end - j_begin;  // >= 1
+  const uint32_t raw_l = lds_addr(raw), side_l = lds_addr(side);
 
-  // id of row r of tile `tile` (-1 past the split's end), from the id ring
+  // id of row r of tile `tile` (-1 past the split's end)
   auto id_at = [&](int tile, int r) -> int {
-    return j_begin + tile * kRT + r < j_end ? ids[(tile & 3) * 64 + r] : -1;
+    const int j = tile * kRT + r;
+    const int v = ids[min(j, n_ids - 1)];
+    return j < n_ids ? v : -1;
   };
-  auto page_of = [&](int id) -> const uint8_t* {
-    return p.lat + (int64_t)(id >> p.plog2) * p.page_bytes;
-  };
-  // copies of one tile's ids: lane l takes entry l & 15 (clamped in range)
-  auto copy_ids = [&](int tile) {
-    const int j = min(j_begin + tile * kRT + (lane & 15), p.k - 1);
-    dma4(rlist + j, ids_l + (tile & 3) * 256);
+  auto row_of = [&](int id) -> const uint8_t* {
+    return p.lat + (int64_t)(id >> p.plog2) * p.page_bytes + (int64_t)(id & (P - 1)) * LatRow<FMT>::kBytes;
   };
   // side and row copies of one tile into ring slot `slot`
   auto copy_tile = [&](int tile, int slot) {
     if (FMT == DSA_LAT_FP8) {
       // row scale of row lane >> 2 (lanes 4r .. 4r+3 carry row r's)
       const int id = id_at(tile, my_row);
-      const uint8_t* src = row_ok(id, p) ? page_of(id) + P * 576 + (id & (P - 1)) * 4 : g_zero_row;
+      const uint8_t* src = row_ok(id, p) ? row_of(id) + LatRow<FMT>::kScale : g_zero_row;
       dma4(src, side_l + slot * 1024);
     } else {
       // 32 bytes of E4M3 block scales per row: lane l < 32 copies half l & 1
       // of row l >> 1 (lanes 32..63 repeat rows 0..15 into the slot's tail)
       const int r = (lane >> 1) & 15;
       const int id = id_at(tile, r);
-      const uint8_t* src = row_ok(id, p) ? page_of(id) + 256 * P + (id & (P - 1)) * 32 + (lane & 1) * 16 : g_zero_row;
+      const uint8_t* src = row_ok(id, p) ? row_of(id) + LatRow<FMT>::kScales + (lane & 1) * 16 : g_zero_row;
       dma16(src, side_l + slot * 1024);
     }
     const int id = id_at(tile, my_row);
-    const bool ok = row_ok(id, p);
-    const uint8_t* page = ok ? page_of(id) : g_zero_row;
-    const int slot_i = ok ? (id & (P - 1)) : 0;
+    // an absent row reads the zero row (never past its 1280 bytes)
+    const uint8_t* row = row_ok(id, p) ? row_of(id) : g_zero_row;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int sp = min(wave + i * NW, SEGS - 1);
-      const uint8_t* src;
-      if (FMT == DSA_LAT_FP8) {
-        src = ok ? page + slot_i * 576 + sp * 64 + q * 16 : g_zero_row + sp * 64 + q * 16;
-      } else {
-        src = !ok ? g_zero_row + q * 16
-                  : (sp < 4 ? page + slot_i * 256 + sp * 64 + q * 16 : page + 288 * P + slot_i * 64 + q * 16);
-      }
-      dma16(src, raw_l + slot * kRawBytes + sp * 1024);
+      // FP8: 9 segments of 64 codes; NVFP4: 4 segments of codes, then the rope
+      const int off = (FMT == DSA_LAT_NVFP4 && sp == 4) ? LatRow<FMT>::kRope : sp * 64;
+      dma16(row + off + q * 16, raw_l + slot * kRawBytes + sp * 1024);
     }
   };
-  // copies outstanding behind the ids of tile it+2 when tile it is consumed
-  constexpr int kBehind = 1 + SPT;
+  // copies still outstanding (tiles it+1 .. it+DP-1) when tile it is consumed
+  constexpr int kBehind = (DP - 1) * (1 + SPT);
+  static_assert(kBehind < 64, "vmcnt range");
+
+  // the split's row ids, read once (plain loads; waited for by the compiler)
+  for (int j = tid; j < n_ids; j += 64 * NW) ids[j] = rlist[j_begin + j];
 
   bf16x8 qf[18];
   {
@@ -475,26 +490,23 @@ __global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
       for (int kk = 0; kk < 18; ++kk) qf[kk] = bf16x8{};
     }
   }
-  f32x4 O[32];
+  f32x4 O[NA * 4];
 #pragma unroll
-  for (int x = 0; x < 32; ++x) O[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int x = 0; x < NA * 4; ++x) O[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), l = 0.f;
 
   // The query loads must be complete (and known to the compiler to be) before
   // the first copy: the compiler does not see the copies, and a query load
   // still pending at the loop would make it wait for everything in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  // prologue: ids of tiles 0, 1; tile 0; ids of tile 2; tile 1
-  copy_ids(0);
-  copy_ids(1);
-  wait_vmcnt<0>();
-  copy_tile(0, 0);
-  copy_ids(2);
-  copy_tile(1, 1);
+  __syncthreads();                     // ids visible to every wave
+  // prologue: tiles 0 .. DP-1
+#pragma unroll
+  for (int d = 0; d < DP; ++d) copy_tile(d, d);
   __bf16* lrow = lat + my_row * kLPad;
 
   for (int it = 0; it < ntile; ++it) {
-    const int slot = it & 1;
+    const int slot = it % DP;
     wait_vmcnt<kBehind>();
     __syncthreads();  // the previous tile's readers are done with lat/rsc/rv
     // A: this wave's segments of tile `it` -> bf16 tile (all LDS reads are
@@ -538,14 +550,13 @@ __global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
                                     : (ok ? 1.f : 0.f);
     }
     __syncthreads();
-    // B: ids of tile it+3, then tile it+2 into the slot tile it vacated
-    copy_ids(it + 3);
-    copy_tile(it + 2, slot);
+    // B: tile it+DP into the slot tile it vacated
+    copy_tile(it + DP, slot);
     // C
-    mla_tile(p, lat, rsc, rv, qf, O, m, l, g, c);
+    mla_tile<NA>(p, lat, rsc, rv, qf, O, m, l, g, c, a0);
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
-  mla_finish(p, O, m, l, t, split, ht, g, c);
+  mla_finish<NA>(p, O, m, l, t, split, ht, g, c, a0);
 }
 
 // Merge of the split partials of one (row, head): all split LSEs are read in
@@ -586,27 +597,25 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
 }
 
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
-  // at most four head tiles (one wave each) per workgroup; the tiles of a row
-  // are spread evenly over grid.z
-  const int groups = (p.ntiles + 3) / 4;
-  const int nw = (p.ntiles + groups - 1) / groups;
-  dim3 grid(p.nsplit, p.T, groups), block(64 * nw);
+  const MlaShape sh = mla_shape(p.ntiles);
+  dim3 grid(p.nsplit, p.T, sh.groups), block(64 * sh.nw);
 #define DSA_MLA_LAUNCH(F)                                                                   \
-  switch (nw) {                                                                            \
+  switch (sh.nw) {                                                                         \
     case 1: hipLaunchKernelGGL((mla_kernel<F, 1>), grid, block, 0, stream, p); break;      \
     case 2: hipLaunchKernelGGL((mla_kernel<F, 2>), grid, block, 0, stream, p); break;      \
     case 3: hipLaunchKernelGGL((mla_kernel<F, 3>), grid, block, 0, stream, p); break;      \
     default: hipLaunchKernelGGL((mla_kernel<F, 4>), grid, block, 0, stream, p); break;     \
   }
-#define DSA_MLA_DMA_LAUNCH(F)                                                                       \
-  {                                                                                                \
-    const size_t lds = (size_t)kRT * kLPad * 2 + 2 * DmaGeo<F>::SEGS * 1024 + 2 * 1024 + 4 * 256;  \
-    switch (nw) {                                                                                  \
-      case 1: hipLaunchKernelGGL((mla_dma_kernel<F, 1>), grid, block, lds, stream, p); break;      \
-      case 2: hipLaunchKernelGGL((mla_dma_kernel<F, 2>), grid, block, lds, stream, p); break;      \
-      case 3: hipLaunchKernelGGL((mla_dma_kernel<F, 3>), grid, block, lds, stream, p); break;      \
-      default: hipLaunchKernelGGL((mla_dma_kernel<F, 4>), grid, block, lds, stream, p); break;     \
-    }                                                                                              \
+#define DSA_MLA_DMA_LAUNCH(F)                                                                      \
+  {                                                                                               \
+    constexpr int DP = kMlaDepth;                                                                 \
+    const size_t lds = mla_dma_lds_bytes(DmaGeo<F>::SEGS, DP, p.split_len);                       \
+    switch (sh.nw) {                                                                              \
+      case 1: hipLaunchKernelGGL((mla_dma_kernel<F, 1, DP>), grid, block, lds, stream, p); break;  \
+      case 2: hipLaunchKernelGGL((mla_dma_kernel<F, 2, DP>), grid, block, lds, stream, p); break;  \
+      case 3: hipLaunchKernelGGL((mla_dma_kernel<F, 3, DP>), grid, block, lds, stream, p); break;  \
+      default: hipLaunchKernelGGL((mla_dma_kernel<F, 4, DP>), grid, block, lds, stream, p); break; \
+    }                                                                                             \
   }
   switch (p.fmt) {
     case DSA_LAT_BF16: DSA_MLA_LAUNCH(DSA_LAT_BF16) break;

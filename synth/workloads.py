@@ -13,16 +13,21 @@ KV cache, three states"); 12 TP8 heads padded to 16 ("Prefill: shard attention
 by token"; MI355X Kimi K3 page, section 4 "MLA"); speculative verify rows that
 share keys (AMD section "native MXFP4 indexer").
 
-Page layout (structure-of-arrays inside each page of P tokens, every region
-16-byte aligned for P a multiple of 4):
+Page layout.  Index keys are streamed page by page, so their pages are
+structure-of-arrays (every region 16-byte aligned for P a multiple of 4):
 
   key  FP8     [P x 128 E4M3 codes][P x fp32 scale]                 132 B/token
   key  MXFP4   [P x 64 B packed E2M1][P x 4 E8M0 (one per 32)]        68 B/token
-  lat  BF16    [P x 576 bf16]                                       1152 B/token
-  lat  FP8     [P x 576 E4M3 codes][P x fp32 scale]                 580 B/token
-  lat  NVFP4   [P x 256 B packed E2M1 (dims 0..511)]
-               [P x 32 E4M3 block scales (one per 16 dims)]
-               [P x 64 E4M3 rope dims 512..575, unscaled]           352 B/token
+
+Latent rows are gathered one by one, so a latent page is P rows, each padded
+to a whole number of 128-byte lines with all of the row's bytes inside it:
+
+  lat  BF16    row 1152 B: [576 bf16]                               1152 B/token
+  lat  FP8     row  640 B: [576 E4M3 codes][fp32 scale][60 B pad]    580 B/token
+  lat  NVFP4   row  384 B: [256 B packed E2M1 (dims 0..511)]
+                           [32 E4M3 block scales (one per 16 dims)]
+                           [64 E4M3 rope dims 512..575, unscaled]
+                           [32 B pad]                                352 B/token
 
 Keys and latents of a token sit in the pages with the same physical id.
 """
@@ -47,7 +52,8 @@ LAT_BF16, LAT_FP8, LAT_NVFP4 = "bf16", "fp8", "nvfp4"
 Q_BF16, Q_FP8 = "bf16", "fp8"
 
 KEY_TOKEN_BYTES = {KEY_FP8: 132, KEY_MXFP4: 68}
-LAT_TOKEN_BYTES = {LAT_BF16: 1152, LAT_FP8: 580, LAT_NVFP4: 352}
+LAT_TOKEN_BYTES = {LAT_BF16: 1152, LAT_FP8: 580, LAT_NVFP4: 352}   # data bytes per token
+LAT_ROW_STRIDE = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}    # bytes per row in a page
 
 
 def key_regions(fmt: str, P: int):
@@ -59,14 +65,14 @@ def key_regions(fmt: str, P: int):
     raise ValueError(fmt)
 
 
-def lat_regions(fmt: str, P: int):
-    """(codes off, codes B/tok, scales off, scales B/tok, rope off, rope B/tok)."""
+def lat_fields(fmt: str):
+    """Byte offsets inside a latent row: (codes, scales, rope)."""
     if fmt == LAT_BF16:
-        return 0, 1152, 0, 0, 0, 0
+        return 0, None, None
     if fmt == LAT_FP8:
-        return 0, 576, 576 * P, 4, 0, 0
+        return 0, 576, None
     if fmt == LAT_NVFP4:
-        return 0, 256, 256 * P, 32, 288 * P, 64
+        return 0, 256, 288
     raise ValueError(fmt)
 
 
@@ -121,7 +127,7 @@ class Workload:
     tok_vis: torch.Tensor               # int32 [T]
     block_table: Optional[torch.Tensor] # int32 [R, pages_per_req] or None (non-paged)
     key_pool: torch.Tensor              # uint8 [num_pages, P*key_bytes]
-    lat_pool: torch.Tensor              # uint8 [num_pages, P*lat_bytes]
+    lat_pool: torch.Tensor              # uint8 [num_pages, P*lat_row_stride]
     q_idx: torch.Tensor                 # bf16 [T,32,128] or uint8 E4M3 codes
     q_idx_scale: Optional[torch.Tensor] # fp32 [T,32] (FP8 q only)
     w: torch.Tensor                     # fp32 [T,32]
@@ -171,20 +177,22 @@ def _write_lat_rows(pool, fmt, P, phys_pages, vals):
     if n < npg * P:
         vals = torch.cat([vals, vals.new_zeros(npg * P - n, vals.shape[1])])
     vals = vals.reshape(npg, P, D_LAT)
-    c_off, c_b, s_off, s_b, r_off, r_b = lat_regions(fmt, P)
+    stride = LAT_ROW_STRIDE[fmt]
+    c_off, s_off, r_off = lat_fields(fmt)
+    rows = torch.zeros(npg, P, stride, dtype=torch.uint8, device=pool.device)
     if fmt == LAT_BF16:
-        b = codecs.bf16_bits(vals).contiguous().view(torch.uint8)
-        pool[phys_pages, :] = b.reshape(npg, P * 1152)
+        rows[:] = codecs.bf16_bits(vals).contiguous().view(torch.uint8).reshape(npg, P, 1152)
     elif fmt == LAT_FP8:
         codes, scale = codecs.fp8_rowwise(vals)
-        pool[phys_pages, c_off:c_off + P * c_b] = codes.reshape(npg, P * c_b)
-        pool[phys_pages, s_off:s_off + P * s_b] = scale.contiguous().view(torch.uint8).reshape(npg, P * s_b)
+        rows[..., c_off:c_off + 576] = codes
+        rows[..., s_off:s_off + 4] = scale.contiguous().view(torch.uint8).reshape(npg, P, 4)
     else:
         codes, sc = codecs.nvfp4_blocks(vals[..., :D_V], 16)
         rope = codecs.e4m3_encode(vals[..., D_V:])
-        pool[phys_pages, c_off:c_off + P * c_b] = codes.reshape(npg, P * c_b)
-        pool[phys_pages, s_off:s_off + P * s_b] = sc.reshape(npg, P * s_b)
-        pool[phys_pages, r_off:r_off + P * r_b] = rope.reshape(npg, P * r_b)
+        rows[..., c_off:c_off + 256] = codes
+        rows[..., s_off:s_off + 32] = sc
+        rows[..., r_off:r_off + 64] = rope
+    pool[phys_pages, :] = rows.reshape(npg, P * stride)
 
 
 def make_workload(spec: Spec, device="cpu", seed: Optional[int] = None) -> Workload:
@@ -250,7 +258,7 @@ def make_workload(spec: Spec, device="cpu", seed: Optional[int] = None) -> Workl
         hot = torch.sort(torch.cat(hot_rows), dim=1).values
 
     key_pool = torch.zeros(num_pages, P * KEY_TOKEN_BYTES[spec.key_fmt], dtype=torch.uint8, device=device)
-    lat_pool = torch.zeros(num_pages, P * LAT_TOKEN_BYTES[spec.lat_fmt], dtype=torch.uint8, device=device)
+    lat_pool = torch.zeros(num_pages, P * LAT_ROW_STRIDE[spec.lat_fmt], dtype=torch.uint8, device=device)
     phys_d = phys.to(device)
     for r in range(R):
         kv = torch.randn(N, DI, generator=g, device=device)

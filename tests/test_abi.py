@@ -118,7 +118,7 @@ def test_topk_rejects_bad_arguments(mut, status):
 
 
 def _mla_args(**kw):
-    a = dict(num_rows=4, num_heads=12, q=FAKE, latents=_cache(fmt=dsa.LAT_FP8, plog2=6, page_bytes=580 * 64, pages=10),
+    a = dict(num_rows=4, num_heads=12, q=FAKE, latents=_cache(fmt=dsa.LAT_FP8, plog2=6, page_bytes=640 * 64, pages=10),
              rows=FAKE, k=2048, sm_scale=0.07, num_splits=0, out=FAKE, lse=None, workspace=FAKE,
              workspace_bytes=1 << 40)
     a.update(kw)
@@ -133,7 +133,8 @@ def _mla_args(**kw):
     (dict(sm_scale=-1.0), dsa.DSA_ERR_INVALID_ARG),
     (dict(out=FAKE + 4), dsa.DSA_ERR_INVALID_ARG),
     (dict(latents=_cache(fmt=0)), dsa.DSA_ERR_UNSUPPORTED),
-    (dict(latents=_cache(fmt=dsa.LAT_NVFP4, plog2=6, page_bytes=351 * 64)), dsa.DSA_ERR_INVALID_ARG),
+    (dict(latents=_cache(fmt=dsa.LAT_NVFP4, plog2=6, page_bytes=383 * 64)), dsa.DSA_ERR_INVALID_ARG),
+    (dict(latents=_cache(fmt=dsa.LAT_FP8, plog2=6, page_bytes=580 * 64)), dsa.DSA_ERR_INVALID_ARG),
     (dict(workspace=None), dsa.DSA_ERR_WORKSPACE),
     (dict(workspace_bytes=10), dsa.DSA_ERR_WORKSPACE),
 ])

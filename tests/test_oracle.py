@@ -145,13 +145,26 @@ def test_key_decode_closed_form_mxfp4():
 
 def test_lat_decode_closed_form_nvfp4():
     P = 2
-    pool = np.zeros((1, 352 * P), np.uint8)
-    pool[0, 256:512] = 0x1F        # row 1: pairs (6.0? no: low nibble 0xF=-6.0, high 0x1=0.5)
-    pool[0, 256 * P + 32: 256 * P + 64] = 0x40   # row 1 block scales: E4M3 0x40 = 2.0
-    pool[0, 288 * P + 64: 288 * P + 128] = 0xB8  # row 1 rope: -1.0
+    pool = np.zeros((1, 384 * P), np.uint8)
+    pool[0, 384:640] = 0x1F            # row 1 codes: low nibble 0xF = -6.0, high nibble 0x1 = 0.5
+    pool[0, 384 + 256: 384 + 288] = 0x40   # row 1 block scales: E4M3 0x40 = 2.0
+    pool[0, 384 + 288: 384 + 352] = 0xB8   # row 1 rope: E4M3 0xB8 = -1.0
+    pool[0, 384 + 352: 768] = 0x7E         # row 1 padding: never read
     lat = O.lat_rows(pool, "nvfp4", P, np.array([1, 0]))
     assert np.all(lat[0, 0:512:2] == -12.0) and np.all(lat[0, 1:512:2] == 1.0)
     assert np.all(lat[0, 512:] == -1.0) and np.all(lat[1] == 0.0)
+
+
+def test_lat_decode_closed_form_fp8():
+    P = 2
+    pool = np.zeros((1, 640 * P), np.uint8)
+    pool[0, 0:576] = 0x38                  # row 0 codes: E4M3 0x38 = 1.0
+    pool[0, 576:580] = np.frombuffer(np.float32(0.25).tobytes(), np.uint8)
+    pool[0, 580:640] = 0x7E                # row 0 padding: never read
+    pool[0, 640:640 + 576] = 0xC0          # row 1 codes: E4M3 0xC0 = -2.0
+    pool[0, 640 + 576:640 + 580] = np.frombuffer(np.float32(3.0).tobytes(), np.uint8)
+    lat = O.lat_rows(pool, "fp8", P, np.array([1, 0]))
+    assert np.all(lat[0] == -6.0) and np.all(lat[1] == 0.25)
 
 
 # ------------------------------------------------------------------ top-k

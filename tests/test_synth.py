@@ -79,7 +79,7 @@ def test_workload_structure():
     spec = synth.CONFIGS["tp8_spec_decode_64k"].replace(R=3, N=1000)
     wl = synth.make_workload(spec)
     assert wl.T == 18 and wl.P == 64 and wl.num_pages == 3 * 16
-    assert wl.key_pool.shape == (48, 64 * 132) and wl.lat_pool.shape == (48, 64 * 580)
+    assert wl.key_pool.shape == (48, 64 * 132) and wl.lat_pool.shape == (48, 64 * 640)
     assert sorted(wl.block_table.flatten().tolist()) == list(range(48))
     assert wl.tok_vis.tolist() == [995, 996, 997, 998, 999, 1000] * 3
     assert wl.q_mla.shape == (18, 12, 576) and wl.q_mla.dtype == torch.bfloat16
