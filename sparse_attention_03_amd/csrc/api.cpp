@@ -229,8 +229,10 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     // their rows once per workgroup, so fewer, longer workgroups (about 512,
     // two per CU) amortise that.
     int64_t target = (int64_t)b.max_vis * b.num_requests / (b.max_rows_per_req == 1 ? 2048 : 512);
+    const int cap = b.max_rows_per_req > 1 ? 4096
+                    : a->keys.fmt == DSA_KEY_FP8 ? dsa::kIndexerRowChunkFp8 : dsa::kIndexerRowChunkMxfp4;
     int chunk = 256;
-    while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
+    while (chunk < cap && chunk * 2 <= target) chunk *= 2;
     p.chunk = chunk;
     p.qrows = std::min(b.max_rows_per_req, dsa::kIndexerMaxRowsPerPass);
     p.max_rows_per_req = b.max_rows_per_req;

@@ -325,21 +325,56 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   }
 }
 
-// One query row per request (long-context decode): the row's query fragments
-// stay in registers (no LDS traffic), each key tile is dequantised just before
-// its eight MFMAs, and the kernel is small enough for three to four waves per
-// SIMD -- enough HBM requests in flight to stream the keys at full rate.
+// One query row per request (long-context decode).  The keys stream into a
+// private LDS ring per wave by direct HBM -> LDS copies (global_load_lds_
+// dwordx4 with the nontemporal hint): a copy moves 1 KiB -- 8 whole FP8 keys
+// or 16 whole MXFP4 keys -- so every 128-byte line is fetched by exactly one
+// instruction, and the copies are waited for with explicit vmcnt counts,
+// so the compiler never drains the stream.  A round is 64 keys per wave
+// (four 16-key tiles) plus their 64 side words (FP8 scale / MXFP4 E8M0
+// codes); while one round is multiplied the next is in flight.  Inside a
+// tile the 16-byte chunk j of key c sits at position c * NC + (j ^ swz(c))
+// (NC chunks per key), which makes the fragment reads below conflict-free.
+// The row's query fragments stay in registers.
+static __device__ __attribute__((aligned(64))) uint8_t g_idx_zero[64] = {0};
+__device__ __forceinline__ void idx_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void idx_dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void idx_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t idx_lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
+}
+
+template <int KFMT> struct KeyStream {
+  static constexpr int kKeyBytes = KFMT == DSA_KEY_FP8 ? 128 : 64;  // code bytes per key
+  static constexpr int kChunks = kKeyBytes / 16;                     // 16-byte chunks per key
+  static constexpr int kCopies = 64 * kKeyBytes / 1024;              // code copies per round
+  static constexpr int kOps = kCopies + 1;                           // + the side copy
+  static constexpr int kRoundBytes = 64 * kKeyBytes + 256;           // codes, then 64 side words
+  static constexpr int kDepth = 2;                                   // rounds per wave ring
+  static constexpr int kMaxChunk = KFMT == DSA_KEY_FP8 ? kIndexerRowChunkFp8 : kIndexerRowChunkMxfp4;
+  // swizzle of key c's chunks (c = key within its tile)
+  __device__ static int swz(int c) { return KFMT == DSA_KEY_FP8 ? (c >> 1) & 7 : (c >> 2) & 3; }
+  // LDS bytes of one workgroup: 4 rings, the chunk's scores, its page ids
+  static constexpr size_t kLds = 4 * kDepth * kRoundBytes + kMaxChunk * 4 + (kMaxChunk / 16 + 1) * 4;
+};
+
 template <int KFMT>
-__global__ __launch_bounds__(256, 4) void indexer_bf16_row_kernel(IndexerParams p) {
-  __shared__ int pg_lds[kIdxMaxChunkPages];
-  __shared__ uint32_t side[kIdxMaxChunk];
-  // the chunk's scores collect in LDS and leave in one coalesced pass at the
-  // end: the round loop then holds no global store, whose operand registers
-  // the compiler would otherwise wait on before reusing them
-  __shared__ float sc_out[kIdxMaxChunk];
+__global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) {
+  using KS = KeyStream<KFMT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* sc_out = reinterpret_cast<float*>(lds + 4 * KS::kDepth * KS::kRoundBytes);  // [chunk]
+  int* pg_lds = reinterpret_cast<int*>(sc_out + KS::kMaxChunk);                       // [chunk/16 + 1]
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int t = p.req_row_start[r];
   if (p.req_row_start[r + 1] <= t) return;
@@ -349,6 +384,7 @@ __global__ __launch_bounds__(256, 4) void indexer_bf16_row_kernel(IndexerParams 
   const int kend = min(k0 + p.chunk, vis);
   const int P = 1 << p.plog2;
   const int lp0 = k0 >> p.plog2;
+  const int nround = (kend - k0 + kIdxRound - 1) / kIdxRound;
   for (int i = tid; i <= ((kend - 1) >> p.plog2) - lp0; i += 256)
     pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
 
@@ -361,17 +397,65 @@ __global__ __launch_bounds__(256, 4) void indexer_bf16_row_kernel(IndexerParams 
       qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
   const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
   const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
-  __syncthreads();
-  stage_side<KFMT>(p, pg_lds, lp0, k0, kend, P, side);
+  // the query loads must be complete (and known to the compiler to be)
+  // before the first copy: a load still pending at the loop would make the
+  // compiler wait for every copy in flight
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  // two raw buffers: the keys of the next round load while this one computes
-  auto round = [&](int base, const RawKeys<KFMT>& cur) {
+  uint8_t* ring = lds + wave * KS::kDepth * KS::kRoundBytes;
+  const uint32_t ring_l = idx_lds_addr(ring);
+  // Copies of round `it` into ring slot it % kDepth.  Keys past the chunk end
+  // are clamped onto its last key, so every round issues the same copies.
+  auto issue = [&](int it) {
+    const int kb = k0 + it * kIdxRound + wave * 64;  // first key of the wave's share
+    const int own = min(kb + lane, kend - 1);         // this lane's key (clamped)
+    const int pg_own = pg_lds[(own >> p.plog2) - lp0];
+    const uint32_t slot_l = ring_l + (it % KS::kDepth) * KS::kRoundBytes;
+#pragma unroll
+    for (int d = 0; d < KS::kCopies; ++d) {
+      // copy d: tile kt, keys cb .. cb + 1024 / kKeyBytes - 1 of the tile
+      constexpr int kPerCopy = 1024 / KS::kKeyBytes;
+      const int kt = d * kPerCopy / 16, cb = d * kPerCopy % 16;
+      const int cc = cb + lane / KS::kChunks;                 // key within the tile
+      const int j = (lane % KS::kChunks) ^ KS::swz(cc);      // its chunk this lane moves
+      const int pg = __builtin_amdgcn_readlane(pg_own, kt * 16);  // the tile lies in one page
+      const int key = min(kb + kt * 16 + cc, kend - 1);
+      const uint8_t* src = pg >= 0 ? p.keys + (int64_t)pg * p.page_bytes + (key & (P - 1)) * KS::kKeyBytes + j * 16
+                                   : g_idx_zero;
+      idx_dma16(src, slot_l + d * 1024);
+    }
+    const uint8_t* sw = pg_own >= 0 ? p.keys + (int64_t)pg_own * p.page_bytes + P * KS::kKeyBytes + (own & (P - 1)) * 4
+                                    : g_idx_zero;
+    idx_dma4(sw, slot_l + 64 * KS::kKeyBytes);
+  };
+
+#pragma unroll
+  for (int d = 0; d < KS::kDepth; ++d) issue(d);
+  for (int it = 0; it < nround; ++it) {
+    idx_wait_vmcnt<(KS::kDepth - 1) * KS::kOps>();
+    const uint8_t* rd = ring + (it % KS::kDepth) * KS::kRoundBytes;
+    const uint32_t* side = reinterpret_cast<const uint32_t*>(rd + 64 * KS::kKeyBytes);
     float v[kIdxKT];
 #pragma unroll
     for (int kt = 0; kt < kIdxKT; ++kt) {
+      const uint8_t* tile = rd + kt * 16 * KS::kKeyBytes + c * KS::kKeyBytes;
       bf16x8 b[4];
-      dequant_tile<KFMT>(cur, kt, b, side[base - k0 + (wave * kIdxKT + kt) * 16 + c], g);
+      if (KFMT == DSA_KEY_FP8) {
+        const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
+        const i32x4 y = *reinterpret_cast<const i32x4*>(tile + ((4 + g) ^ KS::swz(c)) * 16);
+        b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
+        b[1] = e4m3x8_to_bf16x8(x[2], x[3]);
+        b[2] = e4m3x8_to_bf16x8(y[0], y[1]);
+        b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
+      } else {
+        const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
+        const float sc = e8m0_to_f32((side[kt * 16 + c] >> (8 * g)) & 0xFFu);
+        b[0] = e2m1x8_to_bf16x8(x[0], sc);
+        b[1] = e2m1x8_to_bf16x8(x[1], sc);
+        b[2] = e2m1x8_to_bf16x8(x[2], sc);
+        b[3] = e2m1x8_to_bf16x8(x[3], sc);
+      }
       f32x4 a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -387,30 +471,18 @@ __global__ __launch_bounds__(256, 4) void indexer_bf16_row_kernel(IndexerParams 
       }
       v[kt] = x;
     }
-    const int s_own = base + wave * (kIdxKT * 16) + lane;
-    const float own_mul = own_multiplier<KFMT, true>(cur, g, side, s_own - k0);
+    // lane stores key k0 + it * 256 + wave * 64 + lane: its multiplier is the
+    // FP8 scale (1 for MXFP4) on a present page, -inf otherwise
+    const int s_own = k0 + it * kIdxRound + wave * 64 + lane;
+    const int pg_own = pg_lds[(min(s_own, kend - 1) >> p.plog2) - lp0];
+    const float mul = pg_own < 0 ? -__builtin_inff() : (KFMT == DSA_KEY_FP8 ? __uint_as_float(side[lane]) : 1.f);
     const float tot = rows_reduce_scatter4(v, g);
-    sc_out[s_own - k0] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
-  };
-  // Three raw buffers in rotation: two rounds of keys are in flight while one
-  // computes (the compute is short; keeping HBM busy needs the bytes in
-  // flight).  Loads past the last round re-read the last round (cache hits),
-  // so every step issues the same loads and the waits stay exact.
-  const int last_base = k0 + (kend - 1 - k0) / kIdxRound * kIdxRound;
-  RawKeys<KFMT> ra, rb, rc;
-  load_round<KFMT, true>(p, pg_lds, lp0, k0, kend, wave, g, c, P, ra);
-  load_round<KFMT, true>(p, pg_lds, lp0, min(k0 + kIdxRound, last_base), kend, wave, g, c, P, rb);
-  for (int base = k0; base < kend; base += 3 * kIdxRound) {
-    const int b1 = base + kIdxRound, b2 = base + 2 * kIdxRound;
-    load_round<KFMT, true>(p, pg_lds, lp0, min(b2, last_base), kend, wave, g, c, P, rc);
-    round(base, ra);
-    if (b1 >= kend) break;
-    load_round<KFMT, true>(p, pg_lds, lp0, min(b2 + kIdxRound, last_base), kend, wave, g, c, P, ra);
-    round(b1, rb);
-    if (b2 >= kend) break;
-    load_round<KFMT, true>(p, pg_lds, lp0, min(b2 + 2 * kIdxRound, last_base), kend, wave, g, c, P, rb);
-    round(b2, rc);
+    if (s_own < kend) sc_out[s_own - k0] = mul == -__builtin_inff() ? mul : tot * mul;
+    // the slot is read; refill it with round it + kDepth
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    issue(it + KS::kDepth);
   }
+  idx_wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
   __syncthreads();
   float* out = p.scores + (int64_t)t * p.ld;
   for (int i = tid; i < kend - k0; i += 256) out[k0 + i] = sc_out[i];
@@ -420,10 +492,15 @@ dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
   dim3 grid((p.max_vis + p.chunk - 1) / p.chunk, p.R);
   const size_t lds = (size_t)p.qrows * 32 * (kQPad * sizeof(__bf16) + sizeof(float));
   if (p.max_rows_per_req == 1) {
-    if (p.key_fmt == DSA_KEY_FP8)
-      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_FP8>, grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_MXFP4>, grid, dim3(256), 0, stream, p);
+    if (p.key_fmt == DSA_KEY_FP8) {
+      // above the default 64 KiB of dynamic LDS (idempotent, host-side)
+      hipFuncSetAttribute(reinterpret_cast<const void*>(indexer_bf16_row_kernel<DSA_KEY_FP8>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)KeyStream<DSA_KEY_FP8>::kLds);
+      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_FP8>, grid, dim3(256), KeyStream<DSA_KEY_FP8>::kLds, stream, p);
+    } else {
+      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_MXFP4>, grid, dim3(256), KeyStream<DSA_KEY_MXFP4>::kLds,
+                         stream, p);
+    }
   } else if (p.key_fmt == DSA_KEY_FP8) {
     hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_FP8>, grid, dim3(256), lds, stream, p);
   } else {

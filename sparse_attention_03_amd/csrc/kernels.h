@@ -10,6 +10,10 @@ namespace dsa {
 
 // Query rows of a request the BF16 indexer stages in LDS per pass.
 constexpr int kIndexerMaxRowsPerPass = 6;
+// Keys per workgroup of the single-row BF16 indexer (its LDS holds the
+// chunk's scores): FP8 keys, MXFP4 keys.
+constexpr int kIndexerRowChunkFp8 = 2048;
+constexpr int kIndexerRowChunkMxfp4 = 4096;
 
 struct IndexerParams {
   int R, T;
