@@ -376,40 +376,29 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int t = p.req_row_start[r];
-  if (p.req_row_start[r + 1] <= t) return;
-  const int vis = min(p.tok_vis[t], p.max_vis);
   const int k0 = blockIdx.x * p.chunk;
-  if (k0 >= vis) return;
-  const int kend = min(k0 + p.chunk, vis);
+  const int kcap = min(k0 + p.chunk, p.max_vis);  // chunk end before the row's visible count is known
   const int P = 1 << p.plog2;
   const int lp0 = k0 >> p.plog2;
-  const int nround = (kend - k0 + kIdxRound - 1) / kIdxRound;
-  for (int i = tid; i <= ((kend - 1) >> p.plog2) - lp0; i += 256)
+  // Prologue, shortest dependency chain first: the chunk's page ids and the
+  // row index do not depend on each other; the first copies go out as soon
+  // as the page ids are in LDS, before the row's visible count and query
+  // arrive (keys past the visible count are read but never stored).
+  for (int i = tid; i <= ((kcap - 1) >> p.plog2) - lp0; i += 256)
     pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
-
-  bf16x8 qa[2][4];
-  const __bf16* qrow = p.q + (int64_t)t * 32 * 128;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
-  const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
-  const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
-  // the query loads must be complete (and known to the compiler to be)
-  // before the first copy: a load still pending at the loop would make the
-  // compiler wait for every copy in flight
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // (loaded values are uniform; saying so keeps the round bookkeeping scalar)
+  const int t = __builtin_amdgcn_readfirstlane(p.req_row_start[r]);
+  const int t_end = __builtin_amdgcn_readfirstlane(p.req_row_start[r + 1]);
   __syncthreads();
+  if (t_end <= t) return;
 
   uint8_t* ring = lds + wave * KS::kDepth * KS::kRoundBytes;
   const uint32_t ring_l = idx_lds_addr(ring);
-  // Copies of round `it` into ring slot it % kDepth.  Keys past the chunk end
-  // are clamped onto its last key, so every round issues the same copies.
-  auto issue = [&](int it) {
+  // Copies of round `it` into ring slot it % kDepth.  Keys at or past `kc`
+  // are clamped onto key kc - 1, so every round issues the same copies.
+  auto issue = [&](int it, int kc) {
     const int kb = k0 + it * kIdxRound + wave * 64;  // first key of the wave's share
-    const int own = min(kb + lane, kend - 1);         // this lane's key (clamped)
+    const int own = min(kb + lane, kc - 1);           // this lane's key (clamped)
     const int pg_own = pg_lds[(own >> p.plog2) - lp0];
     const uint32_t slot_l = ring_l + (it % KS::kDepth) * KS::kRoundBytes;
 #pragma unroll
@@ -420,7 +409,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
       const int cc = cb + lane / KS::kChunks;                 // key within the tile
       const int j = (lane % KS::kChunks) ^ KS::swz(cc);      // its chunk this lane moves
       const int pg = __builtin_amdgcn_readlane(pg_own, kt * 16);  // the tile lies in one page
-      const int key = min(kb + kt * 16 + cc, kend - 1);
+      const int key = min(kb + kt * 16 + cc, kc - 1);
       const uint8_t* src = pg >= 0 ? p.keys + (int64_t)pg * p.page_bytes + (key & (P - 1)) * KS::kKeyBytes + j * 16
                                    : g_idx_zero;
       idx_dma16(src, slot_l + d * 1024);
@@ -429,11 +418,40 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
                                     : g_idx_zero;
     idx_dma4(sw, slot_l + 64 * KS::kKeyBytes);
   };
+  // rounds the chunk can have before its visible count is known
+  const int nround_cap = (kcap - k0 + kIdxRound - 1) / kIdxRound;
+  const int nfirst = min(KS::kDepth, nround_cap);
+  for (int d = 0; d < nfirst; ++d) issue(d, kcap);
+  int issued = nfirst;  // rounds issued so far (round i uses ring slot i % kDepth)
 
+  // the row's visible count, query fragments and head weights
+  const int vis = __builtin_amdgcn_readfirstlane(min(p.tok_vis[t], p.max_vis));
+  bf16x8 qa[2][4];
+  const __bf16* qrow = p.q + (int64_t)t * 32 * 128;
 #pragma unroll
-  for (int d = 0; d < KS::kDepth; ++d) issue(d);
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
+  // These loads must be complete, and known to the compiler to be, before the
+  // loop: one still pending there would make the compiler wait for every copy
+  // in flight on every round.  (This wait also covers the first copies.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (k0 >= vis) return;                // nothing in flight
+  const int kend = min(kcap, vis);
+  const int nround = (kend - k0 + kIdxRound - 1) / kIdxRound;
+
+  static_assert(KS::kDepth >= 2 && KS::kDepth <= 4, "wait counts for 1 .. 3 rounds behind");
   for (int it = 0; it < nround; ++it) {
-    idx_wait_vmcnt<(KS::kDepth - 1) * KS::kOps>();
+    // rounds it+1 .. issued-1 are the copies issued after round it's
+    switch (issued - 1 - it) {
+      case 0: idx_wait_vmcnt<0>(); break;
+      case 1: idx_wait_vmcnt<KS::kOps>(); break;
+      case 2: idx_wait_vmcnt<2 * KS::kOps>(); break;
+      default: idx_wait_vmcnt<3 * KS::kOps>(); break;
+    }
     const uint8_t* rd = ring + (it % KS::kDepth) * KS::kRoundBytes;
     const uint32_t* side = reinterpret_cast<const uint32_t*>(rd + 64 * KS::kKeyBytes);
     float v[kIdxKT];
@@ -478,9 +496,12 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
     const float mul = pg_own < 0 ? -__builtin_inff() : (KFMT == DSA_KEY_FP8 ? __uint_as_float(side[lane]) : 1.f);
     const float tot = rows_reduce_scatter4(v, g);
     if (s_own < kend) sc_out[s_own - k0] = mul == -__builtin_inff() ? mul : tot * mul;
-    // the slot is read; refill it with round it + kDepth
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    issue(it + KS::kDepth);
+    // the slot is read; refill it with the next round (if the chunk has one)
+    if (issued < nround) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      issue(issued, kend);
+      ++issued;
+    }
   }
   idx_wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
   __syncthreads();
