@@ -64,7 +64,7 @@ dsa_status check_batch(const dsa_batch& b, int plog2, bool need_meta) {
 // ---- top-k plan
 struct TopkPlan {
   int cand_cap, slice, nslices;
-  size_t off_ctr, off_cand, total;
+  size_t off_ctr, off_cand, off_info, total;
 };
 TopkPlan plan_topk(int T, int max_vis, int k) {
   (void)k;
@@ -77,6 +77,8 @@ TopkPlan plan_topk(int T, int max_vis, int k) {
   off = align_up(off + (size_t)T * 16, 256);
   pl.off_cand = off;
   off = align_up(off + (size_t)T * pl.cand_cap * 8, 256);
+  pl.off_info = off;
+  off = align_up(off + (size_t)T * pl.nslices * 8, 256);
   pl.total = off;
   return pl;
 }
@@ -291,6 +293,7 @@ dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   char* ws = static_cast<char*>(a->workspace);
   p.ctr = reinterpret_cast<uint32_t*>(ws + pl.off_ctr);
   p.cand = reinterpret_cast<uint32_t*>(ws + pl.off_cand);
+  p.slice_info = reinterpret_cast<uint32_t*>(ws + pl.off_info);
   p.cand_cap = pl.cand_cap;
   p.slice = pl.slice;
   p.nslices = pl.nslices;

@@ -62,6 +62,7 @@ struct TopkParams {
   // workspace
   uint32_t* ctr;        // [T][4]: candidates appended, -, threshold key, -
   uint32_t* cand;       // [T][cand_cap][2]: order key, index
+  uint32_t* slice_info; // [T][nslices][2]: buffer position and count of each slice's candidates
   int cand_cap;
   int slice;            // scores per workgroup in the filter pass
   int nslices;

@@ -15,13 +15,14 @@
 //      K-th largest key when the whole row is the sample).  So with
 //      overwhelming probability at least K and not many more than K scores
 //      of the row are >= tau.
-//   2. filter: the row is cut into slices; every slice gathers its keys >=
-//      tau in LDS and appends them to the row's candidate buffer behind one
-//      global atomic.
-//   3. finalize: one workgroup per row runs an exact radix select (12-bit
-//      digits) over the candidates' 64-bit composites (key, inverted index)
-//      -- ties go to the lower index -- then ranks the K winners by index
-//      through an LDS bitmap and writes indices and physical rows.
+//   2. filter: the row is cut into slices; every slice appends its keys >=
+//      tau, in index order, to the row's candidate buffer as one block behind
+//      one global atomic, and records where the block went.
+//   3. finalize: one workgroup per row puts the candidates in index order
+//      (blocks by slice), runs an exact radix select (12-bit digits) over
+//      their 64-bit composites (key, inverted index) -- ties go to the lower
+//      index -- and a stable compaction of the winners is the ordered result;
+//      it writes indices and physical rows.
 // The estimate only decides speed: when fewer than K or more than the
 // buffer's capacity of candidates arrived, finalize selects from the whole
 // score row instead (same result).
@@ -33,7 +34,6 @@ namespace dsa {
 constexpr int kExactMax = 8192;     // rows up to this length are sampled completely
 constexpr int kMaxSamples = 16384;  // 16 per thread of the threshold workgroup
 constexpr int kRun = 16;            // consecutive scores per sampled block
-constexpr int kFilterCap = 4096;    // candidates a filter workgroup gathers in LDS
 
 __device__ __forceinline__ int row_vis(const TopkParams& p, int t) {
   return min(max(p.tok_vis[t], 0), p.max_vis);
@@ -194,20 +194,48 @@ __global__ __launch_bounds__(1024) void topk_threshold_kernel(TopkParams p) {
   }
 }
 
-// Keys >= tau are gathered in LDS, then copied out behind one global atomic.
+// Keys >= tau of one slice, in index order: thread tid holds scores
+// 4*tid + 1024*b + e (stripe b < 8, e < 4), so (b, tid, e) order is index
+// order.  A block scan of the per-stripe counts (four 16-bit fields per
+// 64-bit word, two words) gives every candidate its place; the slice's
+// candidates go out as one contiguous block behind one global atomic, and
+// the block's (base, count) is recorded for the finalize.
+__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* wsum, uint64_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t inc = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint64_t before = 0;
+  total = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) before += wsum[w];
+    total += wsum[w];
+  }
+  return before + inc - v;
+}
+
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
-  __shared__ uint32_t l_ck[kFilterCap];
-  __shared__ int l_ci[kFilterCap];
-  __shared__ int n_cand, n_cand2;
-  __shared__ uint32_t base_cand;
+  __shared__ uint64_t wsum[2][4];
+  __shared__ uint32_t s_base;
   const int t = blockIdx.y;
   const int tid = threadIdx.x;
   const int vis = row_vis(p, t);
   if (vis <= p.k) return;
   const int s_begin = blockIdx.x * p.slice;
-  if (s_begin >= vis) return;
-  const int s_end = min(s_begin + p.slice, vis);
   uint32_t* ctr = p.ctr + (int64_t)t * 4;
+  uint32_t* info = p.slice_info + ((int64_t)t * p.nslices + blockIdx.x) * 2;
+  if (s_begin >= vis) {
+    if (tid == 0) {
+      info[0] = 0;
+      info[1] = 0;
+    }
+    return;
+  }
+  const int s_end = min(s_begin + p.slice, vis);
   const float* row = p.scores + (int64_t)t * p.ld;
   // the whole slice (8 float4 per thread) is loaded before any is compared
   f32x4 v[8];
@@ -219,50 +247,50 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
       for (int e = 0; e < 4; ++e) v[b][e] = (s + e < s_end) ? row[s + e] : 0.f;
   }
   const uint32_t tau = ctr[2];
-  if (tid == 0) {
-    n_cand = 0;
-    n_cand2 = 0;
-  }
-  __syncthreads();
+  uint32_t hit[8];  // bit e of hit[b]: score 4*tid + 1024*b + e is a candidate
+  uint64_t pk[2] = {0, 0};
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    const int s = s_begin + 4 * tid + 1024 * b;
+    uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (s + e >= s_end) break;
-      const uint32_t key = order_key(v[b][e]);
-      if (key >= tau) {
-        const int pos = atomicAdd(&n_cand, 1);
-        if (pos < kFilterCap) {
-          l_ck[pos] = key;
-          l_ci[pos] = s + e;
-        }
-      }
+      const int s = s_begin + 4 * tid + 1024 * b + e;
+      if (s < s_end && order_key(v[b][e]) >= tau) m |= 1u << e;
     }
+    hit[b] = m;
+    pk[b >> 2] |= (uint64_t)__popc(m) << (16 * (b & 3));
+  }
+  uint64_t tot0, tot1;
+  const uint64_t ex0 = block_excl_scan_u64(pk[0], wsum[0], tot0);
+  const uint64_t ex1 = block_excl_scan_u64(pk[1], wsum[1], tot1);
+  // stripe totals -> stripe offsets
+  uint32_t off[8], n = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    off[b] = n;
+    n += (uint32_t)(((b < 4 ? tot0 : tot1) >> (16 * (b & 3))) & 0xFFFFu);
+  }
+  if (tid == 0) {
+    const uint32_t base = atomicAdd(&ctr[0], n);
+    s_base = base;
+    info[0] = base;
+    info[1] = n;
   }
   __syncthreads();
-  if (tid == 0) base_cand = atomicAdd(&ctr[0], (uint32_t)n_cand);
-  __syncthreads();
+  const uint32_t base = s_base;
   uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
-  const int nc = n_cand;
-  if (nc <= kFilterCap) {
-    for (int i = tid; i < nc; i += 256) {
-      const uint32_t pos = base_cand + i;
-      if (pos < (uint32_t)p.cand_cap) {
-        candrow[2 * pos] = l_ck[i];
-        candrow[2 * pos + 1] = (uint32_t)l_ci[i];
-      }
-    }
-  } else {
-    // more candidates than LDS holds: write them straight from a rescan
-    for (int s = s_begin + tid; s < s_end; s += 256) {
-      const uint32_t key = order_key(row[s]);
-      if (key >= tau) {
-        const uint32_t pos = base_cand + (uint32_t)atomicAdd(&n_cand2, 1);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    uint32_t pos = base + off[b] + (uint32_t)(((b < 4 ? ex0 : ex1) >> (16 * (b & 3))) & 0xFFFFu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (hit[b] >> e & 1u) {
         if (pos < (uint32_t)p.cand_cap) {
-          candrow[2 * pos] = key;
+          const int s = s_begin + 4 * tid + 1024 * b + e;
+          candrow[2 * pos] = order_key(v[b][e]);
           candrow[2 * pos + 1] = (uint32_t)s;
         }
+        ++pos;
       }
     }
   }
@@ -455,14 +483,48 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   const int ncand = (int)ctr[0];
   const uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
   const float* srow = p.scores + (int64_t)t * p.ld;
-  // candidates in LDS, or (estimate missed) the whole score row
+  // candidates in LDS in index order, or (estimate missed) the whole score row
   const bool from_row = ncand < K || ncand > p.cand_cap;
   const int nsrc = from_row ? vis : ncand;
-  if (!from_row)
+  // rows of up to 1024 slices (8M scores) get their candidates in index order
+  const bool ordered = !from_row && p.nslices <= 1024;
+  if (!from_row && !ordered)
     for (int i = tid; i < ncand; i += blockDim.x) {
       ck[i] = candrow[2 * i];
       ci[i] = candrow[2 * i + 1];
     }
+  if (ordered) {
+    // Every slice's block is contiguous and in index order; blocks lie in
+    // arrival order.  A candidate at buffer position i of slice s goes to
+    // off[s] + (i - base[s]), off = exclusive prefix of the slices' counts.
+    uint32_t* sbase = reinterpret_cast<uint32_t*>(tpre);          // [nslices <= 1024]
+    uint32_t* soff = reinterpret_cast<uint32_t*>(ord);            // [nslices <= 2048]
+    const uint32_t* info = p.slice_info + (int64_t)t * p.nslices * 2;
+    uint32_t cnt = 0;
+    if (tid < p.nslices) {
+      sbase[tid] = info[2 * tid];
+      cnt = info[2 * tid + 1];
+    }
+    int inc = (int)cnt;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(inc, o);
+      if (lane >= o) inc += x;
+    }
+    if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += (int)sl.wtot[w];
+    if (tid < p.nslices) soff[tid] = (uint32_t)(before + inc) - cnt;
+    __syncthreads();
+    for (int i = tid; i < ncand; i += blockDim.x) {
+      const uint32_t key = candrow[2 * i], ix = candrow[2 * i + 1];
+      const int sl_id = (int)ix / p.slice;
+      const uint32_t dst = soff[sl_id] + (uint32_t)i - sbase[sl_id];
+      ck[dst] = key;
+      ci[dst] = ix;
+    }
+  }
   __syncthreads();
   auto each = [&](auto f) {
     for (int i = tid; i < nsrc; i += 1024)
@@ -471,6 +533,39 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   int hi_sh;
   uint64_t prefix;
   select_top(each, (uint32_t)K, sl, hi_sh, prefix);
+  if (ordered) {
+    // the candidates are in index order: a stable compaction of the winners
+    // (thread tid owns candidates 8*tid .. 8*tid+7) is the ordered result
+    constexpr int kPer = kTopkFinalCap / 1024;
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = kPer * tid + u;
+      if (i < ncand && (composite(ck[i], ci[i]) >> hi_sh) >= prefix) m |= 1u << u;
+    }
+    int inc = __popc(m);
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(inc, o);
+      if (lane >= o) inc += x;
+    }
+    __syncthreads();  // sl.wtot was read by select_top
+    if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
+    __syncthreads();
+    int pos = inc - __popc(m);
+    for (int w = 0; w < wave; ++w) pos += (int)sl.wtot[w];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (m >> u & 1u) ord[pos++] = (int)ci[kPer * tid + u];
+    __syncthreads();
+    for (int j = tid; j < p.k; j += 1024) {
+      const int li = j < K ? ord[j] : -1;
+      idx[j] = li;
+      if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+    }
+    if (p.count && tid == 0) p.count[t] = K;
+    return;
+  }
   if (tid == 0) sl.cnt = 0;
   __syncthreads();
   each([&](uint64_t v) {
