@@ -35,9 +35,9 @@
 //            rescaled rarely instead of on almost every tile.
 //   PV       O[heads x 512] += P[heads x 16 rows] . V[16 rows x 512] on
 //            v_mfma_f32_16x16x16_bf16: the V operand needs 4 rows of one
-//            column per lane, read as 4x4 bf16 blocks (ds_read_b64) and
-//            transposed with v_perm_b32.  Lane (g, c) accumulates heads 4g+i
-//            at dims 64a + 4c + u.
+//            column per lane, which one transposing LDS read
+//            (ds_read_b64_tr_b16) delivers per MFMA.  Lane (g, c)
+//            accumulates heads 4g+i at dims 64a + 16u + c.
 #include "common.h"
 #include "kernels.h"
 
@@ -208,20 +208,22 @@ __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, 
       for (int i = 0; i < 4; ++i) O[x][i] *= ai[i];
   }
 
-  // ---- PV: O[heads 4g+i][dims 64a + 4c + u] += P . V over the 16 rows
+  // ---- PV: O[heads 4g+i][dims 64a + 16u + c] += P . V over the 16 rows.
+  // The V operand (rows 4g..4g+3 of one dim per lane) comes from one
+  // transposing LDS read per MFMA: lane s of lane group g points at dims
+  // d0 + 4(s%4) .. +3 of row 4g + s/4, and ds_read_b64_tr_b16 hands lane c
+  // element c%4 of the 8 bytes of lanes 4k + c/4 (k < 4) -- dim d0 + c of
+  // rows 4g .. 4g+3.
+  const __bf16* vsrc = lat + (4 * g + (c >> 2)) * kLPad + 4 * (c & 3);
 #pragma unroll
   for (int aa = 0; aa < NA; ++aa) {
     const int a = a0 + aa;
-    i32x2 vb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vb[j] = *reinterpret_cast<const i32x2*>(&lat[(4 * g + j) * kLPad + 64 * a + 4 * c]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int half = u >> 1;
-      const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-      const i32x2 f = {(int)__builtin_amdgcn_perm((uint32_t)vb[1][half], (uint32_t)vb[0][half], sel),
-                       (int)__builtin_amdgcn_perm((uint32_t)vb[3][half], (uint32_t)vb[2][half], sel)};
-      O[aa * 4 + u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, f), O[aa * 4 + u]);
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const auto* src = (const __attribute__((address_space(3))) s16x4*)(const void*)(vsrc + 64 * a + 16 * u);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<__attribute__((address_space(3))) s16x4*>(src));
+      O[aa * 4 + u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, vb), O[aa * 4 + u]);
     }
   }
 }
@@ -247,10 +249,9 @@ __device__ __forceinline__ void mla_finish(const MlaParams& p, const f32x4 (&O)[
     float* dst = final_out ? p.out + ((int64_t)t * p.H + h) * 512
                            : p.part_o + (((int64_t)t * p.nsplit + split) * p.H + h) * 512;
 #pragma unroll
-    for (int aa = 0; aa < NA; ++aa) {
-      f32x4 v = {O[aa * 4 + 0][i] * inv, O[aa * 4 + 1][i] * inv, O[aa * 4 + 2][i] * inv, O[aa * 4 + 3][i] * inv};
-      *reinterpret_cast<f32x4*>(dst + 64 * (a0 + aa) + 4 * c) = v;
-    }
+    for (int aa = 0; aa < NA; ++aa)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dst[64 * (a0 + aa) + 16 * u + c] = O[aa * 4 + u][i] * inv;
     if (c == 0 && a0 == 0) {
       const float lse = li[i] > 0.f ? (mi[i] + __log2f(li[i])) * 0.69314718055994531f : -__builtin_inff();
       if (final_out) {

@@ -497,12 +497,20 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
     // Every slice's block is contiguous and in index order; blocks lie in
     // arrival order.  A candidate at buffer position i of slice s goes to
     // off[s] + (i - base[s]), off = exclusive prefix of the slices' counts.
+    // The candidate loads are issued together with the slice table's.
+    constexpr int kPer = kTopkFinalCap / 1024;
+    uint2 cv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + 1024 * u;
+      if (i < ncand) cv[u] = reinterpret_cast<const uint2*>(candrow)[i];
+    }
     uint32_t* sbase = reinterpret_cast<uint32_t*>(tpre);          // [nslices <= 1024]
     uint32_t* soff = reinterpret_cast<uint32_t*>(ord);            // [nslices <= 2048]
     const uint32_t* info = p.slice_info + (int64_t)t * p.nslices * 2;
-    uint32_t cnt = 0;
+    uint32_t cnt = 0, sb = 0;
     if (tid < p.nslices) {
-      sbase[tid] = info[2 * tid];
+      sb = info[2 * tid];
       cnt = info[2 * tid + 1];
     }
     int inc = (int)cnt;
@@ -515,14 +523,20 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wave; ++w) before += (int)sl.wtot[w];
-    if (tid < p.nslices) soff[tid] = (uint32_t)(before + inc) - cnt;
+    if (tid < p.nslices) {
+      sbase[tid] = sb;
+      soff[tid] = (uint32_t)(before + inc) - cnt;
+    }
     __syncthreads();
-    for (int i = tid; i < ncand; i += blockDim.x) {
-      const uint32_t key = candrow[2 * i], ix = candrow[2 * i + 1];
-      const int sl_id = (int)ix / p.slice;
-      const uint32_t dst = soff[sl_id] + (uint32_t)i - sbase[sl_id];
-      ck[dst] = key;
-      ci[dst] = ix;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + 1024 * u;
+      if (i < ncand) {
+        const int sl_id = (int)cv[u].y / p.slice;
+        const uint32_t dst = soff[sl_id] + (uint32_t)i - sbase[sl_id];
+        ck[dst] = cv[u].x;
+        ci[dst] = cv[u].y;
+      }
     }
   }
   __syncthreads();
