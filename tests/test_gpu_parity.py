@@ -12,6 +12,7 @@ Tolerances:
   * attention: max-abs-err <= 1e-2 * max|oracle o| (BF16/FP8 latents), 3e-2 (FP4);
     lse within 1e-3 absolute.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -285,6 +286,48 @@ def test_determinism_and_batch_invariance(gpu):
     for j in range(6):
         v = int(one.tok_vis[j])
         assert torch.equal(s1.scores[j, :v], step.scores[2 * 6 + j, :v])
+
+
+# ----------------------------------------------------------------- indexer: rows per request
+def _keep_last_rows(wl, counts):
+    """The workload restricted to the last counts[r] query rows of each
+    request (their causal visible counts unchanged), as a ragged batch."""
+    q = wl.spec.q_per_req
+    sel = torch.cat([torch.arange(r * q + q - n, r * q + q) for r, n in enumerate(counts)]).to(wl.tok_vis.device)
+    starts = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=wl.tok_vis.device)
+    pick = lambda x: None if x is None else x.index_select(0, sel).contiguous()
+    return dataclasses.replace(wl, req_token_start=starts, tok_req=pick(wl.tok_req), tok_vis=pick(wl.tok_vis),
+                               q_idx=pick(wl.q_idx), q_idx_scale=pick(wl.q_idx_scale), w=pick(wl.w),
+                               q_mla=pick(wl.q_mla), hot=pick(wl.hot), spec=wl.spec.replace(q_per_req=max(counts)))
+
+
+@pytest.mark.parametrize("key_fmt,counts,N", [
+    # two passes (9 rows = 6 + 3), one row, odd halves; chunks of 1024 keys
+    # (several ring rounds per workgroup) with a ragged last chunk
+    ("fp8", [1, 9, 5, 4], 140001),
+    ("mxfp4", [6, 3, 2, 7], 140001),
+    # short context: one round per workgroup, a ragged last page
+    ("mxfp4", [6, 1], 1000),
+])
+def test_indexer_rows_per_request(key_fmt, counts, N, gpu):
+    print(f"[gpu] indexer rows {key_fmt} {counts} N={N}", flush=True)
+    spec = synth.CONFIGS["tp8_spec_decode_64k"].replace(R=len(counts), q_per_req=max(counts), N=N,
+                                                          key_fmt=key_fmt, seed=50 + N % 7)
+    wl = _keep_last_rows(synth.make_workload(spec, device=gpu), counts)
+    step = gpu_step(wl)
+    step.indexer()
+    torch.cuda.synchronize()
+    inp = oracle_inputs(wl)
+    rts = inp["req_token_start"]
+    sc = step.scores.cpu().numpy()
+    for r in range(len(counts)):
+        nmax = int(inp["tok_vis"][rts[r]:rts[r + 1]].max())
+        keys = O.request_keys(inp["key_pool"], key_fmt, wl.P, inp["block_table"], r, nmax)
+        for t in range(rts[r], rts[r + 1]):
+            n = int(inp["tok_vis"][t])
+            ref = O.indexer_scores(O.dequant_q_idx(inp, t), inp["w"][t], keys[:n])
+            err = np.abs(sc[t, :n].astype(np.float64) - ref).max()
+            assert err <= 1e-5 * np.abs(ref).max(), f"request {r} row {t}: score err {err}"
 
 
 # ----------------------------------------------------------------- FP8 queries / prefill
