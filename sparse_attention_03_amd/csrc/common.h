@@ -164,6 +164,17 @@ __device__ __forceinline__ f32pair swap_halves32(float x, float y) {
   return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
+// The value of lane l ^ 16 (xor16) or l ^ 32 (xor32), by lane swaps instead
+// of an LDS permute (g = l >> 4).
+__device__ __forceinline__ float xor16(float x, int g) {
+  const f32pair r = swap_rows16(x, x);  // odd rows get their even neighbour, and back
+  return (g & 1) ? r.x : r.y;
+}
+__device__ __forceinline__ float xor32(float x, int g) {
+  const f32pair r = swap_halves32(x, x);  // r.x: lower half twice, r.y: upper half twice
+  return (g >> 1) ? r.x : r.y;
+}
+
 // Reduce-scatter over the four 16-lane rows: lane (g, c) holds v[0..3]; on
 // return it holds sum over g' of v_{g'}[g] (its own row's share of the sum).
 __device__ __forceinline__ float rows_reduce_scatter4(const float (&v)[4], int g) {

@@ -154,15 +154,22 @@ template <int NA>
 __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, const float* rsc, const int* rv,
                                          const bf16x8 (&qf)[18], f32x4 (&O)[NA * 4], float& m, float& l, int g, int c,
                                          int a0) {
-  // ---- QK: S^T tile, rows 4g + i of head c
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  // ---- QK: S^T tile, rows 4g + i of head c.  All 18 fragments are read
+  // before the first multiply, and the k-steps alternate between two
+  // accumulators (two independent chains of nine).
+  f32x4 s;
   {
     const __bf16* lrow = &lat[c * kLPad];
+    bf16x8 af[18];
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lrow + dim_of(kk, g));
-      s = mfma16x16x32(a, qf[kk], s);
+    for (int kk = 0; kk < 18; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(lrow + dim_of(kk, g));
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 18; kk += 2) {
+      s0 = mfma16x16x32(af[kk], qf[kk], s0);
+      s1 = mfma16x16x32(af[kk + 1], qf[kk + 1], s1);
     }
+    s = s0 + s1;
   }
   // ---- online softmax for head c
   float lg[4], rs[4];
@@ -176,8 +183,8 @@ __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, 
     lg[i] = v;
     tmax = fmaxf(tmax, v);
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = fmaxf(tmax, xor16(tmax, g));
+  tmax = fmaxf(tmax, xor32(tmax, g));
   // lazy rescaling: keep a stale max while the tile stays within 2^8 of it
   // (weights stay <= 256); both O and l use the same max, so the final
   // normalisation is exact
@@ -191,7 +198,8 @@ __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, 
     psum += e;
     pw[x] = e * rs[x];  // FP8 row scale enters the value product here
   }
-  psum = wave_sum_xor_16_32(psum);
+  psum += xor16(psum, g);
+  psum += xor32(psum, g);
   l = l * alpha + psum;
   m = mnew;
   const i32x2 pa2 = {(int)pack_bf16x2(pw[0], pw[1]), (int)pack_bf16x2(pw[2], pw[3])};
