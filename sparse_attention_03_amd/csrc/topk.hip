@@ -592,28 +592,167 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   order_and_store(p, out, K, vis, fsm, 2 * kTopkFinalCap, ord, tpre, sl.wtot, t, r, idx, rows);
 }
 
-// Short rows: one workgroup per row does everything with the row held in
-// registers (up to 64 scores per thread, one read of the row, no workspace,
-// one launch): a threshold from every 16th group of four scores (or from all
-// of a row up to kExactMax), candidates compacted into LDS by a block prefix
-// sum, the exact select over them (over the row re-read from memory when the
-// estimate missed), the sort and the stores.  Used when no row is longer
-// than kFusedMax: a CU streams far less than its share of HBM bandwidth
-// alone, so long rows are spread over many workgroups (threshold / filter /
-// finalize) instead.
-constexpr int kFusedMax = 8192;
-constexpr int kFusedCap = 4096;
+// Rows up to kRowMax scores: one workgroup per row does everything with the
+// row held in registers (16 float4 per thread: scores 4*tid + 4096*i + c, so
+// index order is (i, tid, c)), one read of the row, one launch, no workspace.
+//   threshold  from the sample key[tid & 15][*] (every 16th group of four
+//              scores; every score of a row up to kExactMax) by two 12-bit
+//              histogram levels, as in the threshold kernel;
+//   select     the exact radix select runs directly over the register keys
+//              at or above the threshold (over all keys of the row when fewer
+//              than K are: the estimate only decides speed);
+//   order      winners are re-identified in registers and written in index
+//              order: their per-stripe counts, packed four 16-bit fields to a
+//              64-bit word, get one block exclusive scan.
+constexpr int kRowMax = 16 * 4096;
 
-__global__ __launch_bounds__(1024) void topk_fused_kernel(TopkParams p) {
-  __shared__ uint32_t cand[2 * kFusedCap];  // keys | indices; later the ordering bitmap
-  uint32_t* ck = cand;
-  uint32_t* ci = cand + kFusedCap;
-  __shared__ int out[DSA_MAX_TOPK];
-  __shared__ int ord[DSA_MAX_TOPK];
-  __shared__ int tpre[1024];
-  __shared__ SelectLds sl;
-  __shared__ uint32_t s_lo[16], s_hi[16];
-  __shared__ int s_wsum[16];
+constexpr int kRowCap = 8192;  // candidates the per-row kernel holds in LDS
+
+struct RowLds {
+  SelectLds sl;
+  uint32_t h2[4096];          // level-2 histogram (cleared with level 1's)
+  uint32_t ck[kRowCap];       // candidate keys, in index order
+  uint32_t ci[kRowCap];       // their indices
+  int ord[DSA_MAX_TOPK];      // the winners in index order
+  uint32_t s_lo[16], s_hi[16];
+  int s_cnt[16];
+  uint64_t wsum[4][16];
+};
+
+// Block exclusive scan of one int per thread (1024 threads); wsum: 16 ints.
+__device__ __forceinline__ int block_excl_scan_i32(int v, int* wsum, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int inc = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  __syncthreads();  // wsum may still be read by a previous scan
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) before += wsum[w];
+    total += wsum[w];
+  }
+  return before + inc - v;
+}
+
+// Exact K-th largest among n keys get(0 .. n-1) (32-bit radix select, 12-bit
+// digits from the highest bit in which they differ).  Afterwards the keys
+// with (key >> sh) > pre win, and: full -> every key with (key >> sh) == pre
+// wins too; else (sh == 0) the first `need` keys equal to pre win.
+template <class Get>
+__device__ __forceinline__ void select32(Get get, int n, uint32_t K, RowLds& L, int& sh_out, uint32_t& pre_out,
+                                         uint32_t& need_out, bool& full_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t mx = 0, mn = 0xFFFFFFFFu;
+  for (int j = tid; j < n; j += 1024) {
+    const uint32_t k2 = get(j);
+    mx = max(mx, k2);
+    mn = min(mn, k2);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+  }
+  __syncthreads();
+  if (lane == 0) {
+    L.s_lo[wave] = mn;
+    L.s_hi[wave] = mx;
+  }
+  __syncthreads();
+  mn = L.s_lo[0];
+  mx = L.s_hi[0];
+  for (int w = 1; w < 16; ++w) {
+    mn = min(mn, L.s_lo[w]);
+    mx = max(mx, L.s_hi[w]);
+  }
+  const uint32_t dif = mx ^ mn;
+  int sh = dif ? 32 - __clz((int)dif) : 0;
+  uint32_t pre = sh >= 32 ? 0u : (mx >> sh);
+  uint32_t need = K;
+  bool full = true;
+  while (sh > 0) {
+    const int lo_sh = max(sh - 12, 0);
+    const uint32_t dmask = (1u << (sh - lo_sh)) - 1u;
+    for (int i = tid; i < 4096; i += 1024) L.sl.h[i] = 0;
+    if (tid == 0) {
+      L.sl.bin = 0;
+      L.sl.need = 1;
+      L.sl.hcount = 1;
+    }
+    __syncthreads();
+    for (int j = tid; j < n; j += 1024) {
+      const uint32_t k2 = get(j);
+      if ((sh >= 32 ? 0u : (k2 >> sh)) == pre) atomicAdd(&L.sl.h[(k2 >> lo_sh) & dmask], 1u);
+    }
+    __syncthreads();
+    int bsel;
+    uint32_t nn, hv;
+    rank_bin_1024(L.sl.h, need, L.sl.wtot, &L.sl.bin, &L.sl.need, bsel, nn, &L.sl.hcount, &hv);
+    pre = (sh >= 32 ? 0u : (pre << (sh - lo_sh))) | (uint32_t)bsel;
+    sh = lo_sh;
+    need = nn;
+    full = hv == nn;
+    if (full) break;
+  }
+  sh_out = sh;
+  pre_out = pre;
+  need_out = need;
+  full_out = full;
+}
+
+// The winners of select32 among get(0 .. n-1), in index order, into ord[]:
+// chunks of 8192 keys, thread tid owning keys 8 tid .. 8 tid + 7 of a chunk;
+// block scans of the counts of equal keys (the tie-break rank) and of
+// winners, carried from chunk to chunk.
+template <class Get, class Idx>
+__device__ __forceinline__ void emit_winners(Get get, Idx index_of, int n, int sh, uint32_t pre, uint32_t need,
+                                             bool full, RowLds& L) {
+  const int tid = threadIdx.x;
+  int eq_carry = 0, win_carry = 0;
+  for (int base = 0; base < n; base += 8 * 1024) {
+    const int j0 = base + 8 * tid;
+    uint32_t kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kv[u] = j0 + u < n ? get(j0 + u) : 0u;
+    uint32_t wmask = 0;
+    if (full) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < n && (kv[u] >> sh) >= pre) wmask |= 1u << u;
+    } else {
+      int e = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) e += (j0 + u < n && kv[u] == pre) ? 1 : 0;
+      int etot;
+      int rk = eq_carry + block_excl_scan_i32(e, L.s_cnt, etot);
+      eq_carry += etot;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= n) continue;
+        if (kv[u] > pre) {
+          wmask |= 1u << u;
+        } else if (kv[u] == pre) {
+          if ((uint32_t)rk < need) wmask |= 1u << u;
+          ++rk;
+        }
+      }
+    }
+    int wtot;
+    int pos = win_carry + block_excl_scan_i32(__popc(wmask), L.s_cnt, wtot);
+    win_carry += wtot;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (wmask >> u & 1u) L.ord[pos++] = index_of(j0 + u);
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
+  __shared__ RowLds L;
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vis = row_vis(p, t);
@@ -625,158 +764,166 @@ __global__ __launch_bounds__(1024) void topk_fused_kernel(TopkParams p) {
     store_all(p, vis, t, r, idx, rows);
     return;
   }
-  // scores 4*tid + 4096*i + c (i < 16, c < 4); key 0 = past the row's end.
   // Every float4 read is issued, unconditionally: a start past the row's ld
   // columns (ld is a multiple of 4) is clamped to the last float4 and its
-  // values are masked, so no read waits behind a branch.
-  const float* row = p.scores + (int64_t)t * p.ld;
-  const int last4 = (int)min<int64_t>(p.ld - 4, 4 * 1024 * 16 - 4);
-  f32x4 x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = *reinterpret_cast<const f32x4*>(row + min(4 * tid + 4096 * i, last4));
+  // values are masked, so no read waits behind a branch.  Key 0 = past vis.
   uint32_t key[16][4];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) key[i][c] = 4 * tid + 4096 * i + c < vis ? order_key(x[i][c]) : 0u;
-
-  // ---- threshold from the sample: all scores of a short row (groups 0 and
-  // 1 hold them), else group i = tid & 15 of every thread (vis / 16 scores
-  // spread over the row), picked by selects rather than a dynamic index
-  const bool exact = vis <= kExactMax;
-  static_assert(kExactMax == 2 * 4096, "a short row lives in groups 0 and 1");
-  uint32_t samp[8];
   {
-    const int sel = tid & 15;
+    const float* row = p.scores + (int64_t)t * p.ld;
+    const int last4 = (int)min<int64_t>(p.ld - 4, kRowMax - 4);
+    f32x4 x[16];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t x = key[0][c];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) x = sel == i ? key[i][c] : x;
-      samp[c] = exact ? key[0][c] : x;
-      samp[4 + c] = exact ? key[1][c] : 0u;
-    }
-  }
-  auto each_sample = [&](auto f) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (samp[j] != 0u) f(samp[j]);
-  };
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  int ns = 0;
-  each_sample([&](uint32_t k2) {
-    lo = min(lo, k2);
-    hi = max(hi, k2);
-    ++ns;
-  });
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-    ns += __shfl_xor(ns, o);
-  }
-  if (lane == 0) {
-    s_lo[wave] = lo;
-    s_hi[wave] = hi;
-    s_wsum[wave] = ns;
-  }
-  for (int i = tid; i < 4096; i += 1024) sl.h[i] = 0;
-  if (tid == 0) {
-    sl.bin = 0;
-    sl.need = 1;
-  }
-  __syncthreads();
-  lo = s_lo[0];
-  hi = s_hi[0];
-  int S = s_wsum[0];
-  for (int w = 1; w < 16; ++w) {
-    lo = min(lo, s_lo[w]);
-    hi = max(hi, s_hi[w]);
-    S += s_wsum[w];
-  }
-  uint32_t rk;
-  if (exact) {
-    rk = (uint32_t)K;
-  } else {
-    const float mu = (float)K * (float)S / (float)vis;
-    rk = (uint32_t)min<int64_t>(S, (int64_t)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
-  }
-  const uint32_t diff = lo ^ hi;
-  const int nbits = diff ? 32 - __clz((int)diff) : 0;
-  const int sh1 = max(nbits - 12, 0);
-  const uint32_t base1 = lo >> sh1;
-  each_sample([&](uint32_t k2) { atomicAdd(&sl.h[(k2 >> sh1) - base1], 1u); });
-  __syncthreads();
-  int b1;
-  uint32_t need1;
-  rank_bin_1024(sl.h, rk, sl.wtot, &sl.bin, &sl.need, b1, need1);
-  uint32_t tau = (base1 + (uint32_t)b1) << sh1;
-  if (sh1 > 0) {
-    const int sh2 = max(sh1 - 12, 0);
-    const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
-    for (int i = tid; i < 4096; i += 1024) sl.h[i] = 0;
-    __syncthreads();
-    each_sample([&](uint32_t k2) {
-      if ((k2 >> sh1) - base1 == (uint32_t)b1) atomicAdd(&sl.h[(k2 >> sh2) & mask2], 1u);
-    });
-    __syncthreads();
-    int b2;
-    uint32_t need2;
-    rank_bin_1024(sl.h, need1, sl.wtot, &sl.bin, &sl.need, b2, need2);
-    tau |= (uint32_t)b2 << sh2;
-  }
-
-  // ---- candidates: keys >= tau, compacted by a block exclusive prefix sum
-  int mine = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) mine += (key[i][c] >= tau && key[i][c] != 0u) ? 1 : 0;
-  int inc = mine;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) s_wsum[wave] = inc;
-  __syncthreads();
-  int pos = inc - mine, ncand = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) pos += s_wsum[w];
-    ncand += s_wsum[w];
-  }
-  // estimate missed (rare): select over the row re-read from memory
-  const bool from_row = ncand < K || ncand > kFusedCap;
-  if (!from_row) {
+    for (int i = 0; i < 16; ++i) x[i] = *reinterpret_cast<const f32x4*>(row + min(4 * tid + 4096 * i, last4));
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (key[i][c] >= tau && key[i][c] != 0u) {
-          ck[pos] = key[i][c];
-          ci[pos] = (uint32_t)(4 * tid + 4096 * i + c);
-          ++pos;
-        }
+      for (int c = 0; c < 4; ++c) key[i][c] = 4 * tid + 4096 * i + c < vis ? order_key(x[i][c]) : 0u;
   }
-  __syncthreads();
-  auto each = [&](auto f) {
-    if (from_row) {
-      for (int i = tid; i < vis; i += 1024) f(composite(order_key(row[i]), (uint32_t)i));
-    } else {
-      for (int i = tid; i < ncand; i += 1024) f(composite(ck[i], ci[i]));
+  for (int i = tid; i < 4096; i += 1024) {
+    L.sl.h[i] = 0;
+    L.h2[i] = 0;
+  }
+  if (tid == 0) {
+    L.sl.bin = 0;
+    L.sl.need = 1;
+  }
+
+  // ---- threshold: keys >= tau are the candidates (tau = 1: every key)
+  uint32_t tau = 1u;
+  if (vis > kExactMax) {
+    uint32_t samp[4];
+    const int sel = tid & 15;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t v = key[0][c];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) v = sel == i ? key[i][c] : v;
+      samp[c] = v;
     }
-  };
-  int hi_sh;
-  uint64_t prefix;
-  select_top(each, (uint32_t)K, sl, hi_sh, prefix);
-  if (tid == 0) sl.cnt = 0;
-  __syncthreads();
-  each([&](uint64_t v2) {
-    if ((v2 >> hi_sh) >= prefix) {
-      const int q = atomicAdd(&sl.cnt, 1);
-      if (q < DSA_MAX_TOPK) out[q] = (int)(0xFFFFFFFFu - (uint32_t)v2);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    int ns = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (samp[c] != 0u) {
+        lo = min(lo, samp[c]);
+        hi = max(hi, samp[c]);
+        ++ns;
+      }
+    for (int o = 32; o > 0; o >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+      ns += __shfl_xor(ns, o);
     }
-  });
-  __syncthreads();
-  order_and_store(p, out, K, vis, cand, 2 * kFusedCap, ord, tpre, sl.wtot, t, r, idx, rows);
+    if (lane == 0) {
+      L.s_lo[wave] = lo;
+      L.s_hi[wave] = hi;
+      L.s_cnt[wave] = ns;
+    }
+    __syncthreads();
+    lo = L.s_lo[0];
+    hi = L.s_hi[0];
+    int S = L.s_cnt[0];
+    for (int w = 1; w < 16; ++w) {
+      lo = min(lo, L.s_lo[w]);
+      hi = max(hi, L.s_hi[w]);
+      S += L.s_cnt[w];
+    }
+    const float mu = (float)K * (float)S / (float)vis;
+    const uint32_t rk = (uint32_t)min<int64_t>(S, (int64_t)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
+    const uint32_t diff = lo ^ hi;
+    const int nbits = diff ? 32 - __clz((int)diff) : 0;
+    const int sh1 = max(nbits - 12, 0);
+    const uint32_t base1 = lo >> sh1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (samp[c] != 0u) atomicAdd(&L.sl.h[(samp[c] >> sh1) - base1], 1u);
+    __syncthreads();
+    int b1;
+    uint32_t need1;
+    rank_bin_1024(L.sl.h, rk, L.sl.wtot, &L.sl.bin, &L.sl.need, b1, need1);
+    tau = (base1 + (uint32_t)b1) << sh1;
+    if (sh1 > 0) {
+      const int sh2 = max(sh1 - 12, 0);
+      const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (samp[c] != 0u && (samp[c] >> sh1) - base1 == (uint32_t)b1) atomicAdd(&L.h2[(samp[c] >> sh2) & mask2], 1u);
+      __syncthreads();
+      int b2;
+      uint32_t need2;
+      rank_bin_1024(L.h2, need1, L.sl.wtot, &L.sl.bin, &L.sl.need, b2, need2);
+      tau |= (uint32_t)b2 << sh2;
+    }
+    tau = max(tau, 1u);
+  }
+
+  // ---- candidates (keys >= tau) into LDS in index order: stripe i's count
+  // in 16-bit field i & 3 of word i >> 2 (a stripe holds at most 4096 keys,
+  // so fields never carry), one block exclusive scan per word
+  auto field = [](const uint64_t (&w)[4], int i) { return (uint32_t)((w[i >> 2] >> (16 * (i & 3))) & 0xFFFFu); };
+  {
+    uint64_t pc[4] = {0, 0, 0, 0}, exc[4], totc[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int n = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) n += key[i][c] >= tau ? 1 : 0;
+      pc[i >> 2] |= (uint64_t)n << (16 * (i & 3));
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) exc[w] = block_excl_scan_u64(pc[w], L.wsum[w], totc[w]);
+    uint32_t ncand = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ncand += field(totc, i);
+    if (ncand >= (uint32_t)K && ncand <= (uint32_t)kRowCap) {
+      uint32_t off = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t pos = off + field(exc, i);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (key[i][c] >= tau) {
+            L.ck[pos] = key[i][c];
+            L.ci[pos] = (uint32_t)(4 * tid + 4096 * i + c);
+            ++pos;
+          }
+        off += field(totc, i);
+      }
+      __syncthreads();
+      // ---- exact select over the candidates, and the winners in order
+      int sh;
+      uint32_t pre, need;
+      bool full;
+      const uint32_t* ck = L.ck;
+      const uint32_t* ci = L.ci;
+      select32([&](int j) { return ck[j]; }, (int)ncand, (uint32_t)K, L, sh, pre, need, full);
+      emit_winners([&](int j) { return ck[j]; }, [&](int j) { return (int)ci[j]; }, (int)ncand, sh, pre, need, full, L);
+      for (int j = tid; j < p.k; j += 1024) {
+        const int li = j < K ? L.ord[j] : -1;
+        idx[j] = li;
+        if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+      }
+      if (p.count && tid == 0) p.count[t] = K;
+      return;
+    }
+  }
+  // ---- the estimate missed (fewer than K or more than kRowCap candidates):
+  // select over the whole row, read again from memory (rare)
+  {
+    const float* row = p.scores + (int64_t)t * p.ld;
+    auto get = [&](int j) { return order_key(row[j]); };
+    int sh;
+    uint32_t pre, need;
+    bool full;
+    select32(get, vis, (uint32_t)K, L, sh, pre, need, full);
+    emit_winners(get, [](int j) { return j; }, vis, sh, pre, need, full, L);
+  }
+  for (int j = tid; j < p.k; j += 1024) {
+    const int li = j < K ? L.ord[j] : -1;
+    idx[j] = li;
+    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+  }
+  if (p.count && tid == 0) p.count[t] = K;
 }
 
 __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, const int32_t* __restrict__ tok_req,
@@ -789,8 +936,8 @@ __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, 
 }
 
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
-  if (p.max_vis <= kFusedMax) {
-    hipLaunchKernelGGL(topk_fused_kernel, dim3(p.T), dim3(1024), 0, stream, p);
+  if (p.max_vis <= kRowMax) {
+    hipLaunchKernelGGL(topk_row_kernel, dim3(p.T), dim3(1024), 0, stream, p);
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
   }
   hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.T), dim3(1024), 0, stream, p);

@@ -146,13 +146,17 @@ def _topk_alone(scores, vis, k, gpu):
     return idx.cpu().numpy(), cnt.cpu().numpy()
 
 
-@pytest.mark.parametrize("ld", [40000, 8000])
-@pytest.mark.parametrize("kind", ["random", "ties", "all_equal", "short_rows", "k1", "negative", "sampled_high"])
+@pytest.mark.parametrize("ld", [100000, 40000, 8000])
+@pytest.mark.parametrize("kind", ["random", "ties", "all_equal", "short_rows", "k1", "negative", "sampled_high",
+                                  "row_sampled_high"])
 def test_topk_exact_on_same_scores(kind, ld, gpu):
-    # ld 40000: threshold / filter / finalize kernels; ld 8000: the one-workgroup
-    # kernel for short rows.  "all_equal" overflows the candidate buffers and
-    # "sampled_high" (large scores only where the threshold sample looks) makes
-    # the sampled threshold too high: both take the whole-row fallback.
+    # ld 100000: threshold / filter / finalize kernels; ld 40000 and 8000: the
+    # one-workgroup-per-row kernel (sampled threshold at 40000, every score at
+    # 8000).  "all_equal" overflows the candidate buffers; "sampled_high" and
+    # "row_sampled_high" put large scores only where the threshold sample of
+    # the multi-kernel path (the first 16 of every 256) or of the per-row
+    # kernel (group (p >> 12) & 15 == (p >> 2) & 15 of four) looks, so the
+    # sampled threshold comes out too high and the whole row is selected from.
     g = np.random.default_rng(42)
     T, k = 6, 2048
     if kind == "random":
@@ -170,10 +174,16 @@ def test_topk_exact_on_same_scores(kind, ld, gpu):
         s = -np.abs(g.standard_normal((T, ld)).astype(np.float32))
         s[:, ::7] = 0.0
         s[:, 3::7] = -0.0
-    else:
+    elif kind == "sampled_high":
         s = g.standard_normal((T, ld)).astype(np.float32)
         s[:, (np.arange(ld) % 256) < 16] += 1000.0
-    if ld == 40000:
+    else:
+        s = g.standard_normal((T, ld)).astype(np.float32)
+        pos = np.arange(ld)
+        s[:, ((pos >> 12) & 15) == ((pos >> 2) & 15)] += 1000.0
+    if ld == 100000:
+        vis = [ld, ld - 1, 30001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 70001, 65537, 8193, 4097]
+    elif ld == 40000:
         vis = [ld, ld - 1, 30001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 40000, 12345, 8193, 4097]
     else:
         vis = [ld, ld - 1, 5001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 8000, 6345, 4097, 2049]
