@@ -100,7 +100,7 @@ MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
   } else {
     // Fill the resident workgroup slots in one round; a second, partial round
     // would cost a whole extra pass.
-    const dsa::MlaShape sh = dsa::mla_shape(pl.ntiles);
+    const dsa::MlaShape sh = dsa::mla_shape(pl.ntiles, a.latents.fmt == DSA_LAT_NVFP4);
     const int64_t resident = 256 * sh.resident_per_cu;
     const int64_t per_split = (int64_t)a.num_rows * sh.groups;
     want = (int)std::min<int64_t>(64, std::max<int64_t>(1, resident / per_split));

@@ -88,16 +88,24 @@ struct MlaParams {
 };
 
 // Workgroup shape of the sparse-MLA kernels: `groups` workgroups per (row,
-// split), each with nw head tiles of 16 heads, one wave per head tile; the
-// kernels hold one wave per SIMD, so 4 / nw workgroups share a CU.
+// split), each with nw / vs head tiles of 16 heads; a workgroup's LDS tile
+// takes a quarter of a CU's LDS per head tile it serves, so 4 / (nw / vs)
+// workgroups share a CU.
 struct MlaShape {
-  int groups, nw, resident_per_cu;
+  int groups, nw, vs, resident_per_cu;
 };
-inline MlaShape mla_shape(int ntiles) {
+// vs waves per head tile, each holding 512 / vs of the value dims: two when
+// the heads fill a single tile and the latents are NVFP4 (whose dequantisation
+// the two waves then share; both compute the tile's scores, each multiplies
+// its half of the values).  For FP8 latents the second wave only repeats the
+// score chain that bounds the tile, so it stays at one.
+inline MlaShape mla_shape(int ntiles, bool split_values) {
   MlaShape s;
   s.groups = (ntiles + 3) / 4;
-  s.nw = (ntiles + s.groups - 1) / s.groups;
-  s.resident_per_cu = 4 / s.nw;
+  const int tiles = (ntiles + s.groups - 1) / s.groups;
+  s.vs = (split_values && ntiles == 1) ? 2 : 1;
+  s.nw = tiles * s.vs;
+  s.resident_per_cu = 4 / tiles;
   return s;
 }
 

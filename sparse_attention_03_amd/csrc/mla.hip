@@ -416,9 +416,9 @@ template <> struct DmaGeo<DSA_LAT_FP8> { static constexpr int SEGS = 9; };    //
 template <> struct DmaGeo<DSA_LAT_NVFP4> { static constexpr int SEGS = 5; };  // 256 B codes, 64 B rope
 
 // Workgroup = NW head tiles, one wave each; DP tiles of rows in flight.
-template <int FMT, int NW, int DP>
-__global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
-  constexpr int NA = 8;  // 64-dim value blocks per wave (all 512 dims)
+template <int FMT, int NW, int DP, int VS>
+__global__ __launch_bounds__(64 * NW, VS) void mla_dma_kernel(MlaParams p) {
+  constexpr int NA = 8 / VS;  // 64-dim value blocks per wave
   constexpr int SEGS = DmaGeo<FMT>::SEGS;
   constexpr int SPT = (SEGS + NW - 1) / NW;  // segment copies per wave per tile
   constexpr int kRawBytes = SEGS * 1024;
@@ -433,8 +433,8 @@ __global__ __launch_bounds__(64 * NW) void mla_dma_kernel(MlaParams p) {
   const int split = blockIdx.x, t = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ht = blockIdx.z * NW + wave;
-  constexpr int a0 = 0;
+  const int ht = blockIdx.z * (NW / VS) + wave / VS;
+  const int a0 = (wave % VS) * NA;  // first value block of this wave
   const int g = lane >> 4, c = lane & 15;
   const int my_row = lane >> 2, q = lane & 3;
   const int j_begin = split * p.split_len;
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
 }
 
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
-  const MlaShape sh = mla_shape(p.ntiles);
+  const MlaShape sh = mla_shape(p.ntiles, p.fmt == DSA_LAT_NVFP4);
   dim3 grid(p.nsplit, p.T, sh.groups), block(64 * sh.nw);
 #define DSA_MLA_LAUNCH(F)                                                                   \
   switch (sh.nw) {                                                                         \
@@ -615,16 +615,20 @@ dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
     case 3: hipLaunchKernelGGL((mla_kernel<F, 3>), grid, block, 0, stream, p); break;      \
     default: hipLaunchKernelGGL((mla_kernel<F, 4>), grid, block, 0, stream, p); break;     \
   }
-#define DSA_MLA_DMA_LAUNCH(F)                                                                      \
-  {                                                                                               \
-    constexpr int DP = kMlaDepth;                                                                 \
-    const size_t lds = mla_dma_lds_bytes(DmaGeo<F>::SEGS, DP, p.split_len);                       \
-    switch (sh.nw) {                                                                              \
-      case 1: hipLaunchKernelGGL((mla_dma_kernel<F, 1, DP>), grid, block, lds, stream, p); break;  \
-      case 2: hipLaunchKernelGGL((mla_dma_kernel<F, 2, DP>), grid, block, lds, stream, p); break;  \
-      case 3: hipLaunchKernelGGL((mla_dma_kernel<F, 3, DP>), grid, block, lds, stream, p); break;  \
-      default: hipLaunchKernelGGL((mla_dma_kernel<F, 4, DP>), grid, block, lds, stream, p); break; \
-    }                                                                                             \
+#define DSA_MLA_DMA_LAUNCH(F)                                                                         \
+  {                                                                                                  \
+    constexpr int DP = kMlaDepth;                                                                    \
+    const size_t lds = mla_dma_lds_bytes(DmaGeo<F>::SEGS, DP, p.split_len);                          \
+    if (sh.vs == 2) {                                                                                \
+      hipLaunchKernelGGL((mla_dma_kernel<F, 2, DP, 2>), grid, block, lds, stream, p);                \
+    } else {                                                                                         \
+      switch (sh.nw) {                                                                               \
+        case 1: hipLaunchKernelGGL((mla_dma_kernel<F, 1, DP, 1>), grid, block, lds, stream, p); break; \
+        case 2: hipLaunchKernelGGL((mla_dma_kernel<F, 2, DP, 1>), grid, block, lds, stream, p); break; \
+        case 3: hipLaunchKernelGGL((mla_dma_kernel<F, 3, DP, 1>), grid, block, lds, stream, p); break; \
+        default: hipLaunchKernelGGL((mla_dma_kernel<F, 4, DP, 1>), grid, block, lds, stream, p); break; \
+      }                                                                                              \
+    }                                                                                                \
   }
   switch (p.fmt) {
     case DSA_LAT_BF16: DSA_MLA_LAUNCH(DSA_LAT_BF16) break;
