@@ -26,6 +26,8 @@
 // The estimate only decides speed: when fewer than K or more than the
 // buffer's capacity of candidates arrived, finalize selects from the whole
 // score row instead (same result).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -38,6 +40,61 @@ constexpr int kRun = 16;            // consecutive scores per sampled block
 __device__ __forceinline__ int row_vis(const TopkParams& p, int t) {
   return min(max(p.tok_vis[t], 0), p.max_vis);
 }
+
+// Wave-wide scans and reductions on DPP lane moves (no LDS round trip): an
+// inclusive prefix sum by shifts within 16-lane rows and two row broadcasts
+// (lane 15 of each row into the next row for rows 1 and 3, then lane 31 into
+// rows 2 and 3); the totals are read from lane 63.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl) { return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63); }
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) { return ~wave_max(~v); }
+// 64-bit max: each step moves both halves of the neighbour's value.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto step = [&](auto ctrl, int row_mask) {
+    (void)ctrl;
+    constexpr int c = decltype(ctrl)::value;
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32), nl, nh;
+    if (row_mask == 0xf) {
+      nl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, c, 0xf, 0xf, false);
+      nh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, c, 0xf, 0xf, false);
+    } else if (row_mask == 0xa) {
+      nl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, c, 0xa, 0xf, false);
+      nh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, c, 0xa, 0xf, false);
+    } else {
+      nl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, c, 0xc, 0xf, false);
+      nh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, c, 0xc, 0xf, false);
+    }
+    const uint64_t n = ((uint64_t)nh << 32) | nl;
+    v = n > v ? n : v;
+  };
+  step(std::integral_constant<int, 0x111>{}, 0xf);
+  step(std::integral_constant<int, 0x112>{}, 0xf);
+  step(std::integral_constant<int, 0x114>{}, 0xf);
+  step(std::integral_constant<int, 0x118>{}, 0xf);
+  step(std::integral_constant<int, 0x142>{}, 0xa);
+  step(std::integral_constant<int, 0x143>{}, 0xc);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return wave_total(wave_scan_incl(v)); }
 
 // Sampling block of a row: B = kRun (every score) for short rows, else the
 // smallest power of two >= 256 with vis / B * kRun <= kMaxSamples.
@@ -62,12 +119,11 @@ __device__ __forceinline__ void rank_bin_1024(const uint32_t* h, uint32_t r, uin
     loc[i] = h[4 * tid + i];
     sum += loc[i];
   }
-  uint32_t suf = sum;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_down(suf, off);
-    if (lane + off < 64) suf += o;
-  }
-  if (lane == 0) wtot[wave] = suf;
+  // suffix sum over the lanes >= this one = wave total - prefix before it
+  const uint32_t pre_incl = wave_scan_incl(sum);
+  const uint32_t wt = wave_total(pre_incl);
+  uint32_t suf = wt - pre_incl + sum;
+  if (lane == 0) wtot[wave] = wt;
   __syncthreads();
   for (int w = wave + 1; w < 16; ++w) suf += wtot[w];
   const uint32_t above = suf - sum;
@@ -125,10 +181,8 @@ __global__ __launch_bounds__(1024) void topk_threshold_kernel(TopkParams p) {
       hi = max(hi, key[i]);
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
   if (lane == 0) {
     s_lo[wave] = lo;
     s_hi[wave] = hi;
@@ -200,13 +254,14 @@ __global__ __launch_bounds__(1024) void topk_threshold_kernel(TopkParams p) {
 // 64-bit word, two words) gives every candidate its place; the slice's
 // candidates go out as one contiguous block behind one global atomic, and
 // the block's (base, count) is recorded for the finalize.
+// (The words hold 16-bit fields whose sums never carry out of their field,
+// so the two 32-bit halves are scanned independently.)
+__device__ __forceinline__ uint64_t wave_scan_incl_u64(uint64_t v) {
+  return (uint64_t)wave_scan_incl((uint32_t)v) | ((uint64_t)wave_scan_incl((uint32_t)(v >> 32)) << 32);
+}
 __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* wsum, uint64_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t inc = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
+  const uint64_t inc = wave_scan_incl_u64(v);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   uint64_t before = 0;
@@ -216,6 +271,31 @@ __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* ws
     total += wsum[w];
   }
   return before + inc - v;
+}
+
+// Four words at once, behind one barrier.  wsum: [16][4].
+__device__ __forceinline__ void block_excl_scan_u64x4(const uint64_t (&v)[4], uint64_t (&ex)[4], uint64_t (&tot)[4],
+                                                      uint64_t (*wsum)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t inc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) inc[i] = wave_scan_incl_u64(v[i]);
+  if (lane == 63)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wsum[wave][i] = inc[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ex[i] = inc[i] - v[i];
+    tot[i] = 0;
+  }
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t x = wsum[w][i];
+      if (w < wave) ex[i] += x;
+      tot[i] += x;
+    }
 }
 
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
@@ -338,11 +418,8 @@ __device__ __forceinline__ void select_top(Each each, uint32_t K, SelectLds& sl,
     mx = v > mx ? v : mx;
     mn = v < mn ? v : mn;
   });
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t a = __shfl_xor(mx, o), b = __shfl_xor(mn, o);
-    mx = a > mx ? a : mx;
-    mn = b < mn ? b : mn;
-  }
+  mx = wave_max_u64(mx);
+  mn = ~wave_max_u64(~mn);
   if (lane == 0) {
     sl.red[0][wave] = mx;
     sl.red[1][wave] = mn;
@@ -409,11 +486,7 @@ __device__ __forceinline__ void order_and_store(const TopkParams& p, const int* 
     __syncthreads();
     int cnt = 0;
     for (int i = 0; i < W; ++i) cnt += __popc(bm[tid * W + i]);
-    int inc = cnt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(inc, off);
-      if (lane >= off) inc += o;
-    }
+    const int inc = (int)wave_scan_incl((uint32_t)cnt);
     if (lane == 63) wsum[wave] = (uint32_t)inc;
     __syncthreads();
     int before = inc - cnt, tot = 0;
@@ -513,12 +586,8 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
       sb = info[2 * tid];
       cnt = info[2 * tid + 1];
     }
-    int inc = (int)cnt;
+    const int inc = (int)wave_scan_incl(cnt);
     const int lane = tid & 63, wave = tid >> 6;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int x = __shfl_up(inc, o);
-      if (lane >= o) inc += x;
-    }
     if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
     __syncthreads();
     int before = 0;
@@ -557,12 +626,8 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
       const int i = kPer * tid + u;
       if (i < ncand && (composite(ck[i], ci[i]) >> hi_sh) >= prefix) m |= 1u << u;
     }
-    int inc = __popc(m);
+    const int inc = (int)wave_scan_incl((uint32_t)__popc(m));
     const int lane = tid & 63, wave = tid >> 6;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int x = __shfl_up(inc, o);
-      if (lane >= o) inc += x;
-    }
     __syncthreads();  // sl.wtot was read by select_top
     if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
     __syncthreads();
@@ -616,17 +681,13 @@ struct RowLds {
   int ord[DSA_MAX_TOPK];      // the winners in index order
   uint32_t s_lo[16], s_hi[16];
   int s_cnt[16];
-  uint64_t wsum[4][16];
+  uint64_t wsum4[16][4];
 };
 
 // Block exclusive scan of one int per thread (1024 threads); wsum: 16 ints.
 __device__ __forceinline__ int block_excl_scan_i32(int v, int* wsum, int& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int inc = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
+  const int inc = (int)wave_scan_incl((uint32_t)v);
   __syncthreads();  // wsum may still be read by a previous scan
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
@@ -653,10 +714,8 @@ __device__ __forceinline__ void select32(Get get, int n, uint32_t K, RowLds& L, 
     mx = max(mx, k2);
     mn = min(mn, k2);
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-  }
+  mx = wave_max(mx);
+  mn = wave_min(mn);
   __syncthreads();
   if (lane == 0) {
     L.s_lo[wave] = mn;
@@ -809,11 +868,9 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
         hi = max(hi, samp[c]);
         ++ns;
       }
-    for (int o = 32; o > 0; o >>= 1) {
-      lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-      hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-      ns += __shfl_xor(ns, o);
-    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    ns = (int)wave_sum((uint32_t)ns);
     if (lane == 0) {
       L.s_lo[wave] = lo;
       L.s_hi[wave] = hi;
@@ -870,8 +927,7 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
       for (int c = 0; c < 4; ++c) n += key[i][c] >= tau ? 1 : 0;
       pc[i >> 2] |= (uint64_t)n << (16 * (i & 3));
     }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) exc[w] = block_excl_scan_u64(pc[w], L.wsum[w], totc[w]);
+    block_excl_scan_u64x4(pc, exc, totc, L.wsum4);
     uint32_t ncand = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ncand += field(totc, i);
