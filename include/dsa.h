@@ -85,7 +85,7 @@ typedef enum dsa_status {
 /* Cache and query formats. */
 enum { DSA_KEY_FP8 = 1, DSA_KEY_MXFP4 = 2 };
 enum { DSA_LAT_BF16 = 1, DSA_LAT_FP8 = 2, DSA_LAT_NVFP4 = 3 };
-enum { DSA_Q_BF16 = 1, DSA_Q_FP8 = 2 };
+enum { DSA_Q_BF16 = 1, DSA_Q_FP8 = 2, DSA_Q_MXFP4 = 3 };
 
 /* Operation ids for dsa_workspace_size(). */
 enum { DSA_OP_INDEXER = 1, DSA_OP_TOPK = 2, DSA_OP_MLA_DECODE = 3, DSA_OP_MLA_PREFILL = 4 };
@@ -198,6 +198,65 @@ typedef struct dsa_mla_args {
 } dsa_mla_args;
 dsa_status sparse_mla_decode(const dsa_mla_args* args, hipStream_t stream);
 dsa_status sparse_mla_prefill(const dsa_mla_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Front end of a step (Kimi K3.1 Pro day-0 page, "Low-latency decoding: the
+ * fused DSA decode path": the indexer front end quantises the index query to
+ * FP8 or MXFP4 with the head weights folded into the quantisation and writes
+ * the new token's index key; the MLA query step writes the new token's latent
+ * into the KV cache).  Quantisation rules, shared by both calls:
+ *   FP8 row   s = amax / 448 (1 for an all-zero row); code = E4M3(x / s)
+ *   MXFP4     per 32 values E8M0 = (fp32 exponent field of amax) - 2,
+ *             clamped to 0..254; code = E2M1(x / 2^(E8M0 - 127))
+ *   NVFP4     per 16 values s = E4M3(amax / 6); code = E2M1(x / value(s)),
+ *             0 when s decodes to 0; rope dims 512..575 E4M3(x), unscaled
+ * E4M3 / E2M1 codes are the nearest value (ties to the even code, saturating
+ * at 448 / 6; zero stored as +0); each division is an IEEE fp32 division
+ * (subnormals kept).  Inputs are BF16. */
+
+/* dsa_quantize_q -- index-query quantisation per (row, head).
+ * FP8: q_out uint8 [T, 32, 128] E4M3, q_scale fp32 [T, 32]; with w_folded
+ * != NULL also w_folded[t, h] = w[t, h] * q_scale[t, h] (fp32), the head
+ * weight folded into the scale (w' ReLU(code . k) = w ReLU((s code) . k) as
+ * s > 0).  The FP8-q indexer takes q_out with either q_scale and w, or a
+ * unit scale and w_folded.  MXFP4: q_out uint8 [T, 32, 64] E2M1 pairs (low
+ * nibble first), q_scale uint8 [T, 32, 4] E8M0; w and w_folded are unused.
+ * T = 0 launches nothing. */
+typedef struct dsa_quant_q_args {
+  int32_t num_rows;              /* T >= 0                                      */
+  const void* q;                 /* device bf16 [T, 32, 128], 16-byte aligned   */
+  const float* w;                /* device fp32 [T, 32] or NULL                 */
+  int32_t fmt;                   /* DSA_Q_FP8 or DSA_Q_MXFP4                    */
+  void* q_out;                   /* device, 16-byte aligned (see above)         */
+  void* q_scale;                 /* device, fp32 [T, 32] or uint8 [T, 32, 4]    */
+  float* w_folded;               /* device fp32 [T, 32] or NULL (FP8; needs w)  */
+} dsa_quant_q_args;
+dsa_status dsa_quantize_q(const dsa_quant_q_args* args, hipStream_t stream);
+
+/* dsa_cache_insert -- write n new tokens into the paged pools.
+ * Token i (request tok_req[i], logical position tok_pos[i]) goes to page
+ * block_table[r * bt_stride + (pos >> p)] (block_table NULL: page r), slot
+ * pos & (P-1), of the key pool (key_vals bf16 [n, 128] quantised to the
+ * pool's format) and of the latent pool (lat_vals bf16 [n, 576]); either may
+ * be NULL.  Only the token's own bytes are written (its codes and scale
+ * words; a latent row's unused tail is left as it is).  A token with a
+ * request outside [0, num_requests), a negative position, a position past its
+ * block-table row or a page outside [0, num_pages) is skipped.  Tokens that
+ * map to the same slot race.  The pools are written through keys.base and
+ * latents.base (device memory the caller owns; the other calls only read it). */
+typedef struct dsa_insert_args {
+  int32_t num_tokens;            /* n >= 0                                      */
+  int32_t num_requests;
+  const int32_t* tok_req;        /* device int32 [n]                            */
+  const int32_t* tok_pos;        /* device int32 [n]                            */
+  const int32_t* block_table;    /* device int32 [R, bt_stride] or NULL         */
+  int32_t bt_stride;
+  const void* key_vals;          /* device bf16 [n, 128] or NULL, 4-byte aligned */
+  dsa_cache keys;                /* fmt DSA_KEY_FP8 or DSA_KEY_MXFP4            */
+  const void* lat_vals;          /* device bf16 [n, 576] or NULL, 16-byte aligned */
+  dsa_cache latents;             /* fmt DSA_LAT_*; same page size as keys       */
+} dsa_insert_args;
+dsa_status dsa_cache_insert(const dsa_insert_args* args, hipStream_t stream);
 
 /* Workspace bytes an operation needs for these arguments (0 if none, or if
  * the arguments are invalid).  `args` points to the op's argument struct. */

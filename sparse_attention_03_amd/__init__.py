@@ -7,7 +7,8 @@ PyTorch supplies device memory and the stream.
 
 Entry points (same names as include/dsa.h):
     dsa_indexer_scores, dsa_topk, dsa_translate_pages,
-    sparse_mla_decode, sparse_mla_prefill, dsa_workspace_size
+    sparse_mla_decode, sparse_mla_prefill, dsa_workspace_size,
+    dsa_quantize_q, dsa_cache_insert (the step's front end)
 plus `decode_step`, which chains them for one layer step.
 """
 from __future__ import annotations
@@ -24,19 +25,19 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 KEY_FP8, KEY_MXFP4 = 1, 2
 LAT_BF16, LAT_FP8, LAT_NVFP4 = 1, 2, 3
-Q_BF16, Q_FP8 = 1, 2
+Q_BF16, Q_FP8, Q_MXFP4 = 1, 2, 3
 OP_INDEXER, OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL = 1, 2, 3, 4
 
 KEY_FMT = {"fp8": KEY_FP8, "mxfp4": KEY_MXFP4}
 LAT_FMT = {"bf16": LAT_BF16, "fp8": LAT_FP8, "nvfp4": LAT_NVFP4}
-Q_FMT = {"bf16": Q_BF16, "fp8": Q_FP8}
+Q_FMT = {"bf16": Q_BF16, "fp8": Q_FP8, "mxfp4": Q_MXFP4}
 KEY_TOKEN_BYTES = {KEY_FP8: 132, KEY_MXFP4: 68}
 LAT_TOKEN_BYTES = {LAT_BF16: 1152, LAT_FP8: 580, LAT_NVFP4: 352}   # data bytes per token
 LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per latent row in a page
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
            "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
-           "dsa_abi_version")
+           "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert")
 
 
 class DsaError(RuntimeError):
@@ -81,6 +82,20 @@ class MlaArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class QuantQArgs(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32), ("q", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("fmt", ctypes.c_int32), ("q_out", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+                ("w_folded", ctypes.c_void_p)]
+
+
+class InsertArgs(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("num_requests", ctypes.c_int32),
+                ("tok_req", ctypes.c_void_p), ("tok_pos", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int32),
+                ("key_vals", ctypes.c_void_p), ("keys", Cache),
+                ("lat_vals", ctypes.c_void_p), ("latents", Cache)]
+
+
 _lib = None
 
 
@@ -97,7 +112,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        ("dsa_topk", [ctypes.POINTER(TopkArgs), vp]),
                        ("sparse_mla_decode", [ctypes.POINTER(MlaArgs), vp]),
                        ("sparse_mla_prefill", [ctypes.POINTER(MlaArgs), vp]),
-                       ("dsa_translate_pages", [vp, i32, ctypes.POINTER(Batch), i32, vp, vp])):
+                       ("dsa_translate_pages", [vp, i32, ctypes.POINTER(Batch), i32, vp, vp]),
+                       ("dsa_quantize_q", [ctypes.POINTER(QuantQArgs), vp]),
+                       ("dsa_cache_insert", [ctypes.POINTER(InsertArgs), vp])):
         f = getattr(lib, name)
         f.argtypes = argt
         f.restype = ctypes.c_int
@@ -174,6 +191,14 @@ def sparse_mla_prefill(args: MlaArgs, stream=None):
     _check(load().sparse_mla_prefill(ctypes.byref(args), _stream(stream)), "sparse_mla_prefill")
 
 
+def dsa_quantize_q(args: QuantQArgs, stream=None):
+    _check(load().dsa_quantize_q(ctypes.byref(args), _stream(stream)), "dsa_quantize_q")
+
+
+def dsa_cache_insert(args: InsertArgs, stream=None):
+    _check(load().dsa_cache_insert(ctypes.byref(args), _stream(stream)), "dsa_cache_insert")
+
+
 def dsa_workspace_size(op: int, args) -> int:
     return int(load().dsa_workspace_size(int(op), ctypes.cast(ctypes.byref(args), ctypes.c_void_p)))
 
@@ -207,6 +232,45 @@ def mla_args(q: torch.Tensor, latents: Cache, rows: torch.Tensor, out: torch.Ten
     return MlaArgs(int(T), int(H), q.data_ptr(), latents, rows.data_ptr(), int(rows.shape[1]),
                    float(sm_scale), int(num_splits), out.data_ptr(), _ptr(lse), _ptr(ws),
                    0 if ws is None else ws.numel())
+
+
+def quantize_q(q: torch.Tensor, w: Optional[torch.Tensor] = None, fmt: str = "fp8", fold: bool = False,
+               stream=None):
+    """Index-query quantisation (dsa_quantize_q) into new tensors.  FP8:
+    returns (codes uint8 [T,32,128], scale fp32 [T,32], w_folded fp32 [T,32]
+    or None); MXFP4: (codes uint8 [T,32,64], E8M0 uint8 [T,32,4], None)."""
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[1:] == (32, 128)
+    T, dev = int(q.shape[0]), q.device
+    if fmt == "fp8":
+        out = torch.empty(T, 32, 128, dtype=torch.uint8, device=dev)
+        scale = torch.empty(T, 32, dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty(T, 32, 64, dtype=torch.uint8, device=dev)
+        scale = torch.empty(T, 32, 4, dtype=torch.uint8, device=dev)
+    wf = torch.empty(T, 32, dtype=torch.float32, device=dev) if fold else None
+    dsa_quantize_q(QuantQArgs(T, q.data_ptr(), _ptr(w), Q_FMT[fmt], out.data_ptr(), scale.data_ptr(), _ptr(wf)),
+                   stream)
+    return out, scale, wf
+
+
+def cache_insert(tok_req: torch.Tensor, tok_pos: torch.Tensor, num_requests: int,
+                 block_table: Optional[torch.Tensor], page_size: int,
+                 key_vals: Optional[torch.Tensor] = None, key_pool: Optional[torch.Tensor] = None,
+                 key_fmt: str = "fp8", lat_vals: Optional[torch.Tensor] = None,
+                 lat_pool: Optional[torch.Tensor] = None, lat_fmt: str = "fp8", stream=None):
+    """Write new tokens' keys / latents (bf16) into the pools (dsa_cache_insert)."""
+    for t in (tok_req, tok_pos):
+        assert t.dtype == torch.int32 and t.is_contiguous()
+    bt_stride = 0
+    if block_table is not None:
+        assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+        bt_stride = int(block_table.shape[1])
+    keys = cache_view(key_pool, page_size, KEY_FMT[key_fmt]) if key_pool is not None else Cache()
+    lats = cache_view(lat_pool, page_size, LAT_FMT[lat_fmt]) if lat_pool is not None else Cache()
+    for v, d in ((key_vals, 128), (lat_vals, 576)):
+        assert v is None or (v.dtype == torch.bfloat16 and v.is_contiguous() and v.shape[-1] == d)
+    dsa_cache_insert(InsertArgs(int(tok_req.numel()), int(num_requests), tok_req.data_ptr(), tok_pos.data_ptr(),
+                                _ptr(block_table), bt_stride, _ptr(key_vals), keys, _ptr(lat_vals), lats), stream)
 
 
 class DecodeStep:

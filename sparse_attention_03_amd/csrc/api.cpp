@@ -326,6 +326,82 @@ dsa_status sparse_mla_prefill(const dsa_mla_args* a, hipStream_t stream) {
   return run_mla(a, stream, true);
 }
 
+dsa_status dsa_quantize_q(const dsa_quant_q_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "quantize_q: null args");
+  if (a->num_rows < 0) return fail(DSA_ERR_INVALID_ARG, "quantize_q: num_rows < 0");
+  if (a->fmt != DSA_Q_FP8 && a->fmt != DSA_Q_MXFP4) return fail(DSA_ERR_UNSUPPORTED, "quantize_q: fmt %d", a->fmt);
+  if (a->num_rows == 0) return DSA_OK;
+  if (a->num_rows > 0x7FFFFFFF / 32) return fail(DSA_ERR_INVALID_ARG, "quantize_q: too many rows");
+  if (!a->q || !aligned(a->q, 16)) return fail(DSA_ERR_INVALID_ARG, "quantize_q: q null or not 16-byte aligned");
+  if (!a->q_out || !aligned(a->q_out, 16)) return fail(DSA_ERR_INVALID_ARG, "quantize_q: q_out null or not 16-byte aligned");
+  if (!a->q_scale || (a->fmt == DSA_Q_FP8 && !aligned(a->q_scale, 4)))
+    return fail(DSA_ERR_INVALID_ARG, "quantize_q: q_scale null or misaligned");
+  if (a->w_folded) {
+    if (a->fmt != DSA_Q_FP8) return fail(DSA_ERR_INVALID_ARG, "quantize_q: w_folded is for FP8 rows only");
+    if (!a->w || !aligned(a->w, 4) || !aligned(a->w_folded, 4))
+      return fail(DSA_ERR_INVALID_ARG, "quantize_q: w_folded needs w (both 4-byte aligned)");
+  }
+  dsa::QuantQParams p{};
+  p.T = a->num_rows;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.w = a->w;
+  p.fmt = a->fmt;
+  p.out = static_cast<uint8_t*>(a->q_out);
+  p.scale = a->q_scale;
+  p.w_folded = a->w_folded;
+  const dsa_status st = dsa::launch_quantize_q(p, stream);
+  if (st != DSA_OK) return fail(st, "quantize_q: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
+dsa_status dsa_cache_insert(const dsa_insert_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "cache_insert: null args");
+  if (a->num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "cache_insert: num_tokens < 0");
+  if (!a->key_vals && !a->lat_vals) return fail(DSA_ERR_INVALID_ARG, "cache_insert: neither keys nor latents given");
+  if (a->key_vals) {
+    if (a->keys.fmt != DSA_KEY_FP8 && a->keys.fmt != DSA_KEY_MXFP4)
+      return fail(DSA_ERR_UNSUPPORTED, "cache_insert: key fmt %d", a->keys.fmt);
+    dsa_status st = check_cache(a->keys, key_token_bytes(a->keys.fmt), "cache_insert keys");
+    if (st != DSA_OK) return st;
+    if (!aligned(a->key_vals, 4)) return fail(DSA_ERR_INVALID_ARG, "cache_insert: key_vals not 4-byte aligned");
+  }
+  if (a->lat_vals) {
+    dsa_status st = check_cache(a->latents, lat_row_bytes(a->latents.fmt), "cache_insert latents");
+    if (st != DSA_OK) return st;
+    if (!aligned(a->lat_vals, 16)) return fail(DSA_ERR_INVALID_ARG, "cache_insert: lat_vals not 16-byte aligned");
+  }
+  if (a->key_vals && a->lat_vals && a->keys.page_size_log2 != a->latents.page_size_log2)
+    return fail(DSA_ERR_INVALID_ARG, "cache_insert: key and latent pages hold different token counts");
+  if (a->num_tokens == 0) return DSA_OK;
+  if (a->num_requests < 1) return fail(DSA_ERR_INVALID_ARG, "cache_insert: num_requests < 1");
+  if (!a->tok_req || !a->tok_pos) return fail(DSA_ERR_INVALID_ARG, "cache_insert: tok_req / tok_pos null");
+  if (a->block_table && a->bt_stride < 1) return fail(DSA_ERR_INVALID_ARG, "cache_insert: bt_stride < 1");
+  dsa::InsertParams p{};
+  p.n = a->num_tokens;
+  p.R = a->num_requests;
+  p.tok_req = a->tok_req;
+  p.tok_pos = a->tok_pos;
+  p.block_table = a->block_table;
+  p.bt_stride = a->bt_stride;
+  p.key_vals = static_cast<const uint16_t*>(a->key_vals);
+  p.keys = static_cast<uint8_t*>(const_cast<void*>(a->keys.base));  // written by this call
+  p.key_page_bytes = a->keys.page_bytes;
+  p.key_plog2 = a->keys.page_size_log2;
+  p.key_num_pages = a->keys.num_pages;
+  p.key_fmt = a->keys.fmt;
+  p.lat_vals = static_cast<const uint16_t*>(a->lat_vals);
+  p.lat = static_cast<uint8_t*>(const_cast<void*>(a->latents.base));
+  p.lat_page_bytes = a->latents.page_bytes;
+  p.lat_plog2 = a->latents.page_size_log2;
+  p.lat_num_pages = a->latents.num_pages;
+  p.lat_fmt = a->latents.fmt;
+  const dsa_status st = dsa::launch_cache_insert(p, stream);
+  if (st != DSA_OK) return fail(st, "cache_insert: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
 size_t dsa_workspace_size(int32_t op, const void* args) {
   if (!args) return 0;
   switch (op) {

@@ -109,6 +109,34 @@ inline MlaShape mla_shape(int ntiles, bool split_values) {
   return s;
 }
 
+struct QuantQParams {
+  int T;
+  const uint16_t* q;   // bf16 bits [T][32][128]
+  const float* w;
+  int fmt;             // DSA_Q_FP8 or DSA_Q_MXFP4
+  uint8_t* out;
+  void* scale;
+  float* w_folded;
+};
+
+struct InsertParams {
+  int n, R;
+  const int32_t* tok_req;
+  const int32_t* tok_pos;
+  const int32_t* block_table;
+  int bt_stride;
+  const uint16_t* key_vals;  // bf16 bits [n][128] or null
+  uint8_t* keys;
+  int64_t key_page_bytes;
+  int key_plog2, key_num_pages, key_fmt;
+  const uint16_t* lat_vals;  // bf16 bits [n][576] or null
+  uint8_t* lat;
+  int64_t lat_page_bytes;
+  int lat_plog2, lat_num_pages, lat_fmt;
+};
+
+dsa_status launch_quantize_q(const QuantQParams& p, hipStream_t stream);
+dsa_status launch_cache_insert(const InsertParams& p, hipStream_t stream);
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream);

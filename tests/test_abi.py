@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
               "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
-              "dsa_abi_version"):
+              "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert"):
         assert n in names
 
 
@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_the_c_compiler(tmp_path):
     """ctypes mirrors of the argument structs have the C compiler's layout."""
     structs = {"dsa_cache": dsa.Cache, "dsa_batch": dsa.Batch, "dsa_indexer_args": dsa.IndexerArgs,
-               "dsa_topk_args": dsa.TopkArgs, "dsa_mla_args": dsa.MlaArgs}
+               "dsa_topk_args": dsa.TopkArgs, "dsa_mla_args": dsa.MlaArgs, "dsa_quant_q_args": dsa.QuantQArgs,
+               "dsa_insert_args": dsa.InsertArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -169,3 +170,52 @@ def test_status_strings():
     lib = dsa.load()
     assert lib.dsa_status_str(0) == b"DSA_OK"
     assert lib.dsa_status_str(4) == b"DSA_ERR_HIP"
+
+
+def _qq_args(**kw):
+    a = dict(num_rows=4, q=FAKE, w=FAKE, fmt=dsa.Q_FP8, q_out=FAKE, q_scale=FAKE, w_folded=None)
+    a.update(kw)
+    return dsa.QuantQArgs(**a)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(num_rows=-1), dsa.DSA_ERR_INVALID_ARG),
+    (dict(fmt=dsa.Q_BF16), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(q=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_out=FAKE + 8), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_scale=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(w=None, w_folded=FAKE), dsa.DSA_ERR_INVALID_ARG),        # folding needs w
+    (dict(fmt=dsa.Q_MXFP4, w_folded=FAKE), dsa.DSA_ERR_INVALID_ARG),  # folding is FP8 only
+])
+def test_quantize_q_rejects_bad_arguments(mut, status):
+    assert dsa.load().dsa_quantize_q(ctypes.byref(_qq_args(**mut)), None) == status
+
+
+def test_quantize_q_zero_rows_launches_nothing():
+    assert dsa.load().dsa_quantize_q(ctypes.byref(_qq_args(num_rows=0, q=None, q_out=None, q_scale=None)), None) == 0
+
+
+def _ins_args(**kw):
+    a = dict(num_tokens=3, num_requests=2, tok_req=FAKE, tok_pos=FAKE, block_table=FAKE, bt_stride=4,
+             key_vals=FAKE, keys=_cache(fmt=dsa.KEY_FP8, plog2=6, page_bytes=132 * 64, pages=8),
+             lat_vals=FAKE, latents=_cache(fmt=dsa.LAT_FP8, plog2=6, page_bytes=640 * 64, pages=8))
+    a.update(kw)
+    return dsa.InsertArgs(**a)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(num_tokens=-1), dsa.DSA_ERR_INVALID_ARG),
+    (dict(key_vals=None, lat_vals=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(keys=_cache(fmt=7, plog2=6, page_bytes=132 * 64, pages=8)), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(keys=_cache(fmt=dsa.KEY_FP8, plog2=6, page_bytes=131 * 64, pages=8)), dsa.DSA_ERR_INVALID_ARG),
+    (dict(latents=_cache(fmt=dsa.LAT_NVFP4, plog2=6, page_bytes=352 * 64, pages=8)), dsa.DSA_ERR_INVALID_ARG),
+    (dict(latents=_cache(fmt=dsa.LAT_FP8, plog2=5, page_bytes=640 * 64, pages=8)), dsa.DSA_ERR_INVALID_ARG),
+    (dict(key_vals=FAKE + 2), dsa.DSA_ERR_INVALID_ARG),
+    (dict(lat_vals=FAKE + 8), dsa.DSA_ERR_INVALID_ARG),
+    (dict(tok_pos=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(num_requests=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(bt_stride=0), dsa.DSA_ERR_INVALID_ARG),
+])
+def test_cache_insert_rejects_bad_arguments(mut, status):
+    assert dsa.load().dsa_cache_insert(ctypes.byref(_ins_args(**mut)), None) == status

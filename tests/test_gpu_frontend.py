@@ -1,0 +1,156 @@
+"""GPU parity of the step's front end (dsa_quantize_q, dsa_cache_insert)
+against the oracle's quantisers, through the C ABI.
+
+Integer and byte results are compared bit for bit: quantised codes, E8M0 and
+E4M3 block scales, fp32 row scales and folded weights (the same IEEE fp32
+divisions and products on both sides), and every byte of the pools after an
+insertion (untouched bytes included).  The FP8 query the front end produces
+then drives the FP8-q indexer, checked against the oracle's scores on those
+same codes (5e-5 of the row maximum, as for every FP8-q score).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import sparse_attention_03_amd as dsa
+from oracle import dsa as O, quant as Q
+from tests.helpers import gpu_step, oracle_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(x: np.ndarray, gpu):
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(gpu)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy()
+
+
+def _query_rows(T, seed):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((T, 32, 128)) * np.exp(g.uniform(-3, 3, (T, 32, 1)))
+    q[0, 3] = 0.0                      # an all-zero head
+    q[1, 5] = 0.0
+    q[1, 5, 7] = -2.0 ** -130          # a single subnormal value
+    q[2, 0] *= 1e-36                   # tiny row (scale near the fp32 subnormal range)
+    q[3, 1] *= 1e30                    # huge row
+    q[4, 2, :8] = [448, -448, 0.75, -1e-3, 6, -6, 3.5, 5.0]
+    return q
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_quantize_q_bit_exact(fmt, gpu):
+    print(f"[gpu] quantize_q {fmt}", flush=True)
+    T = 37
+    q = _bf16(_query_rows(T, 1), gpu)
+    w = torch.from_numpy(np.random.default_rng(2).uniform(-1, 1, (T, 32)).astype(np.float32)).to(gpu)
+    codes, scale, wf = dsa.quantize_q(q, w, fmt, fold=(fmt == "fp8"))
+    torch.cuda.synchronize()
+    rc, rs, rw = Q.quantize_q(_bits(q), w.cpu().numpy(), fmt)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scale.cpu().numpy(), rs)
+    if fmt == "fp8":
+        assert np.array_equal(wf.cpu().numpy(), rw)
+
+
+def _pools(gpu, key_fmt, lat_fmt, P, npg, seed):
+    g = np.random.default_rng(seed)
+    kb = {"fp8": 132, "mxfp4": 68}[key_fmt] * P
+    lb = Q.LAT_ROW_STRIDE[lat_fmt] * P
+    kp = g.integers(0, 256, (npg, kb)).astype(np.uint8)
+    lp = g.integers(0, 256, (npg, lb)).astype(np.uint8)
+    return kp, lp, torch.from_numpy(kp).to(gpu), torch.from_numpy(lp).to(gpu)
+
+
+@pytest.mark.parametrize("key_fmt,lat_fmt", [("fp8", "fp8"), ("fp8", "bf16"), ("fp8", "nvfp4"),
+                                             ("mxfp4", "nvfp4"), ("mxfp4", "fp8"), ("mxfp4", "bf16")])
+@pytest.mark.parametrize("paged", [True, False])
+def test_cache_insert_bit_exact(key_fmt, lat_fmt, paged, gpu):
+    print(f"[gpu] cache_insert {key_fmt}/{lat_fmt} paged={paged}", flush=True)
+    g = np.random.default_rng(7)
+    P, npg, R = 64, 40, 5
+    kp, lp, kpg, lpg = _pools(gpu, key_fmt, lat_fmt, P, npg, 8)
+    if paged:
+        bt = np.stack([g.permutation(npg)[:8] for _ in range(R)]).astype(np.int32)
+        bt[3, 2] = -1                        # absent page: skipped
+        bt[4, 1] = npg + 3                   # page outside the pool: skipped
+        tok_req = np.array([0, 0, 0, 1, 2, 3, 4, 1, 2, 9, -1, 0, 2], np.int32)
+        tok_pos = np.array([0, 63, 64, 511, 200, 130, 70, 5, 201, 3, 3, -4, 600], np.int32)
+    else:
+        bt = None
+        tok_req = np.array([0, 1, 2, 3, 4, 0, 2, 7], np.int32)
+        tok_pos = np.array([0, 63, 17, 40, 1, 62, 18, 0], np.int32)
+    n = len(tok_req)
+    kv = g.standard_normal((n, 128)) * np.exp(g.uniform(-4, 4, (n, 1)))
+    lv = g.standard_normal((n, 576)) * np.exp(g.uniform(-4, 4, (n, 1)))
+    kv[1] = 0.0
+    lv[2, :16] = 0.0                         # a zero NVFP4 block
+    kvt, lvt = _bf16(kv, gpu), _bf16(lv, gpu)
+    dsa.cache_insert(torch.from_numpy(tok_req).to(gpu), torch.from_numpy(tok_pos).to(gpu), R,
+                     None if bt is None else torch.from_numpy(bt).to(gpu), P,
+                     key_vals=kvt, key_pool=kpg, key_fmt=key_fmt, lat_vals=lvt, lat_pool=lpg, lat_fmt=lat_fmt)
+    torch.cuda.synchronize()
+    # the oracle's request bound: requests outside [0, R) are skipped too
+    keep = (tok_req >= 0) & (tok_req < R)
+    rk, rl = Q.cache_insert(kp, key_fmt, lp, lat_fmt, P, None if bt is None else bt.astype(np.int64),
+                            tok_req[keep], tok_pos[keep], _bits(kvt)[keep], _bits(lvt)[keep], npg)
+    assert np.array_equal(kpg.cpu().numpy(), rk)
+    assert np.array_equal(lpg.cpu().numpy(), rl)
+
+
+def test_e4m3_encoder_on_every_code_and_midpoint(gpu):
+    """The unscaled E4M3 encoder (NVFP4 rope dims) over every finite code value
+    and every midpoint between neighbouring codes, both signs."""
+    print("[gpu] e4m3 encoder", flush=True)
+    from oracle import codecs as OC
+    pos = np.arange(0x7F)
+    v = OC.e4m3(pos.astype(np.uint8))
+    mids = (v[:-1] + v[1:]) / 2
+    vals = np.concatenate([v, mids, -v, -mids, [448, 460, 2.0 ** 17, -2.0 ** 17, 2.0 ** -12]])
+    n = (len(vals) + 63) // 64
+    rope = np.zeros(n * 64)
+    rope[:len(vals)] = vals
+    lat = np.zeros((n, 576))
+    lat[:, 512:] = rope.reshape(n, 64)
+    P, npg = 64, 2
+    _, lp, _, lpg = _pools(gpu, "fp8", "nvfp4", P, npg, 3)
+    latt = _bf16(lat, gpu)
+    assert np.array_equal(latt[:, 512:].float().cpu().numpy(), lat[:, 512:].astype(np.float32))  # exact in bf16
+    tok_req = np.zeros(n, np.int32)
+    tok_pos = np.arange(n, dtype=np.int32)
+    dsa.cache_insert(torch.from_numpy(tok_req).to(gpu), torch.from_numpy(tok_pos).to(gpu), 1, None, P,
+                     lat_vals=latt, lat_pool=lpg, lat_fmt="nvfp4")
+    torch.cuda.synchronize()
+    got = lpg.cpu().numpy()[0].reshape(P, 384)[:n, 288:352].reshape(-1)
+    assert np.array_equal(got, Q.e4m3_encode(rope.astype(np.float32)))
+
+
+def test_front_end_feeds_the_fp8_indexer(gpu):
+    """BF16 index queries quantised on the GPU (per-head scale, and the folded
+    form) score like the oracle on the same codes."""
+    print("[gpu] front end -> FP8 indexer", flush=True)
+    spec = synth.CONFIGS["tp8_spec_decode_64k"].replace(R=2, N=9000, seed=44)
+    wl = synth.make_workload(spec, device=gpu)
+    codes, scale, wf = dsa.quantize_q(wl.q_idx, wl.w, "fp8", fold=True)
+    torch.cuda.synchronize()
+    rc, rs, rw = Q.quantize_q(_bits(wl.q_idx), wl.w.cpu().numpy(), "fp8")
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scale.cpu().numpy(), rs)
+    for q_scale, w in ((scale, wl.w), (torch.ones_like(scale), wf)):
+        wl8 = synth.make_workload(spec, device=gpu)
+        wl8.q_idx, wl8.q_idx_scale, wl8.w = codes, q_scale.contiguous(), w.contiguous()
+        wl8.spec = spec.replace(q_fmt="fp8")
+        step = gpu_step(wl8)
+        step.indexer()
+        torch.cuda.synchronize()
+        inp = oracle_inputs(wl8)
+        sc = step.scores.cpu().numpy()
+        rts = inp["req_token_start"]
+        for r in range(spec.R):
+            nmax = int(inp["tok_vis"][rts[r]:rts[r + 1]].max())
+            keys = O.request_keys(inp["key_pool"], spec.key_fmt, wl8.P, inp["block_table"], r, nmax)
+            for t in range(rts[r], rts[r + 1]):
+                n = int(inp["tok_vis"][t])
+                ref = O.indexer_scores(O.dequant_q_idx(inp, t), inp["w"][t], keys[:n])
+                assert np.abs(sc[t, :n] - ref).max() <= 5e-5 * np.abs(ref).max(), f"row {t}"
