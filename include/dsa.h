@@ -88,7 +88,8 @@ enum { DSA_LAT_BF16 = 1, DSA_LAT_FP8 = 2, DSA_LAT_NVFP4 = 3 };
 enum { DSA_Q_BF16 = 1, DSA_Q_FP8 = 2, DSA_Q_MXFP4 = 3 };
 
 /* Operation ids for dsa_workspace_size(). */
-enum { DSA_OP_INDEXER = 1, DSA_OP_TOPK = 2, DSA_OP_MLA_DECODE = 3, DSA_OP_MLA_PREFILL = 4 };
+enum { DSA_OP_INDEXER = 1, DSA_OP_TOPK = 2, DSA_OP_MLA_DECODE = 3, DSA_OP_MLA_PREFILL = 4,
+       DSA_OP_TOPK_SHARDED = 5 };
 
 /* One paged pool (index keys or latents) of one layer. */
 typedef struct dsa_cache {
@@ -166,6 +167,46 @@ dsa_status dsa_topk(const dsa_topk_args* args, hipStream_t stream);
  * request's block-table row) stays -1.  Non-paged (block_table NULL): page = r. */
 dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* batch,
                                int32_t page_size_log2, int32_t* rows, hipStream_t stream);
+
+/* dsa_topk_sharded -- the exact top-k merge of decode context parallelism,
+ * its W shards emulated on this device (Kimi K3.1 Pro day-0 page, "Long
+ * context: decode context parallel" and "Exact top-k merge").  Shard r of W
+ * holds every W-th token of a row: global token s = j*W + r sits at local
+ * position j, and the shard's scores of row t are
+ *     scores[(r*num_rows + t)*ld + j],  j < n_r(t) = ceil((tok_vis[t] - r)/W)
+ * (the layout each shard's indexer writes).  Steps, all on `stream`:
+ *   1. every shard keeps its local top-min(k, n_r) of each row and sends the
+ *      `cand` best of them as (fp32 score, global index) candidates;
+ *   2. per row, the K_t = min(k, tok_vis[t]) best candidates of the union are
+ *      selected; a shard all of whose candidates were selected while it sent
+ *      fewer than min(k, n_r) is flagged, since it may hold more of the top-k;
+ *   3. flagged shards send their full local top-k and flagged rows are
+ *      selected again (one round always suffices).
+ * The result is the unsharded top-k of the row -- the same as dsa_topk on the
+ * row in global order: idx[t, 0..K_t) the ascending global indices, -1
+ * padded to k; count[t] = K_t (if count != NULL); resend[t*W + r] = 1 for the
+ * flagged shards, else 0 (if resend != NULL).  Scores must be finite.
+ * Errors: DSA_ERR_INVALID_ARG for num_rows < 1, W outside [1, 16], k outside
+ * [1, 2048], cand outside [0, k], max_vis < 1, ld < ceil(max_vis / W) or not
+ * a multiple of 4, a null or unaligned pointer; DSA_ERR_WORKSPACE when the
+ * workspace is missing, unaligned or smaller than dsa_workspace_size(
+ * DSA_OP_TOPK_SHARDED, args). */
+typedef struct dsa_topk_sharded_args {
+  int32_t num_rows;              /* T >= 1                                     */
+  int32_t num_shards;            /* W, 1 .. 16                                 */
+  const float* scores;           /* device fp32 [W, T, ld], 16-byte aligned    */
+  int64_t ld;                    /* >= ceil(max_vis / W), multiple of 4        */
+  const int32_t* tok_vis;        /* device int32 [T]: global visible count     */
+  int32_t max_vis;               /* host bound on tok_vis (values are clamped) */
+  int32_t k;                     /* 1 .. 2048                                  */
+  int32_t cand;                  /* candidates a shard sends, 0 = ceil(1.5k/W) */
+  int32_t* idx;                  /* device int32 [T, k]                        */
+  int32_t* count;                /* device int32 [T] or NULL                   */
+  int32_t* resend;               /* device int32 [T, W] or NULL                */
+  void* workspace;               /* device, 256-byte aligned                   */
+  size_t workspace_bytes;
+} dsa_topk_sharded_args;
+dsa_status dsa_topk_sharded(const dsa_topk_sharded_args* args, hipStream_t stream);
 
 /* sparse_mla_decode / sparse_mla_prefill -- stage 3, exact MLA over the
  * selected rows.  For row t and head h < num_heads, over the valid entries s

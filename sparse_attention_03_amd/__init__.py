@@ -26,7 +26,7 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 KEY_FP8, KEY_MXFP4 = 1, 2
 LAT_BF16, LAT_FP8, LAT_NVFP4 = 1, 2, 3
 Q_BF16, Q_FP8, Q_MXFP4 = 1, 2, 3
-OP_INDEXER, OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL = 1, 2, 3, 4
+OP_INDEXER, OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_TOPK_SHARDED = 1, 2, 3, 4, 5
 
 KEY_FMT = {"fp8": KEY_FP8, "mxfp4": KEY_MXFP4}
 LAT_FMT = {"bf16": LAT_BF16, "fp8": LAT_FP8, "nvfp4": LAT_NVFP4}
@@ -37,7 +37,7 @@ LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per l
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
            "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
-           "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert")
+           "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded")
 
 
 class DsaError(RuntimeError):
@@ -71,6 +71,14 @@ class TopkArgs(ctypes.Structure):
                 ("k", ctypes.c_int32), ("idx", ctypes.c_void_p), ("rows", ctypes.c_void_p),
                 ("page_size_log2", ctypes.c_int32), ("count", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class TopkShardedArgs(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32), ("num_shards", ctypes.c_int32), ("scores", ctypes.c_void_p),
+                ("ld", ctypes.c_int64), ("tok_vis", ctypes.c_void_p), ("max_vis", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("cand", ctypes.c_int32), ("idx", ctypes.c_void_p),
+                ("count", ctypes.c_void_p), ("resend", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class MlaArgs(ctypes.Structure):
@@ -114,7 +122,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        ("sparse_mla_prefill", [ctypes.POINTER(MlaArgs), vp]),
                        ("dsa_translate_pages", [vp, i32, ctypes.POINTER(Batch), i32, vp, vp]),
                        ("dsa_quantize_q", [ctypes.POINTER(QuantQArgs), vp]),
-                       ("dsa_cache_insert", [ctypes.POINTER(InsertArgs), vp])):
+                       ("dsa_cache_insert", [ctypes.POINTER(InsertArgs), vp]),
+                       ("dsa_topk_sharded", [ctypes.POINTER(TopkShardedArgs), vp])):
         f = getattr(lib, name)
         f.argtypes = argt
         f.restype = ctypes.c_int
@@ -199,6 +208,10 @@ def dsa_cache_insert(args: InsertArgs, stream=None):
     _check(load().dsa_cache_insert(ctypes.byref(args), _stream(stream)), "dsa_cache_insert")
 
 
+def dsa_topk_sharded(args: TopkShardedArgs, stream=None):
+    _check(load().dsa_topk_sharded(ctypes.byref(args), _stream(stream)), "dsa_topk_sharded")
+
+
 def dsa_workspace_size(op: int, args) -> int:
     return int(load().dsa_workspace_size(int(op), ctypes.cast(ctypes.byref(args), ctypes.c_void_p)))
 
@@ -271,6 +284,37 @@ def cache_insert(tok_req: torch.Tensor, tok_pos: torch.Tensor, num_requests: int
         assert v is None or (v.dtype == torch.bfloat16 and v.is_contiguous() and v.shape[-1] == d)
     dsa_cache_insert(InsertArgs(int(tok_req.numel()), int(num_requests), tok_req.data_ptr(), tok_pos.data_ptr(),
                                 _ptr(block_table), bt_stride, _ptr(key_vals), keys, _ptr(lat_vals), lats), stream)
+
+
+class ShardedTopk:
+    """The sharded top-k merge (dsa_topk_sharded) over fixed buffers: local
+    scores [W, T, ld] fp32 in the interleaved shard layout."""
+
+    def __init__(self, scores: torch.Tensor, tok_vis: torch.Tensor, max_vis: int, k: int, cand: int = 0):
+        assert scores.dtype == torch.float32 and scores.dim() == 3 and scores.is_contiguous()
+        assert tok_vis.dtype == torch.int32 and tok_vis.is_contiguous()
+        W, T, ld = (int(x) for x in scores.shape)
+        dev = scores.device
+        self.idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+        self.count = torch.empty(T, dtype=torch.int32, device=dev)
+        self.resend = torch.empty(T, W, dtype=torch.int32, device=dev)
+        self.args = TopkShardedArgs(T, W, scores.data_ptr(), ld, tok_vis.data_ptr(), int(max_vis), int(k),
+                                    int(cand), self.idx.data_ptr(), self.count.data_ptr(),
+                                    self.resend.data_ptr(), None, 0)
+        self.ws = workspace(dsa_workspace_size(OP_TOPK_SHARDED, self.args), dev)
+        self.args.workspace = _ptr(self.ws)
+        self.args.workspace_bytes = 0 if self.ws is None else self.ws.numel()
+
+    def __call__(self, stream=None):
+        dsa_topk_sharded(self.args, stream)
+        return self.idx, self.count, self.resend
+
+
+def topk_sharded(scores: torch.Tensor, tok_vis: torch.Tensor, max_vis: int, k: int, cand: int = 0,
+                 stream=None):
+    """One call of dsa_topk_sharded into new tensors: (idx [T,k], count [T],
+    resend flags [T,W])."""
+    return ShardedTopk(scores, tok_vis, max_vis, k, cand)(stream)
 
 
 class DecodeStep:

@@ -83,6 +83,46 @@ TopkPlan plan_topk(int T, int max_vis, int k) {
   return pl;
 }
 
+// ---- sharded top-k plan
+struct ShardedPlan {
+  int W, T, k, cand, max_local;
+  TopkPlan local;
+  size_t off_lvis, off_lidx, off_topk, off_xbuf, off_xcnt, off_flags, off_rowflag, total;
+};
+ShardedPlan plan_sharded(const dsa_topk_sharded_args& a) {
+  ShardedPlan pl;
+  pl.W = a.num_shards;
+  pl.T = a.num_rows;
+  pl.k = a.k;
+  pl.cand = a.cand > 0 ? a.cand : std::min(a.k, (3 * a.k + 2 * a.num_shards - 1) / (2 * a.num_shards));
+  pl.max_local = std::max(1, (a.max_vis + a.num_shards - 1) / a.num_shards);
+  const size_t n = (size_t)pl.W * pl.T;
+  pl.local = plan_topk((int)n, pl.max_local, a.k);
+  size_t off = 0;
+  pl.off_lvis = off;
+  off = align_up(off + n * 4, 256);
+  pl.off_lidx = off;
+  off = align_up(off + n * a.k * 4, 256);
+  pl.off_topk = off;
+  off = align_up(off + pl.local.total, 256);
+  pl.off_xbuf = off;
+  off = align_up(off + n * a.k * 8, 256);
+  pl.off_xcnt = off;
+  off = align_up(off + n * 4, 256);
+  pl.off_flags = off;
+  off = align_up(off + n * 4, 256);
+  pl.off_rowflag = off;
+  off = align_up(off + (size_t)pl.T * 4, 256);
+  pl.total = off;
+  return pl;
+}
+
+bool sharded_shape_ok(const dsa_topk_sharded_args& a) {
+  return a.num_rows >= 1 && a.num_shards >= 1 && a.num_shards <= dsa::kMaxShards && a.k >= 1 &&
+         a.k <= DSA_MAX_TOPK && a.cand >= 0 && a.cand <= a.k && a.max_vis >= 1 &&
+         (int64_t)a.num_rows * a.num_shards <= 65535LL * 64;
+}
+
 // ---- MLA plan
 struct MlaPlan {
   int Hpad, ntiles, nsplit, split_len;
@@ -302,6 +342,63 @@ dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   return DSA_OK;
 }
 
+dsa_status dsa_topk_sharded(const dsa_topk_sharded_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "topk_sharded: null args");
+  if (!sharded_shape_ok(*a))
+    return fail(DSA_ERR_INVALID_ARG, "topk_sharded: rows %d, shards %d (1..%d), k %d, cand %d or max_vis %d out of range",
+                a->num_rows, a->num_shards, dsa::kMaxShards, a->k, a->cand, a->max_vis);
+  if (!a->scores || !aligned(a->scores, 16))
+    return fail(DSA_ERR_INVALID_ARG, "topk_sharded: scores null or not 16-byte aligned");
+  const int64_t max_local = (a->max_vis + a->num_shards - 1) / a->num_shards;
+  if (a->ld < max_local || a->ld % 4 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "topk_sharded: ld %lld (needs >= %lld, multiple of 4)", (long long)a->ld,
+                (long long)max_local);
+  if (!a->tok_vis || !a->idx) return fail(DSA_ERR_INVALID_ARG, "topk_sharded: tok_vis or idx is null");
+  const ShardedPlan pl = plan_sharded(*a);
+  if (!a->workspace || !aligned(a->workspace, 256))
+    return fail(DSA_ERR_WORKSPACE, "topk_sharded: workspace null or not 256-byte aligned (%zu bytes needed)", pl.total);
+  if (a->workspace_bytes < pl.total)
+    return fail(DSA_ERR_WORKSPACE, "topk_sharded: workspace %zu bytes, %zu needed", a->workspace_bytes, pl.total);
+  char* ws = static_cast<char*>(a->workspace);
+  dsa::MergeParams m{};
+  m.T = pl.T;
+  m.W = pl.W;
+  m.k = pl.k;
+  m.cand = pl.cand;
+  m.scores = a->scores;
+  m.ld = a->ld;
+  m.tok_vis = a->tok_vis;
+  m.max_vis = a->max_vis;
+  m.idx = a->idx;
+  m.count = a->count;
+  m.lvis = reinterpret_cast<int32_t*>(ws + pl.off_lvis);
+  m.lidx = reinterpret_cast<int32_t*>(ws + pl.off_lidx);
+  m.xbuf = reinterpret_cast<uint64_t*>(ws + pl.off_xbuf);
+  m.xcnt = reinterpret_cast<int32_t*>(ws + pl.off_xcnt);
+  m.flags = a->resend ? a->resend : reinterpret_cast<int32_t*>(ws + pl.off_flags);
+  m.rowflag = reinterpret_cast<int32_t*>(ws + pl.off_rowflag);
+  dsa::TopkParams p{};
+  p.T = pl.W * pl.T;
+  p.scores = a->scores;
+  p.ld = a->ld;
+  p.tok_vis = m.lvis;
+  p.max_vis = pl.max_local;
+  p.k = a->k;
+  p.idx = m.lidx;
+  char* tws = ws + pl.off_topk;
+  p.ctr = reinterpret_cast<uint32_t*>(tws + pl.local.off_ctr);
+  p.cand = reinterpret_cast<uint32_t*>(tws + pl.local.off_cand);
+  p.slice_info = reinterpret_cast<uint32_t*>(tws + pl.local.off_info);
+  p.cand_cap = pl.local.cand_cap;
+  p.slice = pl.local.slice;
+  p.nslices = pl.local.nslices;
+  p.skip_empty = 1;
+  dsa_status st = dsa::launch_topk_sharded(m, p, stream);
+  if (st != DSA_OK) return fail(st, "topk_sharded: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
 dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* b, int32_t page_size_log2,
                                int32_t* rows, hipStream_t stream) {
   g_err[0] = 0;
@@ -410,6 +507,11 @@ size_t dsa_workspace_size(int32_t op, const void* args) {
       const dsa_topk_args* a = static_cast<const dsa_topk_args*>(args);
       if (a->k < 1 || a->k > DSA_MAX_TOPK || a->batch.num_rows < 1 || a->batch.max_vis < 1) return 0;
       return plan_topk(a->batch.num_rows, a->batch.max_vis, a->k).total;
+    }
+    case DSA_OP_TOPK_SHARDED: {
+      const dsa_topk_sharded_args* a = static_cast<const dsa_topk_sharded_args*>(args);
+      if (!sharded_shape_ok(*a)) return 0;
+      return plan_sharded(*a).total;
     }
     case DSA_OP_MLA_DECODE:
     case DSA_OP_MLA_PREFILL: {

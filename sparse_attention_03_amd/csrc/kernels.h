@@ -66,6 +66,27 @@ struct TopkParams {
   int cand_cap;
   int slice;            // scores per workgroup in the filter pass
   int nslices;
+  int skip_empty;       // rows with no visible score write nothing (not even padding)
+};
+
+// Shards of the sharded top-k merge (context shards of one row).
+constexpr int kMaxShards = 16;
+
+struct MergeParams {
+  int T, W, k, cand;
+  const float* scores;  // [W][T][ld] shard-local scores
+  int64_t ld;
+  const int32_t* tok_vis;
+  int max_vis;
+  int32_t* idx;         // [T][k]
+  int32_t* count;       // [T] or null
+  // workspace
+  int32_t* lvis;        // [W*T] local visible counts (shard row r*T + t)
+  int32_t* lidx;        // [W*T][k] local top-k positions
+  uint64_t* xbuf;       // [W*T][k] exchange buffer: composites each shard row sent
+  int32_t* xcnt;        // [W*T] composites sent
+  int32_t* flags;       // [T][W] re-send flags
+  int32_t* rowflag;     // [T] any re-send in the row
 };
 
 struct MlaParams {
@@ -140,6 +161,7 @@ dsa_status launch_cache_insert(const InsertParams& p, hipStream_t stream);
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream);
+dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hipStream_t stream);
 dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req,
                             const int32_t* block_table, int bt_stride, int plog2, int32_t* rows,
                             hipStream_t stream);

@@ -519,6 +519,7 @@ __device__ __forceinline__ void order_and_store(const TopkParams& p, const int* 
 
 // A row with vis <= k keeps every position.
 __device__ __forceinline__ void store_all(const TopkParams& p, int vis, int t, int r, int32_t* idx, int32_t* rows) {
+  if (vis <= 0 && p.skip_empty) return;
   for (int j = threadIdx.x; j < p.k; j += blockDim.x) {
     const int li = j < vis ? j : -1;
     idx[j] = li;

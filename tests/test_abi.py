@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
               "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
-              "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert"):
+              "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded"):
         assert n in names
 
 
@@ -39,7 +39,7 @@ def test_struct_layouts_match_the_c_compiler(tmp_path):
     """ctypes mirrors of the argument structs have the C compiler's layout."""
     structs = {"dsa_cache": dsa.Cache, "dsa_batch": dsa.Batch, "dsa_indexer_args": dsa.IndexerArgs,
                "dsa_topk_args": dsa.TopkArgs, "dsa_mla_args": dsa.MlaArgs, "dsa_quant_q_args": dsa.QuantQArgs,
-               "dsa_insert_args": dsa.InsertArgs}
+               "dsa_insert_args": dsa.InsertArgs, "dsa_topk_sharded_args": dsa.TopkShardedArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -116,6 +116,46 @@ def _topk_args(**kw):
 ])
 def test_topk_rejects_bad_arguments(mut, status):
     assert dsa.load().dsa_topk(ctypes.byref(_topk_args(**mut)), None) == status
+
+
+def _sharded_args(**kw):
+    a = dict(num_rows=4, num_shards=8, scores=FAKE, ld=8192, tok_vis=FAKE, max_vis=65536, k=2048, cand=0,
+             idx=FAKE, count=None, resend=None, workspace=FAKE, workspace_bytes=1 << 40)
+    a.update(kw)
+    return dsa.TopkShardedArgs(**a)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(num_rows=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(num_shards=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(num_shards=17), dsa.DSA_ERR_INVALID_ARG),
+    (dict(k=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(k=2049), dsa.DSA_ERR_INVALID_ARG),
+    (dict(cand=-1), dsa.DSA_ERR_INVALID_ARG),
+    (dict(cand=2049), dsa.DSA_ERR_INVALID_ARG),
+    (dict(max_vis=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(ld=8188), dsa.DSA_ERR_INVALID_ARG),          # < ceil(65536 / 8)
+    (dict(ld=8194), dsa.DSA_ERR_INVALID_ARG),          # not a multiple of 4
+    (dict(scores=FAKE + 4), dsa.DSA_ERR_INVALID_ARG),
+    (dict(tok_vis=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(idx=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(workspace=None), dsa.DSA_ERR_WORKSPACE),
+    (dict(workspace=FAKE + 64), dsa.DSA_ERR_WORKSPACE),
+    (dict(workspace_bytes=100), dsa.DSA_ERR_WORKSPACE),
+])
+def test_topk_sharded_rejects_bad_arguments(mut, status):
+    lib = dsa.load()
+    assert lib.dsa_topk_sharded(ctypes.byref(_sharded_args(**mut)), None) == status
+    assert lib.dsa_last_error().decode() != ""
+
+
+def test_topk_sharded_workspace_size():
+    a = _sharded_args()
+    n = dsa.dsa_workspace_size(dsa.OP_TOPK_SHARDED, a)
+    # at least the local top-k positions and the exchange buffer (W*T*k*(4+8) bytes)
+    assert n >= 8 * 4 * 2048 * 12
+    assert dsa.dsa_workspace_size(dsa.OP_TOPK_SHARDED, _sharded_args(num_shards=17)) == 0
+    assert dsa.dsa_workspace_size(dsa.OP_TOPK_SHARDED, _sharded_args(cand=3000)) == 0
 
 
 def _mla_args(**kw):
