@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--workload", default="tp8_spec_decode_64k")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle sample (0 disables the CPU baseline)")
+    ap.add_argument("--shards", type=int, default=8,
+                    help="context shards of the sharded top-k merge measurement (0 or 1 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
                          "the HBM byte counters of a profiler against a known size")
@@ -239,6 +241,42 @@ def main():
         fe = {"us": round(fe_ms * 1e3, 2), "q_fmt": q_fmt_fe, "tokens": wl.T, "alg_bytes": fe_bytes,
               "GB_per_s": round(fe_bytes / (fe_ms * 1e-3) / 1e9, 2), "gpu_bound_timing": backlog_ok}
 
+    # The exact sharded top-k merge (context shards emulated on this device),
+    # timed apart from the step on the step's own scores: each shard's share
+    # of every row in the interleaved layout, eight shards.
+    shard = None
+    if not prefill and args.shards > 1:
+        W = args.shards
+        ld_l = -(-(-(-spec.N // W)) // 4) * 4
+        full = torch.zeros(wl.T, ld_l * W, dtype=torch.float32, device=dev)
+        n_cols = min(step.scores.shape[1], ld_l * W)
+        full[:, :n_cols] = step.scores[:, :n_cols]
+        local = full.view(wl.T, ld_l, W).permute(2, 0, 1).contiguous()
+        del full
+        st_op = dsa.ShardedTopk(local, wl.tok_vis, spec.N, spec.k)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            st_op()
+        torch.cuda.synchronize()
+        s0, s1 = E(enable_timing=True), E(enable_timing=True)
+        s0.record()
+        for _ in range(K):
+            st_op()
+        s1.record()
+        torch.cuda.synchronize()
+        sh_ms = s0.elapsed_time(s1) / K
+        same = bool(torch.equal(st_op.idx, step.idx))
+        resent = st_op.resend.cpu().numpy()
+        cand = min(spec.k, -(-3 * spec.k // (2 * W)))
+        n_loc = [[max(0, -(-(v - r) // W)) for r in range(W)] for v in vis]
+        sent = sum(min(cand, n) for row in n_loc for n in row)
+        sent += sum(min(spec.k, n_loc[t][r]) for t in range(wl.T) for r in range(W) if resent[t, r])
+        generic = sum(min(spec.k, n) for row in n_loc for n in row)
+        shard = {"shards": W, "cand": cand, "us": round(sh_ms * 1e3, 2), "unsharded_topk_us": round(st["topk"] * 1e3, 2),
+                 "equals_unsharded": same, "rows_resent": int((resent.sum(axis=1) > 0).sum()),
+                 "exchange_bytes": 8 * sent, "generic_exchange_bytes": 8 * generic}
+        del local, st_op
+
     cpu = None
     if args.cpu_seconds > 0:
         def bytes_of_rows(nreq, rows):
@@ -263,6 +301,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "front_end": fe,
+        "sharded_topk": shard,
     }
     print(json.dumps(rec), flush=True)
 

@@ -87,7 +87,7 @@ TopkPlan plan_topk(int T, int max_vis, int k) {
 struct ShardedPlan {
   int W, T, k, cand, max_local;
   TopkPlan local;
-  size_t off_lvis, off_lidx, off_topk, off_xbuf, off_xcnt, off_flags, off_rowflag, total;
+  size_t off_lvis, off_lvis2, off_lidx, off_topk, off_xbuf, off_xcnt, off_flags, off_rowflag, total;
 };
 ShardedPlan plan_sharded(const dsa_topk_sharded_args& a) {
   ShardedPlan pl;
@@ -100,6 +100,8 @@ ShardedPlan plan_sharded(const dsa_topk_sharded_args& a) {
   pl.local = plan_topk((int)n, pl.max_local, a.k);
   size_t off = 0;
   pl.off_lvis = off;
+  off = align_up(off + n * 4, 256);
+  pl.off_lvis2 = off;
   off = align_up(off + n * 4, 256);
   pl.off_lidx = off;
   off = align_up(off + n * a.k * 4, 256);
@@ -373,6 +375,7 @@ dsa_status dsa_topk_sharded(const dsa_topk_sharded_args* a, hipStream_t stream) 
   m.idx = a->idx;
   m.count = a->count;
   m.lvis = reinterpret_cast<int32_t*>(ws + pl.off_lvis);
+  m.lvis2 = reinterpret_cast<int32_t*>(ws + pl.off_lvis2);
   m.lidx = reinterpret_cast<int32_t*>(ws + pl.off_lidx);
   m.xbuf = reinterpret_cast<uint64_t*>(ws + pl.off_xbuf);
   m.xcnt = reinterpret_cast<int32_t*>(ws + pl.off_xcnt);

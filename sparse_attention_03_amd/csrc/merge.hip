@@ -13,90 +13,29 @@
 //
 // Launch sequence (all on the caller's stream, no host round trip):
 //   shard_vis     n_r(t) = ceil((vis_t - r) / W) for every (r, t)
-//   local top-k   the per-row top-k on the W*T shard rows (k per row, the full
-//                 local top-k a shard keeps for a possible re-send)
-//   pack(1)       per shard row, the cand best of its local top-k -> exchange
+//   top-k(cand)   every shard row selects its cand best local positions (the
+//                 per-row top-k kernels on the W*T shard rows)
+//   pack(1)       -> composites in the exchange buffer
 //   merge(1)      per row: select K_t = min(k, vis_t) from the union; flag the
 //                 shards that must re-send, or emit the ordered result
-//   pack(2)       flagged shard rows: the full local top-k -> exchange
+//   top-k(k)      flagged shard rows select their full local top-k (the other
+//                 shard rows see no visible token and return at once)
+//   pack(2)       flagged shard rows -> exchange
 //   merge(2)      flagged rows: select again and emit (cannot flag again)
 #include "common.h"
 #include "kernels.h"
+#include "radix.h"
 
 namespace dsa {
 
 namespace {
 
 constexpr int kMergeThreads = 1024;
-constexpr int kMergePer = kMaxShards * DSA_MAX_TOPK / kMergeThreads;  // 32 composites per thread
+constexpr int kMergeLdsCap = 4096;  // unions up to this many composites are staged in LDS
 constexpr int kPackThreads = 256;
-constexpr int kPackPer = DSA_MAX_TOPK / kPackThreads;                   // 8
 
-struct SelLds {
-  uint32_t hist[256];
-  uint32_t wsum[16];
-  uint64_t prefix;
-  int rho;
-  int done;
-};
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
-// The rho-th largest nonzero composite held by the block (PER per thread, 0 =
-// empty slot), 1 <= rho <= number of nonzero composites.  Radix select over
-// 8-bit digits from the top; stops at the first digit whose chosen bin is
-// taken whole.  On return a composite c is among the rho largest iff
-// c != 0 and (c >> shift) >= (prefix >> shift).
-template <int PER>
-__device__ void select_rank(const uint64_t (&c)[PER], int rho, SelLds& L, uint64_t& out_prefix, int& out_shift) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t prefix = 0;
-  int shift = 56;
-  for (int pass = 0; pass < 8; ++pass, shift -= 8) {
-    for (int b = tid; b < 256; b += blockDim.x) L.hist[b] = 0;
-    __syncthreads();
-    const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (c[i] != 0 && ((c[i] ^ prefix) & hi_mask) == 0) atomicAdd(&L.hist[(uint32_t)(c[i] >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    // inclusive scan over bins in descending order: thread j holds bin 255 - j
-    const uint32_t h = tid < 256 ? L.hist[255 - tid] : 0u;
-    uint32_t incl = wave_incl_scan(h);
-    if (lane == 63 && wave < 4) L.wsum[wave] = incl;
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < wave; ++w) incl += L.wsum[w];
-      const uint32_t above = incl - h;
-      if (above < (uint32_t)rho && incl >= (uint32_t)rho) {
-        const int r2 = rho - (int)above;
-        L.prefix = prefix | ((uint64_t)(255 - tid) << shift);
-        L.rho = r2;
-        L.done = (int)h == r2;
-      }
-    }
-    __syncthreads();
-    prefix = L.prefix;
-    rho = L.rho;
-    const int done = L.done;
-    if (done) break;
-  }
-  // (distinct composites end the loop by the last digit at the latest)
-  out_prefix = prefix;
-  out_shift = max(shift, 0);
-}
-
-__device__ __forceinline__ bool selected(uint64_t c, uint64_t prefix, int shift) {
-  return c != 0 && (c >> shift) >= (prefix >> shift);
+__device__ __forceinline__ bool selected(uint64_t c, uint64_t prefix, int hi) {
+  return c != 0 && shr_sat<uint64_t>(c, hi) >= shr_sat<uint64_t>(prefix, hi);
 }
 
 __device__ __forceinline__ int shard_count(int vis, int r, int W) {
@@ -114,64 +53,38 @@ __global__ __launch_bounds__(256) void shard_vis_kernel(MergeParams p) {
   p.lvis[i] = shard_count(clamp_vis(p, t), r, p.W);
 }
 
-// One workgroup per shard row (r, t): its local top-k (ascending local
-// positions) -> composites; round 1 sends the cand best of them, round 2 (only
-// for flagged shard rows) sends them all.
+// One workgroup per shard row (r, t): the shard's selected local positions
+// (ascending, `kk` per row: cand in round 1, k in round 2) -> composites in
+// the exchange buffer.  Round 2 packs only the flagged shard rows.
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(MergeParams p, int round) {
-  __shared__ SelLds L;
-  __shared__ int s_slot;
   const int sr = blockIdx.x;  // r * T + t
   const int r = sr / p.T, t = sr - r * p.T;
   const int tid = threadIdx.x;
   if (round == 2 && p.flags[t * p.W + r] == 0) return;
-  const int m = min(p.k, p.lvis[sr]);
-  const int32_t* lidx = p.lidx + (int64_t)sr * p.k;
+  const int kk = round == 1 ? p.cand : p.k;
+  const int m = min(kk, round == 1 ? p.lvis[sr] : p.lvis2[sr]);
+  const int32_t* lidx = p.lidx + (int64_t)sr * kk;
   const float* row = p.scores + (int64_t)sr * p.ld;
-  uint64_t c[kPackPer];
-#pragma unroll
-  for (int i = 0; i < kPackPer; ++i) {
-    const int e = tid + kPackThreads * i;
-    c[i] = 0;
-    if (e < m) {
-      const int j = lidx[e];
-      const uint32_t g = (uint32_t)j * (uint32_t)p.W + (uint32_t)r;
-      c[i] = ((uint64_t)order_key(row[j]) << 32) | (uint64_t)(~g);
-    }
-  }
   uint64_t* out = p.xbuf + (int64_t)sr * p.k;
-  const int send = round == 1 ? min(p.cand, m) : m;
-  if (send == m) {
-#pragma unroll
-    for (int i = 0; i < kPackPer; ++i) {
-      const int e = tid + kPackThreads * i;
-      if (e < m) out[e] = c[i];
-    }
-  } else {
-    uint64_t prefix;
-    int shift;
-    select_rank<kPackPer>(c, send, L, prefix, shift);
-    if (tid == 0) s_slot = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kPackPer; ++i) {
-      if (selected(c[i], prefix, shift)) {
-        const int slot = atomicAdd(&s_slot, 1);
-        if (slot < send) out[slot] = c[i];
-      }
-    }
+  for (int e = tid; e < m; e += kPackThreads) {
+    const int j = lidx[e];
+    const uint32_t g = (uint32_t)j * (uint32_t)p.W + (uint32_t)r;
+    out[e] = ((uint64_t)order_key(row[j]) << 32) | (uint64_t)(~g);
   }
-  if (tid == 0) p.xcnt[sr] = send;
+  if (tid == 0) p.xcnt[sr] = m;
 }
 
 // One workgroup per query row: select from the union of the shards' messages,
 // decide the re-sends (round 1), emit the ascending global indices.
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int round) {
-  __shared__ SelLds L;
+  __shared__ RadixLds<uint64_t, kMergeThreads> L;
   __shared__ int s_pre[kMaxShards + 1];
   __shared__ int s_sel[kMaxShards];
   __shared__ int s_any;
   __shared__ int s_slot;
-  __shared__ uint32_t s_out[DSA_MAX_TOPK];
+  __shared__ __align__(16) uint32_t s_out[DSA_MAX_TOPK];
+  __shared__ __align__(16) uint32_t s_out2[DSA_MAX_TOPK];
+  __shared__ uint64_t s_comp[kMergeLdsCap];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int W = p.W;
@@ -179,42 +92,52 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
   const int vis = clamp_vis(p, t);
   const int K = min(p.k, vis);
   int32_t* idx = p.idx + (int64_t)t * p.k;
+  if (tid < W) {
+    s_pre[tid + 1] = p.xcnt[tid * p.T + t];  // loads in parallel, summed below
+    s_sel[tid] = 0;
+  }
   if (tid == 0) {
-    int acc = 0;
-    for (int r = 0; r < W; ++r) {
-      s_pre[r] = acc;
-      acc += p.xcnt[r * p.T + t];
-      s_sel[r] = 0;
-    }
-    s_pre[W] = acc;
+    s_pre[0] = 0;
     s_any = 0;
     s_slot = 0;
   }
   __syncthreads();
+  if (tid == 0)
+    for (int r = 1; r <= W; ++r) s_pre[r] += s_pre[r - 1];
+  __syncthreads();
   const int ntot = s_pre[W];
 
-  uint64_t c[kMergePer];
-#pragma unroll
-  for (int i = 0; i < kMergePer; ++i) {
-    const int e = tid + kMergeThreads * i;
-    c[i] = 0;
-    if (e < ntot) {
-      int r = 0;
-      while (r + 1 < W && s_pre[r + 1] <= e) ++r;
-      c[i] = p.xbuf[(int64_t)(r * p.T + t) * p.k + (e - s_pre[r])];
-    }
+  // the union: staged in LDS when it fits, else read from the exchange buffer
+  // (L2-resident) on every pass
+  auto comp_at = [&](int e) {
+    int r = 0;
+    while (r + 1 < W && s_pre[r + 1] <= e) ++r;
+    return p.xbuf[(int64_t)(r * p.T + t) * p.k + (e - s_pre[r])];
+  };
+  const bool staged = ntot <= kMergeLdsCap;
+  if (staged) {
+    for (int e = tid; e < ntot; e += kMergeThreads) s_comp[e] = comp_at(e);
+    __syncthreads();
   }
+  auto each = [&](auto f) {
+    if (staged) {
+      for (int e = tid; e < ntot; e += kMergeThreads) f(s_comp[e]);
+    } else {
+      for (int e = tid; e < ntot; e += kMergeThreads) f(comp_at(e));
+    }
+  };
   uint64_t prefix = 0;
   int shift = 0;
-  if (K > 0 && ntot > K) select_rank<kMergePer>(c, K, L, prefix, shift);
+  if (K > 0 && ntot > K) {
+    int rho_eq;  // composites are distinct: the last digit is always taken whole
+    radix_kth<uint64_t, kMergeThreads>(each, K, L, prefix, shift, rho_eq);
+  }
   // (ntot <= K: every composite is selected; prefix 0 / shift 0 admits all)
 
-#pragma unroll
-  for (int i = 0; i < kMergePer; ++i) {
-    if (K > 0 && selected(c[i], prefix, shift)) {
-      const uint32_t g = ~(uint32_t)c[i];
-      atomicAdd(&s_sel[g % (uint32_t)W], 1);
-    }
+  if (K > 0) {
+    each([&](uint64_t c) {
+      if (selected(c, prefix, shift)) atomicAdd(&s_sel[(~(uint32_t)c) % (uint32_t)W], 1);
+    });
   }
   __syncthreads();
   if (round == 1 && tid < W) {
@@ -223,6 +146,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
     const int sent = s_pre[r + 1] - s_pre[r];
     const int flag = (K > 0 && s_sel[r] == sent && sent < min(p.k, n)) ? 1 : 0;
     p.flags[t * W + r] = flag;
+    p.lvis2[r * p.T + t] = flag ? n : 0;  // the shards that select their full local top-k
     if (flag) atomicOr(&s_any, 1);
   }
   __syncthreads();
@@ -231,35 +155,58 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
     if (s_any) return;  // emitted by round 2
   }
 
-  // ascending global indices: gather the winners, bitonic sort in LDS
-  int n2 = 1;
-  while (n2 < K) n2 <<= 1;
-  for (int j = tid; j < n2; j += kMergeThreads) s_out[j] = 0xFFFFFFFFu;
+  // ascending global indices: gather the winners into 2048 slots (padding
+  // 0xFFFFFFFF sorts last), then a bitonic sort with two slots per thread:
+  // partners within a wave exchange by lane shuffles, partners in other waves
+  // through LDS (two buffers used in turn, one barrier per such stage)
+  for (int j = tid; j < DSA_MAX_TOPK; j += kMergeThreads) s_out[j] = 0xFFFFFFFFu;
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kMergePer; ++i) {
-    if (K > 0 && selected(c[i], prefix, shift)) {
-      const int slot = atomicAdd(&s_slot, 1);
-      if (slot < n2) s_out[slot] = ~(uint32_t)c[i];
-    }
-  }
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (n2 >> 1); i += kMergeThreads) {
-        const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint32_t a = s_out[lo], b = s_out[hi];
-        if ((a > b) == up) {
-          s_out[lo] = b;
-          s_out[hi] = a;
-        }
+  if (K > 0) {
+    each([&](uint64_t c) {
+      if (selected(c, prefix, shift)) {
+        const int slot = atomicAdd(&s_slot, 1);
+        if (slot < DSA_MAX_TOPK) s_out[slot] = ~(uint32_t)c;
       }
-      __syncthreads();
+    });
+  }
+  __syncthreads();
+  const uint2 ab = reinterpret_cast<const uint2*>(s_out)[tid];  // slots 2*tid, 2*tid + 1
+  uint32_t a = ab.x, b = ab.y;
+  int cur = 1;
+#pragma unroll
+  for (int size = 2; size <= DSA_MAX_TOPK; size <<= 1) {
+    const bool up = ((2 * tid) & size) == 0;
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride == 1) {
+        if ((a > b) == up) {
+          const uint32_t x = a;
+          a = b;
+          b = x;
+        }
+        continue;
+      }
+      const int m = stride >> 1;  // partner thread tid ^ m holds the partner slots
+      uint32_t pa, pb;
+      if (m < 64) {
+        pa = lane_xor(a, m);
+        pb = lane_xor(b, m);
+      } else {
+        uint2* bp = reinterpret_cast<uint2*>(cur ? s_out2 : s_out);
+        bp[tid] = make_uint2(a, b);
+        __syncthreads();
+        const uint2 q = bp[tid ^ m];
+        pa = q.x;
+        pb = q.y;
+        cur ^= 1;
+      }
+      const bool keep_min = ((tid & m) == 0) == up;
+      a = keep_min ? min(a, pa) : max(a, pa);
+      b = keep_min ? min(b, pb) : max(b, pb);
     }
   }
-  for (int j = tid; j < p.k; j += kMergeThreads) idx[j] = j < K ? (int32_t)s_out[j] : -1;
+  if (2 * tid < p.k) idx[2 * tid] = 2 * tid < K ? (int32_t)a : -1;
+  if (2 * tid + 1 < p.k) idx[2 * tid + 1] = 2 * tid + 1 < K ? (int32_t)b : -1;
   if (p.count && tid == 0) p.count[t] = K;
 }
 
@@ -269,10 +216,21 @@ dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hi
   const int n = p.W * p.T;
   hipLaunchKernelGGL(shard_vis_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
-  dsa_status st = launch_topk(local, stream);
+  // round 1: every shard row selects its cand best positions
+  TopkParams l1 = local;
+  l1.tok_vis = p.lvis;
+  l1.k = p.cand;
+  dsa_status st = launch_topk(l1, stream);
   if (st != DSA_OK) return st;
   hipLaunchKernelGGL(pack_kernel, dim3(n), dim3(kPackThreads), 0, stream, p, 1);
   hipLaunchKernelGGL(merge_kernel, dim3(p.T), dim3(kMergeThreads), 0, stream, p, 1);
+  // round 2: flagged shard rows select their full local top-k (every other
+  // shard row has lvis2 = 0 and its workgroups return at once)
+  TopkParams l2 = local;
+  l2.tok_vis = p.lvis2;
+  l2.k = p.k;
+  st = launch_topk(l2, stream);
+  if (st != DSA_OK) return st;
   hipLaunchKernelGGL(pack_kernel, dim3(n), dim3(kPackThreads), 0, stream, p, 2);
   hipLaunchKernelGGL(merge_kernel, dim3(p.T), dim3(kMergeThreads), 0, stream, p, 2);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;

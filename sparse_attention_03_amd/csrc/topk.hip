@@ -30,6 +30,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "radix.h"
 
 namespace dsa {
 
@@ -983,6 +984,92 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
   if (p.count && tid == 0) p.count[t] = K;
 }
 
+// Rows up to kShortMax scores: one 256-thread workgroup per row holds the row
+// in registers (32 consecutive scores per thread), finds the K-th largest key
+// by an 8-bit radix select (early exit once the chosen bin is taken whole),
+// and emits the winners in index order: all keys above the threshold digit
+// prefix plus the first rho keys equal to it (lower indices first), placed by
+// one block scan of the per-thread counts.  Little LDS, so many rows share a
+// CU: this is the path for short rows (one 8K row, or many context-shard rows).
+constexpr int kShortMax = 8192;
+constexpr int kShortThreads = 256;
+constexpr int kShortPer = kShortMax / kShortThreads;  // 32, one run per thread
+
+__global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkParams p) {
+  __shared__ RadixLds<uint32_t, kShortThreads> L;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vis = row_vis(p, t);
+  const int K = min(p.k, vis);
+  const int r = p.tok_req ? p.tok_req[t] : 0;
+  int32_t* idx = p.idx + (int64_t)t * p.k;
+  int32_t* rows = p.rows ? p.rows + (int64_t)t * p.k : nullptr;
+  if (vis <= p.k) {
+    store_all(p, vis, t, r, idx, rows);
+    return;
+  }
+  // Loads: float4 q covers scores j0+4q .. j0+4q+3; it is issued only when its
+  // first score is visible, and then lies inside the row (ld and j0+4q are
+  // multiples of 4, j0+4q < vis <= ld).  Key 0 marks "no score" (no finite
+  // score has key 0).
+  const float* row = p.scores + (int64_t)t * p.ld;
+  const int j0 = tid * kShortPer;
+  uint32_t key[kShortPer];
+#pragma unroll
+  for (int q = 0; q < kShortPer / 4; ++q) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j0 + 4 * q < vis) x = *reinterpret_cast<const float4*>(row + j0 + 4 * q);
+    key[4 * q + 0] = j0 + 4 * q + 0 < vis ? order_key(x.x) : 0u;
+    key[4 * q + 1] = j0 + 4 * q + 1 < vis ? order_key(x.y) : 0u;
+    key[4 * q + 2] = j0 + 4 * q + 2 < vis ? order_key(x.z) : 0u;
+    key[4 * q + 3] = j0 + 4 * q + 3 < vis ? order_key(x.w) : 0u;
+  }
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int i = 0; i < kShortPer; ++i) f(key[i]);
+  };
+  uint32_t prefix;
+  int shift, rho;
+  radix_kth<uint32_t, kShortThreads>(each, K, L, prefix, shift, rho);
+  const uint32_t P = shr_sat<uint32_t>(prefix, shift);
+  uint32_t gt = 0, eq = 0;
+  each([&](uint32_t k) {
+    if (k != 0) {
+      gt += shr_sat<uint32_t>(k, shift) > P;
+      eq += shr_sat<uint32_t>(k, shift) == P;
+    }
+  });
+  // exclusive scan of (gt, eq) packed in 16-bit halves (each total <= 8192)
+  const uint32_t v = (gt << 16) | eq;
+  uint32_t inc = wave_scan_incl(v);
+  if (lane == 63) L.wsum[wave] = inc;  // (the selection read wsum before its final barrier)
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) inc += L.wsum[w];
+  const uint32_t ex = inc - v;
+  const int eq_before = (int)(ex & 0xFFFFu);
+  int pos = (int)(ex >> 16) + min(eq_before, rho);
+  int eqi = eq_before;
+#pragma unroll
+  for (int i = 0; i < kShortPer; ++i) {
+    if (key[i] != 0) {
+      const uint32_t kk = shr_sat<uint32_t>(key[i], shift);
+      const bool take = kk > P || (kk == P && eqi < rho);
+      eqi += kk == P;
+      if (take) {
+        const int j = j0 + i;
+        idx[pos] = j;
+        if (rows) rows[pos] = translate_one(j, r, p.block_table, p.bt_stride, p.plog2);
+        ++pos;
+      }
+    }
+  }
+  for (int j = K + tid; j < p.k; j += kShortThreads) {
+    idx[j] = -1;
+    if (rows) rows[j] = -1;
+  }
+  if (p.count && tid == 0) p.count[t] = K;
+}
+
 __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, const int32_t* __restrict__ tok_req,
                                  const int32_t* __restrict__ bt, int bt_stride, int plog2, int32_t* __restrict__ rows) {
   const int64_t n = (int64_t)T * k;
@@ -993,6 +1080,10 @@ __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, 
 }
 
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
+  if (p.max_vis <= kShortMax) {
+    hipLaunchKernelGGL(topk_short_kernel, dim3(p.T), dim3(kShortThreads), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+  }
   if (p.max_vis <= kRowMax) {
     hipLaunchKernelGGL(topk_row_kernel, dim3(p.T), dim3(1024), 0, stream, p);
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
