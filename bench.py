@@ -258,11 +258,18 @@ def main():
         for _ in range(3):
             st_op()
         torch.cuda.synchronize()
+        # (queued behind a backlog of steps, as the front end: a call's seven or
+        # more launches can take the host longer than the GPU)
+        n_busy = max(1, int(2.0 * K * 150e-3 / ms_step) + 1)
         s0, s1 = E(enable_timing=True), E(enable_timing=True)
+        for _ in range(n_busy):
+            step()
+        h0 = time.perf_counter()
         s0.record()
         for _ in range(K):
             st_op()
         s1.record()
+        sh_host_ms = (time.perf_counter() - h0) * 1e3
         torch.cuda.synchronize()
         sh_ms = s0.elapsed_time(s1) / K
         same = bool(torch.equal(st_op.idx, step.idx))
@@ -274,7 +281,8 @@ def main():
         generic = sum(min(spec.k, n) for row in n_loc for n in row)
         shard = {"shards": W, "cand": cand, "us": round(sh_ms * 1e3, 2), "unsharded_topk_us": round(st["topk"] * 1e3, 2),
                  "equals_unsharded": same, "rows_resent": int((resent.sum(axis=1) > 0).sum()),
-                 "exchange_bytes": 8 * sent, "generic_exchange_bytes": 8 * generic}
+                 "exchange_bytes": 8 * sent, "generic_exchange_bytes": 8 * generic,
+                 "gpu_bound_timing": sh_host_ms < n_busy * ms_step}
         del local, st_op
 
     cpu = None

@@ -994,6 +994,7 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
 constexpr int kShortMax = 8192;
 constexpr int kShortThreads = 256;
 constexpr int kShortPer = kShortMax / kShortThreads;  // 32, one run per thread
+constexpr int kShortMinRows = 512;                     // rows to fill the device twice over
 
 __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkParams p) {
   __shared__ RadixLds<uint32_t, kShortThreads> L;
@@ -1080,7 +1081,8 @@ __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, 
 }
 
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
-  if (p.max_vis <= kShortMax) {
+  // (few short rows: the 1024-thread row kernel has the shorter per-row latency)
+  if (p.max_vis <= kShortMax && p.T >= kShortMinRows) {
     hipLaunchKernelGGL(topk_short_kernel, dim3(p.T), dim3(kShortThreads), 0, stream, p);
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
   }

@@ -196,6 +196,39 @@ def test_topk_exact_on_same_scores(kind, ld, gpu):
         assert np.all(idx[t, K:] == -1)
 
 
+@pytest.mark.parametrize("kind", ["random", "ties", "all_equal", "negative", "binade"])
+@pytest.mark.parametrize("k", [2048, 384, 1])
+def test_topk_many_short_rows(kind, k, gpu):
+    """>= 512 rows of <= 8192 scores: the one-workgroup short-row kernel (keys
+    in registers), against the oracle row by row; ragged lengths, rows that
+    keep everything, ties, +-0, and scores of one binade (shared leading
+    digits)."""
+    print(f"[gpu] topk short rows {kind} k={k}", flush=True)
+    g = np.random.default_rng(7 + k)
+    T, ld = 600, 8192
+    if kind == "random":
+        s = g.standard_normal((T, ld)).astype(np.float32)
+    elif kind == "ties":
+        s = g.integers(0, 40, (T, ld)).astype(np.float32)
+    elif kind == "all_equal":
+        s = np.full((T, ld), -2.25, np.float32)
+    elif kind == "negative":
+        s = -np.abs(g.standard_normal((T, ld)).astype(np.float32))
+        s[:, ::5] = 0.0
+        s[:, 2::5] = -0.0
+    else:
+        s = (1.0 + g.random((T, ld))).astype(np.float32)
+    vis = g.integers(1, ld + 1, T)
+    vis[:8] = [ld, ld - 1, k, k + 1, max(1, k - 1), 1, 4097, 33]
+    idx, cnt = _topk_alone(torch.from_numpy(s), vis.tolist(), k, gpu)
+    for t in range(T):
+        ref, _ = O.topk(s[t, : vis[t]].astype(np.float64), k)
+        K = len(ref)
+        assert cnt[t] == K
+        assert np.array_equal(idx[t, :K], ref), f"{kind} row {t}"
+        assert np.all(idx[t, K:] == -1)
+
+
 def test_topk_candidate_overflow_path(gpu):
     # > 8192 scores share the threshold bin: the finalize pass rescans the row
     g = np.random.default_rng(3)
