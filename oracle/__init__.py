@@ -11,4 +11,4 @@ every function here is pinned by closed forms, invariants, library routines or
 brute force on tiny inputs; the absolute values on random inputs are fixed only
 through those pins (the pages print no worked DSA example).
 """
-from . import codecs, dsa, merge, quant  # noqa: F401
+from . import codecs, dsa, merge, msa, quant  # noqa: F401
