@@ -89,7 +89,7 @@ enum { DSA_Q_BF16 = 1, DSA_Q_FP8 = 2, DSA_Q_MXFP4 = 3 };
 
 /* Operation ids for dsa_workspace_size(). */
 enum { DSA_OP_INDEXER = 1, DSA_OP_TOPK = 2, DSA_OP_MLA_DECODE = 3, DSA_OP_MLA_PREFILL = 4,
-       DSA_OP_TOPK_SHARDED = 5 };
+       DSA_OP_TOPK_SHARDED = 5, DSA_OP_MSA_DECODE = 6 };
 
 /* One paged pool (index keys or latents) of one layer. */
 typedef struct dsa_cache {
@@ -298,6 +298,50 @@ typedef struct dsa_insert_args {
   dsa_cache latents;             /* fmt DSA_LAT_*; same page size as keys       */
 } dsa_insert_args;
 dsa_status dsa_cache_insert(const dsa_insert_args* args, hipStream_t stream);
+
+/* dsa_msa_decode -- the MSA block-sparse variant (MiniMax M3.1 page, "MSA
+ * primer"), one decode step over a paged cache of 128-token blocks.
+ * For row t (request r = tok_req[t], visible tokens 0 .. tok_vis[t]-1) and
+ * group g < Hkv:
+ *   score(g, s)  = q_idx[t,g,:] . k_s        (k_s: the token's 128 E4M3 index
+ *                                              values, unscaled; exact products,
+ *                                              fp32 accumulation)
+ *   block b      = max of score over its visible tokens
+ *   sel[t,g,:]   = the most recent block plus the top_blocks-1 best other
+ *                  blocks (ties to the lower id), ascending, -1 padded; every
+ *                  block when there are at most top_blocks
+ *   out[t,h,:]   = softmax_s(sm_scale * q[t,h,:] . K_g(s)) weighted sum of
+ *                  V_g(s) over the visible tokens of the selected blocks, for
+ *                  every head h of group g = h / (Hq/Hkv); lse[t,h] in nats.
+ * K_g(s) / V_g(s) = k_scale / v_scale x the E4M3 values of head g.
+ * Layouts (device, 16-byte aligned): index_keys [num_blocks][128][128] bytes;
+ * kv [num_blocks][128][2][Hkv][128] bytes (per token: K of every head, then
+ * V); batch.block_table [R, bt_stride] maps logical block b of request r to a
+ * pool block (entries < 0 or >= num_blocks: absent, their tokens score -inf
+ * and are never attended); q_idx bf16 [T, Hkv, 128]; q bf16 [T, Hq, 128].
+ * Errors: DSA_ERR_INVALID_ARG for Hkv outside [1, 8], Hq not a multiple of
+ * Hkv or Hq/Hkv > 16, top_blocks outside [1, 16], a bad batch, null or
+ * unaligned pointers; DSA_ERR_WORKSPACE below dsa_workspace_size(
+ * DSA_OP_MSA_DECODE, args) (the block scores, 4 * T * Hkv * ceil(max_vis/128)
+ * bytes). */
+typedef struct dsa_msa_args {
+  dsa_batch batch;               /* rows by request; block_table of 128-token blocks */
+  const void* index_keys;        /* device E4M3 [num_blocks, 128, 128]          */
+  const void* kv;                /* device E4M3 [num_blocks, 128, 2, Hkv, 128]  */
+  int32_t num_blocks;            /* blocks in both pools                        */
+  int32_t num_kv_heads;          /* Hkv = GQA groups, 1 .. 8                    */
+  int32_t num_q_heads;           /* Hq, multiple of Hkv, Hq / Hkv <= 16         */
+  int32_t top_blocks;            /* 1 .. 16                                     */
+  const void* q_idx;             /* device bf16 [T, Hkv, 128]                   */
+  const void* q;                 /* device bf16 [T, Hq, 128]                    */
+  float k_scale, v_scale, sm_scale;
+  int32_t* sel_blocks;           /* device int32 [T, Hkv, top_blocks]           */
+  float* out;                    /* device fp32 [T, Hq, 128]                    */
+  float* lse;                    /* device fp32 [T, Hq] or NULL                 */
+  void* workspace;               /* device, 256-byte aligned                    */
+  size_t workspace_bytes;
+} dsa_msa_args;
+dsa_status dsa_msa_decode(const dsa_msa_args* args, hipStream_t stream);
 
 /* Workspace bytes an operation needs for these arguments (0 if none, or if
  * the arguments are invalid).  `args` points to the op's argument struct. */

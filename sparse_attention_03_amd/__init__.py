@@ -26,7 +26,7 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 KEY_FP8, KEY_MXFP4 = 1, 2
 LAT_BF16, LAT_FP8, LAT_NVFP4 = 1, 2, 3
 Q_BF16, Q_FP8, Q_MXFP4 = 1, 2, 3
-OP_INDEXER, OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_TOPK_SHARDED = 1, 2, 3, 4, 5
+OP_INDEXER, OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_TOPK_SHARDED, OP_MSA_DECODE = 1, 2, 3, 4, 5, 6
 
 KEY_FMT = {"fp8": KEY_FP8, "mxfp4": KEY_MXFP4}
 LAT_FMT = {"bf16": LAT_BF16, "fp8": LAT_FP8, "nvfp4": LAT_NVFP4}
@@ -37,7 +37,8 @@ LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per l
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
            "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
-           "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded")
+           "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded",
+           "dsa_msa_decode")
 
 
 class DsaError(RuntimeError):
@@ -79,6 +80,15 @@ class TopkShardedArgs(ctypes.Structure):
                 ("k", ctypes.c_int32), ("cand", ctypes.c_int32), ("idx", ctypes.c_void_p),
                 ("count", ctypes.c_void_p), ("resend", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t)]
+
+
+class MsaArgs(ctypes.Structure):
+    _fields_ = [("batch", Batch), ("index_keys", ctypes.c_void_p), ("kv", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("top_blocks", ctypes.c_int32), ("q_idx", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("sm_scale", ctypes.c_float),
+                ("sel_blocks", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class MlaArgs(ctypes.Structure):
@@ -123,7 +133,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        ("dsa_translate_pages", [vp, i32, ctypes.POINTER(Batch), i32, vp, vp]),
                        ("dsa_quantize_q", [ctypes.POINTER(QuantQArgs), vp]),
                        ("dsa_cache_insert", [ctypes.POINTER(InsertArgs), vp]),
-                       ("dsa_topk_sharded", [ctypes.POINTER(TopkShardedArgs), vp])):
+                       ("dsa_topk_sharded", [ctypes.POINTER(TopkShardedArgs), vp]),
+                       ("dsa_msa_decode", [ctypes.POINTER(MsaArgs), vp])):
         f = getattr(lib, name)
         f.argtypes = argt
         f.restype = ctypes.c_int
@@ -210,6 +221,10 @@ def dsa_cache_insert(args: InsertArgs, stream=None):
 
 def dsa_topk_sharded(args: TopkShardedArgs, stream=None):
     _check(load().dsa_topk_sharded(ctypes.byref(args), _stream(stream)), "dsa_topk_sharded")
+
+
+def dsa_msa_decode(args: MsaArgs, stream=None):
+    _check(load().dsa_msa_decode(ctypes.byref(args), _stream(stream)), "dsa_msa_decode")
 
 
 def dsa_workspace_size(op: int, args) -> int:
@@ -315,6 +330,38 @@ def topk_sharded(scores: torch.Tensor, tok_vis: torch.Tensor, max_vis: int, k: i
     """One call of dsa_topk_sharded into new tensors: (idx [T,k], count [T],
     resend flags [T,W])."""
     return ShardedTopk(scores, tok_vis, max_vis, k, cand)(stream)
+
+
+class MsaDecode:
+    """The MSA block-sparse decode step (dsa_msa_decode) over fixed buffers.
+    idx_pool uint8 [blocks, 128*128]; kv_pool uint8 [blocks, 128*2*Hkv*128];
+    block_table int32 [R, nblk]; q_idx bf16 [T, Hkv, 128]; q bf16 [T, Hq, 128]."""
+
+    def __init__(self, *, req_row_start, tok_req, tok_vis, block_table, idx_pool, kv_pool, q_idx, q,
+                 max_vis: int, max_rows_per_req: int, top_blocks: int = 16, k_scale: float = 1.0,
+                 v_scale: float = 1.0, sm_scale: Optional[float] = None):
+        dev = q.device
+        T, hq, _ = q.shape
+        hkv = int(q_idx.shape[1])
+        for t in (idx_pool, kv_pool, q_idx, q):
+            assert t.is_contiguous()
+        self.batch = batch_view(req_row_start, tok_req, tok_vis, block_table, max_vis, max_rows_per_req)
+        self.sel = torch.empty(T, hkv, top_blocks, dtype=torch.int32, device=dev)
+        self.out = torch.empty(T, hq, 128, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(T, hq, dtype=torch.float32, device=dev)
+        sm = 1.0 / 128 ** 0.5 if sm_scale is None else sm_scale
+        self.args = MsaArgs(self.batch, idx_pool.data_ptr(), kv_pool.data_ptr(), int(idx_pool.shape[0]), hkv,
+                            int(hq), int(top_blocks), q_idx.data_ptr(), q.data_ptr(), float(k_scale),
+                            float(v_scale), float(sm), self.sel.data_ptr(), self.out.data_ptr(),
+                            self.lse.data_ptr(), None, 0)
+        self.ws = workspace(dsa_workspace_size(OP_MSA_DECODE, self.args), dev)
+        self.args.workspace = _ptr(self.ws)
+        self.args.workspace_bytes = 0 if self.ws is None else self.ws.numel()
+        self._keep = (req_row_start, tok_req, tok_vis, block_table, idx_pool, kv_pool, q_idx, q)
+
+    def __call__(self, stream=None):
+        dsa_msa_decode(self.args, stream)
+        return self.sel, self.out, self.lse
 
 
 class DecodeStep:

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.cpp", "indexer.hip", "indexer_fp8.hip", "topk.hip", "mla.hip", "quant.hip", "merge.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "indexer_fp8.hip", "topk.hip", "mla.hip", "quant.hip", "merge.hip", "msa.hip"]
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

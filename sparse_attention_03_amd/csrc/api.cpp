@@ -402,6 +402,61 @@ dsa_status dsa_topk_sharded(const dsa_topk_sharded_args* a, hipStream_t stream) 
   return DSA_OK;
 }
 
+dsa_status dsa_msa_decode(const dsa_msa_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "msa: null args");
+  const dsa_batch& b = a->batch;
+  if (a->num_kv_heads < 1 || a->num_kv_heads > 8) return fail(DSA_ERR_INVALID_ARG, "msa: Hkv %d outside [1, 8]", a->num_kv_heads);
+  if (a->num_q_heads < a->num_kv_heads || a->num_q_heads % a->num_kv_heads != 0 ||
+      a->num_q_heads / a->num_kv_heads > 16)
+    return fail(DSA_ERR_INVALID_ARG, "msa: Hq %d must be a multiple of Hkv %d with at most 16 per group",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->top_blocks < 1 || a->top_blocks > 16) return fail(DSA_ERR_INVALID_ARG, "msa: top_blocks %d", a->top_blocks);
+  if (!b.block_table) return fail(DSA_ERR_INVALID_ARG, "msa: a block table is required");
+  dsa_status st = check_batch(b, 7, true);
+  if (st != DSA_OK) return st;
+  if (!b.tok_req) return fail(DSA_ERR_INVALID_ARG, "msa: tok_req is null");
+  if (a->num_blocks < 1) return fail(DSA_ERR_INVALID_ARG, "msa: num_blocks < 1");
+  if (!a->index_keys || !aligned(a->index_keys, 16) || !a->kv || !aligned(a->kv, 16) || !a->q_idx ||
+      !aligned(a->q_idx, 16) || !a->q || !aligned(a->q, 16) || !a->sel_blocks || !a->out)
+    return fail(DSA_ERR_INVALID_ARG, "msa: null or unaligned pointer");
+  if (b.num_rows > 65535 * 64 / 8) return fail(DSA_ERR_INVALID_ARG, "msa: too many rows");
+  const int nblk = (b.max_vis + 127) / 128;
+  const size_t need = align_up((size_t)b.num_rows * a->num_kv_heads * nblk * 4, 256);
+  if (!a->workspace || !aligned(a->workspace, 256))
+    return fail(DSA_ERR_WORKSPACE, "msa: workspace null or not 256-byte aligned (%zu bytes needed)", need);
+  if (a->workspace_bytes < need) return fail(DSA_ERR_WORKSPACE, "msa: workspace %zu bytes, %zu needed", a->workspace_bytes, need);
+  dsa::MsaParams p{};
+  p.R = b.num_requests;
+  p.T = b.num_rows;
+  p.hkv = a->num_kv_heads;
+  p.hq = a->num_q_heads;
+  p.G = a->num_q_heads / a->num_kv_heads;
+  p.top = a->top_blocks;
+  p.nblk_ld = nblk;
+  p.req_row_start = b.req_row_start;
+  p.tok_req = b.tok_req;
+  p.tok_vis = b.tok_vis;
+  p.max_vis = b.max_vis;
+  p.bt = b.block_table;
+  p.bt_stride = b.bt_stride;
+  p.pool_blocks = a->num_blocks;
+  p.idx_pool = static_cast<const uint8_t*>(a->index_keys);
+  p.kv_pool = static_cast<const uint8_t*>(a->kv);
+  p.q_idx = static_cast<const __bf16*>(a->q_idx);
+  p.q = static_cast<const __bf16*>(a->q);
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.sm_scale = a->sm_scale;
+  p.bscore = static_cast<float*>(a->workspace);
+  p.sel = a->sel_blocks;
+  p.out = a->out;
+  p.lse = a->lse;
+  st = dsa::launch_msa(p, nblk, stream);
+  if (st != DSA_OK) return fail(st, "msa: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DSA_OK;
+}
+
 dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* b, int32_t page_size_log2,
                                int32_t* rows, hipStream_t stream) {
   g_err[0] = 0;
@@ -510,6 +565,11 @@ size_t dsa_workspace_size(int32_t op, const void* args) {
       const dsa_topk_args* a = static_cast<const dsa_topk_args*>(args);
       if (a->k < 1 || a->k > DSA_MAX_TOPK || a->batch.num_rows < 1 || a->batch.max_vis < 1) return 0;
       return plan_topk(a->batch.num_rows, a->batch.max_vis, a->k).total;
+    }
+    case DSA_OP_MSA_DECODE: {
+      const dsa_msa_args* a = static_cast<const dsa_msa_args*>(args);
+      if (a->batch.num_rows < 1 || a->batch.max_vis < 1 || a->num_kv_heads < 1 || a->num_kv_heads > 8) return 0;
+      return align_up((size_t)a->batch.num_rows * a->num_kv_heads * ((a->batch.max_vis + 127) / 128) * 4, 256);
     }
     case DSA_OP_TOPK_SHARDED: {
       const dsa_topk_sharded_args* a = static_cast<const dsa_topk_sharded_args*>(args);

@@ -161,7 +161,28 @@ dsa_status launch_quantize_q(const QuantQParams& p, hipStream_t stream);
 dsa_status launch_cache_insert(const InsertParams& p, hipStream_t stream);
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream);
+struct MsaParams {
+  int R, T, hkv, hq, G, top, nblk_ld;
+  const int32_t* req_row_start;
+  const int32_t* tok_req;
+  const int32_t* tok_vis;
+  int max_vis;
+  const int32_t* bt;
+  int bt_stride;
+  int pool_blocks;
+  const uint8_t* idx_pool;  // [blocks][128 tokens][128] E4M3
+  const uint8_t* kv_pool;   // [blocks][128 tokens][2][hkv][128] E4M3
+  const __bf16* q_idx;      // [T][hkv][128]
+  const __bf16* q;          // [T][hq][128]
+  float k_scale, v_scale, sm_scale;
+  float* bscore;            // workspace [T][hkv][nblk_ld]
+  int32_t* sel;             // [T][hkv][top]
+  float* out;               // [T][hq][128]
+  float* lse;               // [T][hq] or null
+};
+
 dsa_status launch_topk(const TopkParams& p, hipStream_t stream);
+dsa_status launch_msa(const MsaParams& p, int nblk_max, hipStream_t stream);
 dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hipStream_t stream);
 dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req,
                             const int32_t* block_table, int bt_stride, int plog2, int32_t* rows,

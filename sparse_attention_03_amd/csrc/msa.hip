@@ -1,0 +1,297 @@
+// MSA block-sparse decode (MiniMax M3.1 page, "MSA primer"; its AMD section
+// for the FP8/NVFP4 caches): 128-token blocks, one index query per GQA group
+// scored against one shared FP8 index-key head, a max-pool to one score per
+// block, the top blocks (the most recent always kept), and exact attention of
+// every query head of a group over its group's selected blocks.
+//
+//   msa_index_kernel   one workgroup per (request, block): the block's 128
+//                      index keys are read once for every row and group of
+//                      the request; scores on v_mfma_f32_16x16x32_bf16 with
+//                      keys as M (FP8 -> BF16 is exact) and (row, group)
+//                      queries as N; the block maximum over visible keys.
+//   msa_select_kernel  one workgroup per (row, group): the most recent block
+//                      plus the top - 1 best others, by a block radix select
+//                      over (score order key, inverted block id) composites;
+//                      ascending ids, -1 padded.
+//   msa_attn_kernel    one 8-wave workgroup per (row, group): each wave runs
+//                      its selected blocks in 16-key tiles -- S^T = K . Q^T
+//                      (keys x heads, so the softmax weights land where the
+//                      PV product wants its A operand), online softmax per
+//                      head, O += P . V with V staged as BF16 rows in LDS and
+//                      read transposed (ds_read_b64_tr_b16) -- then the waves'
+//                      partial results merge by log-sum-exp.
+#include "common.h"
+#include "kernels.h"
+#include "radix.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kBlk = 128;       // tokens per block
+constexpr int kD = 128;         // head dim
+constexpr int kAttnWaves = 8;
+constexpr int kVStride = 136;   // bf16 per LDS V row (272 B)
+
+__device__ __forceinline__ int msa_vis(const MsaParams& p, int t) { return min(max(p.tok_vis[t], 0), p.max_vis); }
+
+__device__ __forceinline__ int msa_page(const MsaParams& p, int r, int b) {
+  if (b < 0 || b >= p.bt_stride) return -1;
+  const int pg = p.bt[(int64_t)r * p.bt_stride + b];
+  return (pg >= 0 && pg < p.pool_blocks) ? pg : -1;
+}
+
+__global__ __launch_bounds__(256) void msa_index_kernel(MsaParams p) {
+  __shared__ float red[4][16];
+  const int b = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+  const int rs = p.req_row_start[r], nrows = p.req_row_start[r + 1] - rs;
+  int vmax = 0;
+  for (int i = 0; i < nrows; ++i) vmax = max(vmax, msa_vis(p, rs + i));
+  if (b * kBlk >= vmax) return;
+  const int page = msa_page(p, r, b);
+  const int nq = nrows * p.hkv;
+  // A fragments: keys 32w + 16mt + c, dims 32ks + 8g .. +8 (exact FP8 -> BF16)
+  bf16x8 A[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint2 v = make_uint2(0u, 0u);
+      if (page >= 0)
+        v = *reinterpret_cast<const uint2*>(p.idx_pool + (int64_t)page * (kBlk * kD) +
+                                            (32 * w + 16 * mt + c) * kD + 32 * ks + 8 * g);
+      A[mt][ks] = e4m3x8_to_bf16x8(v.x, v.y);
+    }
+  }
+  for (int q0 = 0; q0 < nq; q0 += 16) {
+    const int qq = q0 + c;  // this lane's query column
+    const bool qok = qq < nq;
+    const int row = rs + (qok ? qq / p.hkv : 0), grp = qok ? qq % p.hkv : 0;
+    const int vis = qok ? msa_vis(p, row) : 0;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 bq = {};
+      if (qok) bq = *reinterpret_cast<const bf16x8*>(p.q_idx + ((int64_t)row * p.hkv + grp) * kD + 32 * ks + 8 * g);
+      acc[0] = mfma16x16x32(A[0][ks], bq, acc[0]);
+      acc[1] = mfma16x16x32(A[1][ks], bq, acc[1]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = b * kBlk + 32 * w + 16 * mt + 4 * g + i;
+        if (page >= 0 && j < vis) mx = fmaxf(mx, acc[mt][i]);
+      }
+    mx = fmaxf(mx, __uint_as_float(lane_xor(__float_as_uint(mx), 16)));
+    mx = fmaxf(mx, __uint_as_float(lane_xor(__float_as_uint(mx), 32)));
+    if (lane < 16) red[w][lane] = mx;
+    __syncthreads();
+    if (tid < 16 && qok && b * kBlk < vis) {
+      const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+      p.bscore[((int64_t)row * p.hkv + grp) * p.nblk_ld + b] = m;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void msa_select_kernel(MsaParams p) {
+  __shared__ RadixLds<uint64_t, 256> L;
+  __shared__ int s_sel[16];
+  __shared__ int s_n;
+  const int tg = blockIdx.x, t = tg / p.hkv;
+  const int tid = threadIdx.x;
+  const int vis = msa_vis(p, t);
+  const int nb = (vis + kBlk - 1) / kBlk;
+  int32_t* out = p.sel + (int64_t)tg * p.top;
+  if (p.top == 1 && nb > 1) {  // only the most recent block
+    if (tid == 0) out[0] = nb - 1;
+    return;
+  }
+  if (nb <= p.top) {
+    for (int j = tid; j < p.top; j += 256) out[j] = j < nb ? j : -1;
+    return;
+  }
+  const float* bs = p.bscore + (int64_t)tg * p.nblk_ld;
+  const int nother = nb - 1;
+  auto each = [&](auto f) {
+    for (int b = tid; b < nother; b += 256) f(((uint64_t)order_key(bs[b]) << 32) | (uint64_t)(~(uint32_t)b));
+  };
+  uint64_t prefix;
+  int hi, rho;
+  radix_kth<uint64_t, 256>(each, p.top - 1, L, prefix, hi, rho);
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  each([&](uint64_t cc) {
+    if (shr_sat<uint64_t>(cc, hi) >= shr_sat<uint64_t>(prefix, hi)) {
+      const int slot = atomicAdd(&s_n, 1);
+      if (slot < 15) s_sel[slot] = (int)(~(uint32_t)cc);
+    }
+  });
+  __syncthreads();
+  if (tid == 0) {
+    int n = min(s_n, p.top - 1);
+    s_sel[n++] = nb - 1;
+    for (int i = 1; i < n; ++i) {  // insertion sort of at most 16 ids
+      const int v = s_sel[i];
+      int j = i - 1;
+      while (j >= 0 && s_sel[j] > v) {
+        s_sel[j + 1] = s_sel[j];
+        --j;
+      }
+      s_sel[j + 1] = v;
+    }
+    for (int j = 0; j < p.top; ++j) out[j] = j < n ? s_sel[j] : -1;
+  }
+}
+
+__global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) {
+  __shared__ __align__(16) __bf16 vt[kAttnWaves][16 * kVStride];
+  __shared__ float pm[kAttnWaves][16], pl[kAttnWaves][16];
+  __shared__ float po[kAttnWaves][16][kD];
+  const int tg = blockIdx.x, t = tg / p.hkv, grp = tg - t * p.hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+  const int r = p.tok_req[t];
+  const int vis = msa_vis(p, t);
+  const int hbase = grp * p.G;
+  const float lscale = p.sm_scale * p.k_scale;
+  const int64_t tok_bytes = 2LL * p.hkv * kD;
+  const int64_t page_bytes = (int64_t)kBlk * tok_bytes;
+  // Q^T fragments: head c of the group, dims 32ks + 8g .. +8 (zero past G)
+  bf16x8 bq[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bq[ks] = bf16x8{};
+    if (c < p.G) bq[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((int64_t)t * p.hq + hbase + c) * kD + 32 * ks + 8 * g);
+  }
+  f32x4 O[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) O[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_c = -INFINITY, l_c = 0.f;  // running max / sum of head c
+  __bf16* vrow = vt[w];
+  const __bf16* vsrc = vrow + (4 * g + (c >> 2)) * kVStride + 4 * (c & 3);
+  for (int sj = w; sj < p.top; sj += kAttnWaves) {
+    const int blk = p.sel[(int64_t)tg * p.top + sj];
+    if (blk < 0) continue;
+    const int page = msa_page(p, r, blk);
+    if (page < 0) continue;
+    const uint8_t* base = p.kv_pool + (int64_t)page * page_bytes + grp * kD;
+    for (int tile = 0; tile < kBlk / 16; ++tile) {
+      const int key0 = blk * kBlk + 16 * tile;
+      if (key0 >= vis) break;
+      // S^T[key 4g+i][head c] over the tile's 16 keys
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = base + (int64_t)(16 * tile + c) * tok_bytes;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint2 kv = *reinterpret_cast<const uint2*>(krow + 32 * ks + 8 * g);
+        s = mfma16x16x32(e4m3x8_to_bf16x8(kv.x, kv.y), bq[ks], s);
+      }
+      // V rows of the tile -> BF16 in LDS (zero rows past vis)
+      {
+        const bool vok = key0 + c < vis;
+        const uint4* vp = reinterpret_cast<const uint4*>(krow + p.hkv * kD + 32 * g);
+        uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+        if (vok) {
+          v0 = vp[0];
+          v1 = vp[1];
+        }
+        bf16x8* dst = reinterpret_cast<bf16x8*>(vrow + c * kVStride + 32 * g);
+        dst[0] = e4m3x8_to_bf16x8(v0.x, v0.y);
+        dst[1] = e4m3x8_to_bf16x8(v0.z, v0.w);
+        dst[2] = e4m3x8_to_bf16x8(v1.x, v1.y);
+        dst[3] = e4m3x8_to_bf16x8(v1.z, v1.w);
+      }
+      float x[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = key0 + 4 * g + i < vis;
+        x[i] = ok ? s[i] * lscale : -INFINITY;
+        tmax = fmaxf(tmax, x[i]);
+      }
+      tmax = fmaxf(tmax, __uint_as_float(lane_xor(__float_as_uint(tmax), 16)));
+      tmax = fmaxf(tmax, __uint_as_float(lane_xor(__float_as_uint(tmax), 32)));
+      const float m_new = fmaxf(m_c, tmax);  // finite: key0 < vis
+      const float alpha = __expf(m_c - m_new);
+      float pv[4], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = __expf(x[i] - m_new);
+        ps += pv[i];
+      }
+      ps += __uint_as_float(lane_xor(__float_as_uint(ps), 16));
+      ps += __uint_as_float(lane_xor(__float_as_uint(ps), 32));
+      l_c = l_c * alpha + ps;
+      m_c = m_new;
+      // rescale the output rows (heads 4g+i): alpha of head h sits in lane h
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[u][i] *= ar[i];
+      bf16x4 pa;
+      pa[0] = (__bf16)pv[0];
+      pa[1] = (__bf16)pv[1];
+      pa[2] = (__bf16)pv[2];
+      pa[3] = (__bf16)pv[3];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const auto* src = (const __attribute__((address_space(3))) s16x4*)(const void*)(vsrc + 16 * u);
+        const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<__attribute__((address_space(3))) s16x4*>(src));
+        O[u] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, vb), O[u]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  // the wave's partial result
+  if (g == 0) {
+    pm[w][c] = m_c;
+    pl[w][c] = l_c;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) po[w][4 * g + i][16 * u + c] = O[u][i];
+  __syncthreads();
+  for (int e = tid; e < 16 * kD; e += 64 * kAttnWaves) {
+    const int h = e / kD, d = e - h * kD;
+    if (h >= p.G) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, pm[v][h]);
+    float Lsum = 0.f, acc = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < kAttnWaves; ++v) {
+        const float e_v = pm[v][h] > -INFINITY ? __expf(pm[v][h] - M) : 0.f;
+        Lsum += e_v * pl[v][h];
+        acc += e_v * po[v][h][d];
+      }
+    }
+    const int64_t oh = (int64_t)t * p.hq + hbase + h;
+    p.out[oh * kD + d] = Lsum > 0.f ? p.v_scale * acc / Lsum : 0.f;
+    if (d == 0 && p.lse) p.lse[oh] = Lsum > 0.f ? M + __logf(Lsum) : -INFINITY;
+  }
+}
+
+}  // namespace
+
+dsa_status launch_msa(const MsaParams& p, int nblk_max, hipStream_t stream) {
+  hipLaunchKernelGGL(msa_index_kernel, dim3(nblk_max, p.R), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(msa_select_kernel, dim3(p.T * p.hkv), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(msa_attn_kernel, dim3(p.T * p.hkv), dim3(64 * kAttnWaves), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+}  // namespace dsa

@@ -47,7 +47,9 @@ MSA_CONFIGS = {
 
 
 def make_inputs(spec: MsaSpec, device="cpu") -> dict:
-    """Tensors on `device` (codes uint8, queries bf16, indices int32)."""
+    """Tensors on `device` (codes uint8, queries bf16, indices int32).  The
+    pools are drawn in chunks of blocks on `device` (seed, chunk) so that a
+    full-size cache never exists in fp32."""
     g = torch.Generator(device="cpu")
     g.manual_seed(spec.seed)
     R, rows, N, hkv, hq = spec.R, spec.rows, spec.N, spec.hkv, spec.hq
@@ -59,28 +61,40 @@ def make_inputs(spec: MsaSpec, device="cpu") -> dict:
     tok_req = torch.arange(R, dtype=torch.int32).repeat_interleave(rows)
     tok_vis = torch.tensor([N - rows + 1 + j for _ in range(R) for j in range(rows)], dtype=torch.int32)
     req_row_start = torch.arange(0, T + 1, rows, dtype=torch.int32)
-    q_idx = torch.randn(T, hkv, DIM, generator=g)
-    q = torch.randn(T, hq, DIM, generator=g)
-    idx_vals = torch.randn(pool_blocks * BLOCK, DIM, generator=g)
+    q_idx = codecs.bf16_bits(torch.randn(T, hkv, DIM, generator=g))
+    q = codecs.bf16_bits(torch.randn(T, hq, DIM, generator=g))
+    idx_pool = torch.empty(pool_blocks, BLOCK * DIM, dtype=torch.uint8, device=device)
+    kv_pool = torch.empty(pool_blocks, BLOCK * 2 * hkv * DIM, dtype=torch.uint8, device=device)
+    gd = torch.Generator(device=device)
+    chunk = 256
+    for i, b0 in enumerate(range(0, pool_blocks, chunk)):
+        b1 = min(pool_blocks, b0 + chunk)
+        gd.manual_seed(spec.seed * 1000 + i)
+        iv = torch.randn((b1 - b0) * BLOCK, DIM, generator=gd, device=device)
+        idx_pool[b0:b1] = codecs.e4m3_encode(iv).view(b1 - b0, BLOCK * DIM)
+        kv = torch.randn((b1 - b0) * BLOCK, 2 * hkv * DIM, generator=gd, device=device) * 2.0
+        kv_pool[b0:b1] = codecs.e4m3_encode(kv).view(b1 - b0, BLOCK * 2 * hkv * DIM)
     if spec.planted:
-        # one key per planted block along the group's index query (|q|-scaled,
-        # length 4 sqrt(128) before FP8 rounding): scores ~ 4 * 128 * |q|
+        # for every (row, group): one key in each of top_blocks - 1 random
+        # earlier blocks along the group's index query, length 4 sqrt(128)
+        # before FP8 rounding, so its score (~ 4 sqrt(128) |q|) dwarfs the rest
+        qf = q_idx.float()
         for t in range(T):
             r, vis = int(tok_req[t]), int(tok_vis[t])
             last = (vis - 1) // BLOCK
             for gg in range(hkv):
                 cand = torch.randperm(last, generator=g)[:spec.top_blocks - 1]
-                u = q_idx[t, gg] / q_idx[t, gg].norm()
-                for b in cand.tolist():
+                u = qf[t, gg] / qf[t, gg].norm()
+                code = codecs.e4m3_encode(4.0 * (DIM ** 0.5) * u).to(device)
+                for bb in cand.tolist():
                     slot = int(torch.randint(0, BLOCK, (1,), generator=g))
-                    tok = int(block_table[r, b]) * BLOCK + slot
-                    idx_vals[tok] = 4.0 * (DIM ** 0.5) * u
-    idx_pool = codecs.e4m3_encode(idx_vals).view(pool_blocks, BLOCK * DIM)
-    kv_vals = torch.randn(pool_blocks * BLOCK, 2, hkv, DIM, generator=g) * 2.0
-    kv_pool = codecs.e4m3_encode(kv_vals).view(pool_blocks, BLOCK * 2 * hkv * DIM)
+                    page = int(block_table[r, bb])
+                    idx_pool[page, slot * DIM:(slot + 1) * DIM] = code
     out = dict(block_table=block_table, tok_req=tok_req, tok_vis=tok_vis, req_row_start=req_row_start,
-               q_idx=codecs.bf16_bits(q_idx), q=codecs.bf16_bits(q), idx_pool=idx_pool, kv_pool=kv_pool)
-    return {k: v.to(device) for k, v in out.items()}
+               q_idx=q_idx, q=q)
+    out = {k: v.to(device) for k, v in out.items()}
+    out.update(idx_pool=idx_pool, kv_pool=kv_pool)
+    return out
 
 
 def oracle_view(inp: dict, spec: MsaSpec) -> dict:

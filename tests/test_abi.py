@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
               "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
-              "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded"):
+              "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded", "dsa_msa_decode"):
         assert n in names
 
 
@@ -39,7 +39,8 @@ def test_struct_layouts_match_the_c_compiler(tmp_path):
     """ctypes mirrors of the argument structs have the C compiler's layout."""
     structs = {"dsa_cache": dsa.Cache, "dsa_batch": dsa.Batch, "dsa_indexer_args": dsa.IndexerArgs,
                "dsa_topk_args": dsa.TopkArgs, "dsa_mla_args": dsa.MlaArgs, "dsa_quant_q_args": dsa.QuantQArgs,
-               "dsa_insert_args": dsa.InsertArgs, "dsa_topk_sharded_args": dsa.TopkShardedArgs}
+               "dsa_insert_args": dsa.InsertArgs, "dsa_topk_sharded_args": dsa.TopkShardedArgs,
+               "dsa_msa_args": dsa.MsaArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -156,6 +157,43 @@ def test_topk_sharded_workspace_size():
     assert n >= 8 * 4 * 2048 * 12
     assert dsa.dsa_workspace_size(dsa.OP_TOPK_SHARDED, _sharded_args(num_shards=17)) == 0
     assert dsa.dsa_workspace_size(dsa.OP_TOPK_SHARDED, _sharded_args(cand=3000)) == 0
+
+
+def _msa_args(**kw):
+    a = dict(batch=_batch(block_table=FAKE, bt_stride=1024, max_vis=131072), index_keys=FAKE, kv=FAKE,
+             num_blocks=1024, num_kv_heads=4, num_q_heads=64, top_blocks=16, q_idx=FAKE, q=FAKE, k_scale=1.0,
+             v_scale=1.0, sm_scale=0.088, sel_blocks=FAKE, out=FAKE, lse=None, workspace=FAKE,
+             workspace_bytes=1 << 40)
+    a.update(kw)
+    return dsa.MsaArgs(**a)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(num_kv_heads=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=9), dsa.DSA_ERR_INVALID_ARG),
+    (dict(num_q_heads=66), dsa.DSA_ERR_INVALID_ARG),       # not a multiple of Hkv
+    (dict(num_q_heads=68), dsa.DSA_ERR_INVALID_ARG),       # 17 per group
+    (dict(top_blocks=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(top_blocks=17), dsa.DSA_ERR_INVALID_ARG),
+    (dict(batch=_batch(block_table=None, max_vis=131072)), dsa.DSA_ERR_INVALID_ARG),
+    (dict(batch=_batch(block_table=FAKE, bt_stride=1000, max_vis=131072)), dsa.DSA_ERR_INVALID_ARG),
+    (dict(index_keys=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(kv=FAKE + 8), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(out=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(workspace=None), dsa.DSA_ERR_WORKSPACE),
+    (dict(workspace_bytes=64), dsa.DSA_ERR_WORKSPACE),
+])
+def test_msa_rejects_bad_arguments(mut, status):
+    lib = dsa.load()
+    assert lib.dsa_msa_decode(ctypes.byref(_msa_args(**mut)), None) == status
+    assert lib.dsa_last_error().decode() != ""
+
+
+def test_msa_workspace_size():
+    a = _msa_args()
+    assert dsa.dsa_workspace_size(dsa.OP_MSA_DECODE, a) == 1 * 4 * 1024 * 4
 
 
 def _mla_args(**kw):
