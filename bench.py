@@ -39,6 +39,7 @@ def parse():
                     help="target length of the oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--shards", type=int, default=8,
                     help="context shards of the sharded top-k merge measurement (0 or 1 = skip)")
+    ap.add_argument("--msa", type=int, default=1, help="also time the MSA block-sparse variant (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
                          "the HBM byte counters of a profiler against a known size")
@@ -285,6 +286,44 @@ def main():
                  "gpu_bound_timing": sh_host_ms < n_busy * ms_step}
         del local, st_op
 
+    # The MSA block-sparse variant on its own workload (apart from the metric):
+    # 128-token blocks, FP8 index keys of one shared head, FP8 K/V of 4 heads.
+    msa = None
+    if args.msa and not prefill:
+        import synth.msa as SM
+        mspec = SM.MSA_CONFIGS["msa_decode_128k"]
+        minp = SM.make_inputs(mspec, device=dev)
+        mop = dsa.MsaDecode(req_row_start=minp["req_row_start"], tok_req=minp["tok_req"], tok_vis=minp["tok_vis"],
+                            block_table=minp["block_table"], idx_pool=minp["idx_pool"], kv_pool=minp["kv_pool"],
+                            q_idx=minp["q_idx"], q=minp["q"], max_vis=mspec.N, max_rows_per_req=mspec.rows,
+                            top_blocks=mspec.top_blocks, k_scale=mspec.k_scale, v_scale=mspec.v_scale)
+        for _ in range(3):
+            mop()
+        torch.cuda.synchronize()
+        m0, m1 = E(enable_timing=True), E(enable_timing=True)
+        m0.record()
+        for _ in range(K):
+            mop()
+        m1.record()
+        torch.cuda.synchronize()
+        msa_ms = m0.elapsed_time(m1) / K
+        mvis = minp["tok_vis"].cpu().tolist()
+        T_m = len(mvis)
+        sel = mop.sel.cpu()
+        kv_tok = 0
+        for t in range(T_m):
+            for g_ in range(mspec.hkv):
+                for b_ in sel[t, g_].tolist():
+                    if b_ >= 0:
+                        kv_tok += min(128, mvis[t] - 128 * b_)
+        mbytes = (mspec.R * 128 * mspec.N + T_m * mspec.hkv * 256 + T_m * mspec.hq * 256 + kv_tok * 256
+                  + T_m * mspec.hq * (512 + 4) + mspec.R * (-(-mspec.N // 128)) * 4)
+        msa = {"workload": mspec.name, "requests": mspec.R, "context": mspec.N, "kv_heads": mspec.hkv,
+               "q_heads": mspec.hq, "top_blocks": mspec.top_blocks, "us": round(msa_ms * 1e3, 2),
+               "alg_bytes": mbytes, "GB_per_s": round(mbytes / (msa_ms * 1e-3) / 1e9, 1),
+               "roofline_frac": round(mbytes / (msa_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
+        del minp, mop
+
     cpu = None
     if args.cpu_seconds > 0:
         def bytes_of_rows(nreq, rows):
@@ -310,6 +349,7 @@ def main():
         "cpu_baseline": cpu,
         "front_end": fe,
         "sharded_topk": shard,
+        "msa": msa,
     }
     print(json.dumps(rec), flush=True)
 

@@ -323,7 +323,7 @@ dsa_status dsa_cache_insert(const dsa_insert_args* args, hipStream_t stream);
  * Hkv or Hq/Hkv > 16, top_blocks outside [1, 16], a bad batch, null or
  * unaligned pointers; DSA_ERR_WORKSPACE below dsa_workspace_size(
  * DSA_OP_MSA_DECODE, args) (the block scores, 4 * T * Hkv * ceil(max_vis/128)
- * bytes). */
+ * bytes, and two partial attention results per (row, group), 16.5 KB each). */
 typedef struct dsa_msa_args {
   dsa_batch batch;               /* rows by request; block_table of 128-token blocks */
   const void* index_keys;        /* device E4M3 [num_blocks, 128, 128]          */

@@ -422,7 +422,9 @@ dsa_status dsa_msa_decode(const dsa_msa_args* a, hipStream_t stream) {
     return fail(DSA_ERR_INVALID_ARG, "msa: null or unaligned pointer");
   if (b.num_rows > 65535 * 64 / 8) return fail(DSA_ERR_INVALID_ARG, "msa: too many rows");
   const int nblk = (b.max_vis + 127) / 128;
-  const size_t need = align_up((size_t)b.num_rows * a->num_kv_heads * nblk * 4, 256);
+  const size_t off_part = align_up((size_t)b.num_rows * a->num_kv_heads * nblk * 4, 256);
+  const size_t need = off_part + align_up((size_t)b.num_rows * a->num_kv_heads * dsa::kMsaSplits *
+                                          dsa::kMsaPartFloats * 4, 256);
   if (!a->workspace || !aligned(a->workspace, 256))
     return fail(DSA_ERR_WORKSPACE, "msa: workspace null or not 256-byte aligned (%zu bytes needed)", need);
   if (a->workspace_bytes < need) return fail(DSA_ERR_WORKSPACE, "msa: workspace %zu bytes, %zu needed", a->workspace_bytes, need);
@@ -449,6 +451,7 @@ dsa_status dsa_msa_decode(const dsa_msa_args* a, hipStream_t stream) {
   p.v_scale = a->v_scale;
   p.sm_scale = a->sm_scale;
   p.bscore = static_cast<float*>(a->workspace);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + off_part);
   p.sel = a->sel_blocks;
   p.out = a->out;
   p.lse = a->lse;
@@ -569,7 +572,8 @@ size_t dsa_workspace_size(int32_t op, const void* args) {
     case DSA_OP_MSA_DECODE: {
       const dsa_msa_args* a = static_cast<const dsa_msa_args*>(args);
       if (a->batch.num_rows < 1 || a->batch.max_vis < 1 || a->num_kv_heads < 1 || a->num_kv_heads > 8) return 0;
-      return align_up((size_t)a->batch.num_rows * a->num_kv_heads * ((a->batch.max_vis + 127) / 128) * 4, 256);
+      return align_up((size_t)a->batch.num_rows * a->num_kv_heads * ((a->batch.max_vis + 127) / 128) * 4, 256) +
+             align_up((size_t)a->batch.num_rows * a->num_kv_heads * dsa::kMsaSplits * dsa::kMsaPartFloats * 4, 256);
     }
     case DSA_OP_TOPK_SHARDED: {
       const dsa_topk_sharded_args* a = static_cast<const dsa_topk_sharded_args*>(args);

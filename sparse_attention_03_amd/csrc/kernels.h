@@ -161,6 +161,11 @@ dsa_status launch_quantize_q(const QuantQParams& p, hipStream_t stream);
 dsa_status launch_cache_insert(const InsertParams& p, hipStream_t stream);
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream);
 dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream);
+// Attention workgroups per (row, group) of the MSA decode, and the floats of
+// one workgroup's partial result (16 maxima, 16 sums, 16 x 128 outputs).
+constexpr int kMsaSplits = 2;
+constexpr int kMsaPartFloats = 16 * 128 + 32;
+
 struct MsaParams {
   int R, T, hkv, hq, G, top, nblk_ld;
   const int32_t* req_row_start;
@@ -176,6 +181,7 @@ struct MsaParams {
   const __bf16* q;          // [T][hq][128]
   float k_scale, v_scale, sm_scale;
   float* bscore;            // workspace [T][hkv][nblk_ld]
+  float* part;              // workspace [T*hkv][kMsaSplits][kMsaPartFloats]
   int32_t* sel;             // [T][hkv][top]
   float* out;               // [T][hq][128]
   float* lse;               // [T][hq] or null

@@ -31,6 +31,7 @@ namespace {
 constexpr int kBlk = 128;       // tokens per block
 constexpr int kD = 128;         // head dim
 constexpr int kAttnWaves = 8;
+constexpr int kAttnSplits = kMsaSplits;  // workgroups per (row, group)
 constexpr int kVStride = 136;   // bf16 per LDS V row (272 B)
 
 __device__ __forceinline__ int msa_vis(const MsaParams& p, int t) { return min(max(p.tok_vis[t], 0), p.max_vis); }
@@ -41,57 +42,97 @@ __device__ __forceinline__ int msa_page(const MsaParams& p, int r, int b) {
   return (pg >= 0 && pg < p.pool_blocks) ? pg : -1;
 }
 
+constexpr int kIdxBlocks = 4;  // blocks per index workgroup
+
+// 32 contiguous key bytes per lane (dims 32g .. 32g+31 of keys 32w + 16mt + c):
+// k-step ks takes dims 32g + 8ks .. +8 from lane group g (any split of the 128
+// dims works when the query side uses the same one).
+struct KeyRegs {
+  i32x4 v[2][2];
+};
+
+__device__ __forceinline__ void load_keys(const MsaParams& p, int page, int w, int g, int c, KeyRegs& k) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    if (page >= 0) {
+      const i32x4* src = reinterpret_cast<const i32x4*>(p.idx_pool + (int64_t)page * (kBlk * kD) +
+                                                        (32 * w + 16 * mt + c) * kD + 32 * g);
+      k.v[mt][0] = __builtin_nontemporal_load(src);
+      k.v[mt][1] = __builtin_nontemporal_load(src + 1);
+    } else {
+      k.v[mt][0] = i32x4{0, 0, 0, 0};
+      k.v[mt][1] = i32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// One workgroup per (request, kIdxBlocks consecutive blocks): every wave
+// scores 32 keys of each block for every (row, group) query of the request
+// (keys as MFMA M, FP8 -> BF16 exact, queries as N), the next block's keys
+// loading while the current one is scored; the per-wave block maxima meet in
+// LDS once per query tile.
 __global__ __launch_bounds__(256) void msa_index_kernel(MsaParams p) {
-  __shared__ float red[4][16];
-  const int b = blockIdx.x, r = blockIdx.y;
+  __shared__ float red[kIdxBlocks][4][16];
+  const int bb0 = blockIdx.x * kIdxBlocks, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int rs = p.req_row_start[r], nrows = p.req_row_start[r + 1] - rs;
   int vmax = 0;
   for (int i = 0; i < nrows; ++i) vmax = max(vmax, msa_vis(p, rs + i));
-  if (b * kBlk >= vmax) return;
-  const int page = msa_page(p, r, b);
+  const int nblk = min(kIdxBlocks, (vmax + kBlk - 1) / kBlk - bb0);
+  if (nblk <= 0) return;
   const int nq = nrows * p.hkv;
-  // A fragments: keys 32w + 16mt + c, dims 32ks + 8g .. +8 (exact FP8 -> BF16)
-  bf16x8 A[2][4];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint2 v = make_uint2(0u, 0u);
-      if (page >= 0)
-        v = *reinterpret_cast<const uint2*>(p.idx_pool + (int64_t)page * (kBlk * kD) +
-                                            (32 * w + 16 * mt + c) * kD + 32 * ks + 8 * g);
-      A[mt][ks] = e4m3x8_to_bf16x8(v.x, v.y);
-    }
-  }
   for (int q0 = 0; q0 < nq; q0 += 16) {
     const int qq = q0 + c;  // this lane's query column
     const bool qok = qq < nq;
     const int row = rs + (qok ? qq / p.hkv : 0), grp = qok ? qq % p.hkv : 0;
     const int vis = qok ? msa_vis(p, row) : 0;
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    bf16x8 bq[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 bq = {};
-      if (qok) bq = *reinterpret_cast<const bf16x8*>(p.q_idx + ((int64_t)row * p.hkv + grp) * kD + 32 * ks + 8 * g);
-      acc[0] = mfma16x16x32(A[0][ks], bq, acc[0]);
-      acc[1] = mfma16x16x32(A[1][ks], bq, acc[1]);
+      bq[ks] = bf16x8{};
+      if (qok) bq[ks] = *reinterpret_cast<const bf16x8*>(p.q_idx + ((int64_t)row * p.hkv + grp) * kD + 32 * g + 8 * ks);
     }
-    float mx = -INFINITY;
+    KeyRegs cur, nxt;
+    int page = msa_page(p, r, bb0);
+    load_keys(p, page, w, g, c, cur);
+    for (int i = 0; i < nblk; ++i) {
+      const int b = bb0 + i;
+      const int npage = i + 1 < nblk ? msa_page(p, r, b + 1) : -1;
+      if (i + 1 < nblk) load_keys(p, npage, w, g, c, nxt);
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = b * kBlk + 32 * w + 16 * mt + 4 * g + i;
-        if (page >= 0 && j < vis) mx = fmaxf(mx, acc[mt][i]);
+      for (int mt = 0; mt < 2; ++mt) {
+        acc[mt] = mfma16x16x32(e4m3x8_to_bf16x8(cur.v[mt][0][0], cur.v[mt][0][1]), bq[0], acc[mt]);
+        acc[mt] = mfma16x16x32(e4m3x8_to_bf16x8(cur.v[mt][0][2], cur.v[mt][0][3]), bq[1], acc[mt]);
+        acc[mt] = mfma16x16x32(e4m3x8_to_bf16x8(cur.v[mt][1][0], cur.v[mt][1][1]), bq[2], acc[mt]);
+        acc[mt] = mfma16x16x32(e4m3x8_to_bf16x8(cur.v[mt][1][2], cur.v[mt][1][3]), bq[3], acc[mt]);
       }
-    mx = fmaxf(mx, __uint_as_float(lane_xor(__float_as_uint(mx), 16)));
-    mx = fmaxf(mx, __uint_as_float(lane_xor(__float_as_uint(mx), 32)));
-    if (lane < 16) red[w][lane] = mx;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tok = b * kBlk + 32 * w + 16 * mt + 4 * g + j;
+          if (page >= 0 && tok < vis) mx = fmaxf(mx, acc[mt][j]);
+        }
+      mx = fmaxf(mx, __uint_as_float(lane_xor(__float_as_uint(mx), 16)));
+      mx = fmaxf(mx, __uint_as_float(lane_xor(__float_as_uint(mx), 32)));
+      if (lane < 16) red[i][w][lane] = mx;
+      cur = nxt;
+      page = npage;
+    }
     __syncthreads();
-    if (tid < 16 && qok && b * kBlk < vis) {
-      const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-      p.bscore[((int64_t)row * p.hkv + grp) * p.nblk_ld + b] = m;
+    if (tid < 16 * kIdxBlocks) {
+      const int i = tid >> 4, col = tid & 15;
+      const int qc = q0 + col;
+      const int b = bb0 + i;
+      if (i < nblk && qc < nq) {
+        const int rw = rs + qc / p.hkv, gp = qc % p.hkv;
+        if (b * kBlk < msa_vis(p, rw)) {
+          const float m = fmaxf(fmaxf(red[i][0][col], red[i][1][col]), fmaxf(red[i][2][col], red[i][3][col]));
+          p.bscore[((int64_t)rw * p.hkv + gp) * p.nblk_ld + b] = m;
+        }
+      }
     }
     __syncthreads();
   }
@@ -159,12 +200,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) 
   const float lscale = p.sm_scale * p.k_scale;
   const int64_t tok_bytes = 2LL * p.hkv * kD;
   const int64_t page_bytes = (int64_t)kBlk * tok_bytes;
-  // Q^T fragments: head c of the group, dims 32ks + 8g .. +8 (zero past G)
+  // Q^T fragments: head c of the group, dims 32g + 8ks .. +8 (zero past G)
   bf16x8 bq[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     bq[ks] = bf16x8{};
-    if (c < p.G) bq[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((int64_t)t * p.hq + hbase + c) * kD + 32 * ks + 8 * g);
+    if (c < p.G) bq[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((int64_t)t * p.hq + hbase + c) * kD + 32 * g + 8 * ks);
   }
   f32x4 O[8];
 #pragma unroll
@@ -172,7 +213,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) 
   float m_c = -INFINITY, l_c = 0.f;  // running max / sum of head c
   __bf16* vrow = vt[w];
   const __bf16* vsrc = vrow + (4 * g + (c >> 2)) * kVStride + 4 * (c & 3);
-  for (int sj = w; sj < p.top; sj += kAttnWaves) {
+  // split s of kAttnSplits takes selected blocks s*kAttnWaves + w, + kAttnWaves*kAttnSplits, ...
+  const int split = blockIdx.y;
+  for (int sj = split * kAttnWaves + w; sj < p.top; sj += kAttnWaves * kAttnSplits) {
     const int blk = p.sel[(int64_t)tg * p.top + sj];
     if (blk < 0) continue;
     const int page = msa_page(p, r, blk);
@@ -182,13 +225,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) 
       const int key0 = blk * kBlk + 16 * tile;
       if (key0 >= vis) break;
       // S^T[key 4g+i][head c] over the tile's 16 keys
+      // (k-step ks takes dims 32g + 8ks .. +8 from lane group g, as the
+      // query fragments do: 32 contiguous key bytes per lane)
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
       const uint8_t* krow = base + (int64_t)(16 * tile + c) * tok_bytes;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint2 kv = *reinterpret_cast<const uint2*>(krow + 32 * ks + 8 * g);
-        s = mfma16x16x32(e4m3x8_to_bf16x8(kv.x, kv.y), bq[ks], s);
-      }
+      const i32x4 k0 = *reinterpret_cast<const i32x4*>(krow + 32 * g);
+      const i32x4 k1 = *reinterpret_cast<const i32x4*>(krow + 32 * g + 16);
+      s = mfma16x16x32(e4m3x8_to_bf16x8(k0[0], k0[1]), bq[0], s);
+      s = mfma16x16x32(e4m3x8_to_bf16x8(k0[2], k0[3]), bq[1], s);
+      s = mfma16x16x32(e4m3x8_to_bf16x8(k1[0], k1[1]), bq[2], s);
+      s = mfma16x16x32(e4m3x8_to_bf16x8(k1[2], k1[3]), bq[3], s);
       // V rows of the tile -> BF16 in LDS (zero rows past vis)
       {
         const bool vok = key0 + c < vis;
@@ -264,9 +310,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) po[w][4 * g + i][16 * u + c] = O[u][i];
   __syncthreads();
+  // the workgroup's partial (max, sum, unnormalised output) per head
+  float* part = p.part + ((int64_t)tg * kAttnSplits + split) * kMsaPartFloats;
   for (int e = tid; e < 16 * kD; e += 64 * kAttnWaves) {
     const int h = e / kD, d = e - h * kD;
-    if (h >= p.G) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, pm[v][h]);
@@ -279,7 +326,35 @@ __global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) 
         acc += e_v * po[v][h][d];
       }
     }
-    const int64_t oh = (int64_t)t * p.hq + hbase + h;
+    part[32 + e] = acc;
+    if (d == 0) {
+      part[h] = M;
+      part[16 + h] = Lsum;
+    }
+  }
+}
+
+// Merge the kAttnSplits partials of every (row, group) by log-sum-exp.
+__global__ __launch_bounds__(256) void msa_combine_kernel(MsaParams p) {
+  const int tg = blockIdx.x, t = tg / p.hkv, grp = tg - t * p.hkv;
+  const float* part = p.part + (int64_t)tg * kAttnSplits * kMsaPartFloats;
+  for (int e = threadIdx.x; e < 16 * kD; e += 256) {
+    const int h = e / kD, d = e - h * kD;
+    if (h >= p.G) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kAttnSplits; ++sp) M = fmaxf(M, part[sp * kMsaPartFloats + h]);
+    float Lsum = 0.f, acc = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int sp = 0; sp < kAttnSplits; ++sp) {
+        const float* q = part + sp * kMsaPartFloats;
+        const float e_s = q[h] > -INFINITY ? __expf(q[h] - M) : 0.f;
+        Lsum += e_s * q[16 + h];
+        acc += e_s * q[32 + e];
+      }
+    }
+    const int64_t oh = (int64_t)t * p.hq + grp * p.G + h;
     p.out[oh * kD + d] = Lsum > 0.f ? p.v_scale * acc / Lsum : 0.f;
     if (d == 0 && p.lse) p.lse[oh] = Lsum > 0.f ? M + __logf(Lsum) : -INFINITY;
   }
@@ -288,9 +363,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) 
 }  // namespace
 
 dsa_status launch_msa(const MsaParams& p, int nblk_max, hipStream_t stream) {
-  hipLaunchKernelGGL(msa_index_kernel, dim3(nblk_max, p.R), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(msa_index_kernel, dim3((nblk_max + kIdxBlocks - 1) / kIdxBlocks, p.R), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(msa_select_kernel, dim3(p.T * p.hkv), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(msa_attn_kernel, dim3(p.T * p.hkv), dim3(64 * kAttnWaves), 0, stream, p);
+  hipLaunchKernelGGL(msa_attn_kernel, dim3(p.T * p.hkv, kAttnSplits), dim3(64 * kAttnWaves), 0, stream, p);
+  hipLaunchKernelGGL(msa_combine_kernel, dim3(p.T * p.hkv), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

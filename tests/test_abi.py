@@ -193,7 +193,8 @@ def test_msa_rejects_bad_arguments(mut, status):
 
 def test_msa_workspace_size():
     a = _msa_args()
-    assert dsa.dsa_workspace_size(dsa.OP_MSA_DECODE, a) == 1 * 4 * 1024 * 4
+    # block scores (rows x Hkv x blocks fp32) + two partial results of 16 x 128 + 32 fp32 per (row, group)
+    assert dsa.dsa_workspace_size(dsa.OP_MSA_DECODE, a) == 1 * 4 * 1024 * 4 + 1 * 4 * 2 * (16 * 128 + 32) * 4
 
 
 def _mla_args(**kw):
