@@ -89,7 +89,7 @@ enum { DSA_Q_BF16 = 1, DSA_Q_FP8 = 2, DSA_Q_MXFP4 = 3 };
 
 /* Operation ids for dsa_workspace_size(). */
 enum { DSA_OP_INDEXER = 1, DSA_OP_TOPK = 2, DSA_OP_MLA_DECODE = 3, DSA_OP_MLA_PREFILL = 4,
-       DSA_OP_TOPK_SHARDED = 5, DSA_OP_MSA_DECODE = 6 };
+       DSA_OP_TOPK_SHARDED = 5, DSA_OP_MSA_DECODE = 6, DSA_OP_INDEXER_PREFIX = 7 };
 
 /* One paged pool (index keys or latents) of one layer. */
 typedef struct dsa_cache {
@@ -136,6 +136,35 @@ typedef struct dsa_indexer_args {
   int64_t ld;                    /* row stride of scores, >= max_vis, %4 == 0  */
 } dsa_indexer_args;
 dsa_status dsa_indexer_scores(const dsa_indexer_args* args, hipStream_t stream);
+
+/* dsa_indexer_scores_prefix -- the indexer for batches whose requests share
+ * a cached prefix (high-concurrency decode over one long shared context; the
+ * MiniMax M3.1 page's AMD section dequantises a shared-prefix page once for
+ * up to 64 requests).  Requests form groups of consecutive requests whose
+ * rows are consecutive: group g owns rows [group_row_start[g],
+ * group_row_start[g+1]); every request of a group maps its first
+ * prefix_len / P logical pages to the same physical pages, those of request
+ * group_first_req[g].  The shared pages are streamed once for all rows of the
+ * group (one multi-row pass), the rest of every request once for its own
+ * rows.  The scores are those of dsa_indexer_scores(&base) on the same
+ * inputs, up to the order of fp32 additions (the shared pass may run on the
+ * multi-row kernel where the plain call runs the single-row one).
+ * prefix_len is a multiple of the page size, 0 <= prefix_len <= max_vis;
+ * BF16 q only; groups of at most 64 requests' rows are the intended case.
+ * Errors as dsa_indexer_scores, plus DSA_ERR_INVALID_ARG for a bad group
+ * description and DSA_ERR_WORKSPACE below dsa_workspace_size(
+ * DSA_OP_INDEXER_PREFIX, args). */
+typedef struct dsa_indexer_prefix_args {
+  dsa_indexer_args base;         /* the plain call's arguments (block table required) */
+  int32_t num_groups;            /* G >= 1                                       */
+  const int32_t* group_row_start;/* device int32 [G+1], from 0 to num_rows       */
+  const int32_t* group_first_req;/* device int32 [G]: a request of each group    */
+  int32_t prefix_len;            /* shared tokens per group                      */
+  int32_t max_rows_per_group;    /* host bound on rows of one group              */
+  void* workspace;               /* device, 256-byte aligned                     */
+  size_t workspace_bytes;
+} dsa_indexer_prefix_args;
+dsa_status dsa_indexer_scores_prefix(const dsa_indexer_prefix_args* args, hipStream_t stream);
 
 /* dsa_topk -- stage 2, per-row top-k with a deterministic tie-break.
  * Keeps K_t = min(k, tok_vis[t]) positions of row t: the highest scores, and

@@ -27,6 +27,7 @@ KEY_FP8, KEY_MXFP4 = 1, 2
 LAT_BF16, LAT_FP8, LAT_NVFP4 = 1, 2, 3
 Q_BF16, Q_FP8, Q_MXFP4 = 1, 2, 3
 OP_INDEXER, OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_TOPK_SHARDED, OP_MSA_DECODE = 1, 2, 3, 4, 5, 6
+OP_INDEXER_PREFIX = 7
 
 KEY_FMT = {"fp8": KEY_FP8, "mxfp4": KEY_MXFP4}
 LAT_FMT = {"bf16": LAT_BF16, "fp8": LAT_FP8, "nvfp4": LAT_NVFP4}
@@ -38,7 +39,7 @@ LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per l
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
            "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
            "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded",
-           "dsa_msa_decode")
+           "dsa_msa_decode", "dsa_indexer_scores_prefix")
 
 
 class DsaError(RuntimeError):
@@ -65,6 +66,13 @@ class IndexerArgs(ctypes.Structure):
     _fields_ = [("batch", Batch), ("keys", Cache), ("q", ctypes.c_void_p),
                 ("q_fmt", ctypes.c_int32), ("q_scale", ctypes.c_void_p),
                 ("w", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("ld", ctypes.c_int64)]
+
+
+class IndexerPrefixArgs(ctypes.Structure):
+    _fields_ = [("base", IndexerArgs), ("num_groups", ctypes.c_int32), ("group_row_start", ctypes.c_void_p),
+                ("group_first_req", ctypes.c_void_p), ("prefix_len", ctypes.c_int32),
+                ("max_rows_per_group", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class TopkArgs(ctypes.Structure):
@@ -134,7 +142,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        ("dsa_quantize_q", [ctypes.POINTER(QuantQArgs), vp]),
                        ("dsa_cache_insert", [ctypes.POINTER(InsertArgs), vp]),
                        ("dsa_topk_sharded", [ctypes.POINTER(TopkShardedArgs), vp]),
-                       ("dsa_msa_decode", [ctypes.POINTER(MsaArgs), vp])):
+                       ("dsa_msa_decode", [ctypes.POINTER(MsaArgs), vp]),
+                       ("dsa_indexer_scores_prefix", [ctypes.POINTER(IndexerPrefixArgs), vp])):
         f = getattr(lib, name)
         f.argtypes = argt
         f.restype = ctypes.c_int
@@ -191,6 +200,23 @@ def batch_view(req_row_start: torch.Tensor, tok_req: torch.Tensor, tok_vis: torc
 # ------------------------------------------------------------ entry points
 def dsa_indexer_scores(args: IndexerArgs, stream=None):
     _check(load().dsa_indexer_scores(ctypes.byref(args), _stream(stream)), "dsa_indexer_scores")
+
+
+def dsa_indexer_scores_prefix(args: IndexerPrefixArgs, stream=None):
+    _check(load().dsa_indexer_scores_prefix(ctypes.byref(args), _stream(stream)), "dsa_indexer_scores_prefix")
+
+
+def indexer_prefix_args(base: IndexerArgs, group_row_start: torch.Tensor, group_first_req: torch.Tensor,
+                        prefix_len: int, max_rows_per_group: int, device) -> tuple:
+    """(IndexerPrefixArgs, workspace tensor) for dsa_indexer_scores_prefix."""
+    for t in (group_row_start, group_first_req):
+        assert t.dtype == torch.int32 and t.is_contiguous()
+    a = IndexerPrefixArgs(base, int(group_first_req.numel()), group_row_start.data_ptr(),
+                          group_first_req.data_ptr(), int(prefix_len), int(max_rows_per_group), None, 0)
+    ws = workspace(dsa_workspace_size(OP_INDEXER_PREFIX, a), device)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel()
+    return a, ws
 
 
 def dsa_topk(args: TopkArgs, stream=None):

@@ -297,6 +297,84 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
   return DSA_OK;
 }
 
+namespace {
+struct PrefixPlan {
+  int npfx;
+  size_t off_vis1, off_vis2, off_ptab, total;
+};
+PrefixPlan plan_prefix(const dsa_indexer_prefix_args& a) {
+  PrefixPlan pl;
+  const int P = 1 << a.base.keys.page_size_log2;
+  pl.npfx = a.prefix_len / P;
+  size_t off = 0;
+  pl.off_vis1 = off;
+  off = align_up(off + (size_t)a.base.batch.num_rows * 4, 256);
+  pl.off_vis2 = off;
+  off = align_up(off + (size_t)a.base.batch.num_rows * 4, 256);
+  pl.off_ptab = off;
+  off = align_up(off + (size_t)std::max(1, a.num_groups) * std::max(1, pl.npfx) * 4, 256);
+  pl.total = off;
+  return pl;
+}
+}  // namespace
+
+dsa_status dsa_indexer_scores_prefix(const dsa_indexer_prefix_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "indexer_prefix: null args");
+  const dsa_indexer_args& base = a->base;
+  dsa_status st = check_cache(base.keys, key_token_bytes(base.keys.fmt), "indexer keys");
+  if (st != DSA_OK) return st;
+  st = check_batch(base.batch, base.keys.page_size_log2, true);
+  if (st != DSA_OK) return st;
+  if (base.q_fmt != DSA_Q_BF16) return fail(DSA_ERR_UNSUPPORTED, "indexer_prefix: BF16 q only");
+  if (!base.batch.block_table) return fail(DSA_ERR_INVALID_ARG, "indexer_prefix: a block table is required");
+  const int P = 1 << base.keys.page_size_log2;
+  if (a->num_groups < 1 || a->num_groups > base.batch.num_requests || !a->group_row_start || !a->group_first_req ||
+      a->max_rows_per_group < 1)
+    return fail(DSA_ERR_INVALID_ARG, "indexer_prefix: bad group description");
+  if (a->prefix_len < 0 || a->prefix_len % P != 0 || a->prefix_len > base.batch.max_vis)
+    return fail(DSA_ERR_INVALID_ARG, "indexer_prefix: prefix_len %d (multiple of %d, at most max_vis)", a->prefix_len, P);
+  if (!base.scores || !aligned(base.scores, 16) || base.ld % 4 != 0 || base.ld < base.batch.max_vis)
+    return fail(DSA_ERR_INVALID_ARG, "indexer_prefix: scores / ld");
+  const PrefixPlan pl = plan_prefix(*a);
+  if (!a->workspace || !aligned(a->workspace, 256))
+    return fail(DSA_ERR_WORKSPACE, "indexer_prefix: workspace null or not 256-byte aligned (%zu bytes needed)", pl.total);
+  if (a->workspace_bytes < pl.total)
+    return fail(DSA_ERR_WORKSPACE, "indexer_prefix: workspace %zu bytes, %zu needed", a->workspace_bytes, pl.total);
+  char* ws = static_cast<char*>(a->workspace);
+  int32_t* vis1 = reinterpret_cast<int32_t*>(ws + pl.off_vis1);
+  int32_t* vis2 = reinterpret_cast<int32_t*>(ws + pl.off_vis2);
+  int32_t* ptab = reinterpret_cast<int32_t*>(ws + pl.off_ptab);
+  const int L = a->prefix_len;
+  st = dsa::launch_prefix_prep(base.batch.tok_vis, base.batch.num_rows, base.batch.max_vis, L, base.batch.block_table,
+                               base.batch.bt_stride, base.batch.num_requests, a->group_first_req, a->num_groups,
+                               pl.npfx, vis1, vis2, ptab, stream);
+  if (st != DSA_OK) return fail(st, "indexer_prefix: launch failed: %s", hipGetErrorString(hipGetLastError()));
+  if (L > 0) {  // shared pages, once per group for all of its rows
+    dsa_indexer_args a1 = base;
+    a1.batch.num_requests = a->num_groups;
+    a1.batch.req_row_start = a->group_row_start;
+    a1.batch.tok_vis = vis1;
+    a1.batch.block_table = ptab;
+    a1.batch.bt_stride = pl.npfx;
+    a1.batch.max_vis = L;
+    a1.batch.max_rows_per_req = a->max_rows_per_group;
+    st = dsa_indexer_scores(&a1, stream);
+    if (st != DSA_OK) return st;
+  }
+  if (base.batch.max_vis > L) {  // every request's own pages past the prefix
+    dsa_indexer_args a2 = base;
+    a2.batch.tok_vis = vis2;
+    a2.batch.block_table = base.batch.block_table + L / P;
+    a2.batch.bt_stride = base.batch.bt_stride;
+    a2.batch.max_vis = base.batch.max_vis - L;
+    a2.scores = base.scores + L;
+    st = dsa_indexer_scores(&a2, stream);
+    if (st != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
 dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   g_err[0] = 0;
   if (!a) return fail(DSA_ERR_INVALID_ARG, "topk: null args");
@@ -568,6 +646,13 @@ size_t dsa_workspace_size(int32_t op, const void* args) {
       const dsa_topk_args* a = static_cast<const dsa_topk_args*>(args);
       if (a->k < 1 || a->k > DSA_MAX_TOPK || a->batch.num_rows < 1 || a->batch.max_vis < 1) return 0;
       return plan_topk(a->batch.num_rows, a->batch.max_vis, a->k).total;
+    }
+    case DSA_OP_INDEXER_PREFIX: {
+      const dsa_indexer_prefix_args* a = static_cast<const dsa_indexer_prefix_args*>(args);
+      if (a->base.batch.num_rows < 1 || a->num_groups < 1 || a->base.keys.page_size_log2 < 4 ||
+          a->base.keys.page_size_log2 > 24 || a->prefix_len < 0)
+        return 0;
+      return plan_prefix(*a).total;
     }
     case DSA_OP_MSA_DECODE: {
       const dsa_msa_args* a = static_cast<const dsa_msa_args*>(args);

@@ -509,6 +509,35 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
   for (int i = tid; i < kend - k0; i += 256) out[k0 + i] = sc_out[i];
 }
 
+// Shared-prefix plan: the visible counts of the prefix and suffix passes, and
+// the prefix pages of every group (read from the block-table row of one of
+// its requests).
+__global__ void prefix_prep_kernel(const int32_t* __restrict__ tok_vis, int T, int max_vis, int L,
+                                   const int32_t* __restrict__ bt, int bt_stride, int R,
+                                   const int32_t* __restrict__ first_req, int G, int npfx, int32_t* __restrict__ vis1,
+                                   int32_t* __restrict__ vis2, int32_t* __restrict__ ptab) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) {
+    const int v = min(max(tok_vis[i], 0), max_vis);
+    vis1[i] = min(v, L);
+    vis2[i] = max(v - L, 0);
+  }
+  if (i < G * npfx) {
+    const int g = i / npfx, j = i - g * npfx;
+    const int r = first_req[g];
+    ptab[i] = (r >= 0 && r < R) ? bt[(int64_t)r * bt_stride + j] : -1;  // (a bad request id: absent pages)
+  }
+}
+
+dsa_status launch_prefix_prep(const int32_t* tok_vis, int T, int max_vis, int L, const int32_t* bt, int bt_stride,
+                              int R, const int32_t* first_req, int G, int npfx, int32_t* vis1, int32_t* vis2,
+                              int32_t* ptab, hipStream_t stream) {
+  const int n = max(T, G * npfx);
+  hipLaunchKernelGGL(prefix_prep_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, tok_vis, T, max_vis, L, bt,
+                     bt_stride, R, first_req, G, npfx, vis1, vis2, ptab);
+  return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
   dim3 grid((p.max_vis + p.chunk - 1) / p.chunk, p.R);
   const size_t lds = (size_t)p.qrows * 32 * (kQPad * sizeof(__bf16) + sizeof(float));

@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
               "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
-              "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded", "dsa_msa_decode"):
+              "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded", "dsa_msa_decode",
+              "dsa_indexer_scores_prefix"):
         assert n in names
 
 
@@ -40,7 +41,7 @@ def test_struct_layouts_match_the_c_compiler(tmp_path):
     structs = {"dsa_cache": dsa.Cache, "dsa_batch": dsa.Batch, "dsa_indexer_args": dsa.IndexerArgs,
                "dsa_topk_args": dsa.TopkArgs, "dsa_mla_args": dsa.MlaArgs, "dsa_quant_q_args": dsa.QuantQArgs,
                "dsa_insert_args": dsa.InsertArgs, "dsa_topk_sharded_args": dsa.TopkShardedArgs,
-               "dsa_msa_args": dsa.MsaArgs}
+               "dsa_msa_args": dsa.MsaArgs, "dsa_indexer_prefix_args": dsa.IndexerPrefixArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -96,6 +97,45 @@ def test_indexer_rejects_bad_arguments(mut, status):
     a = _idx_args(**mut)
     assert lib.dsa_indexer_scores(ctypes.byref(a), None) == status
     assert lib.dsa_last_error().decode() != ""
+
+
+def _prefix_args(**kw):
+    base = _idx_args(batch=_batch(num_requests=4, num_rows=4, block_table=FAKE, bt_stride=128, max_vis=8192),
+                     keys=_cache(plog2=6, page_bytes=132 * 64, pages=512))
+    a = dict(base=base, num_groups=1, group_row_start=FAKE, group_first_req=FAKE, prefix_len=4096,
+             max_rows_per_group=4, workspace=FAKE, workspace_bytes=1 << 40)
+    a.update(kw)
+    return dsa.IndexerPrefixArgs(**a)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(num_groups=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(num_groups=5), dsa.DSA_ERR_INVALID_ARG),          # more groups than requests
+    (dict(group_row_start=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(group_first_req=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(prefix_len=100), dsa.DSA_ERR_INVALID_ARG),        # not a multiple of the page size
+    (dict(prefix_len=8256), dsa.DSA_ERR_INVALID_ARG),       # beyond max_vis
+    (dict(prefix_len=-64), dsa.DSA_ERR_INVALID_ARG),
+    (dict(max_rows_per_group=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(workspace=None), dsa.DSA_ERR_WORKSPACE),
+    (dict(workspace_bytes=16), dsa.DSA_ERR_WORKSPACE),
+])
+def test_indexer_prefix_rejects_bad_arguments(mut, status):
+    lib = dsa.load()
+    assert lib.dsa_indexer_scores_prefix(ctypes.byref(_prefix_args(**mut)), None) == status
+    assert lib.dsa_last_error().decode() != ""
+
+
+def test_indexer_prefix_rejects_fp8_q_and_missing_table():
+    lib = dsa.load()
+    a = _prefix_args()
+    a.base.q_fmt = dsa.Q_FP8
+    a.base.q_scale = FAKE
+    assert lib.dsa_indexer_scores_prefix(ctypes.byref(a), None) == dsa.DSA_ERR_UNSUPPORTED
+    a = _prefix_args()
+    a.base.batch.block_table = None
+    a.base.batch.max_vis = 64
+    assert lib.dsa_indexer_scores_prefix(ctypes.byref(a), None) == dsa.DSA_ERR_INVALID_ARG
 
 
 def _topk_args(**kw):
