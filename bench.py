@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--shards", type=int, default=8,
                     help="context shards of the sharded top-k merge measurement (0 or 1 = skip)")
     ap.add_argument("--msa", type=int, default=1, help="also time the MSA block-sparse variant (0 = skip)")
+    ap.add_argument("--prefix", type=int, default=1,
+                    help="also time the shared-prefix indexer on a 64-request FP4 batch (0 = skip)")
+    ap.add_argument("--prefix-group", type=int, default=64, help="requests per shared-prefix group")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
                          "the HBM byte counters of a profiler against a known size")
@@ -324,6 +327,59 @@ def main():
                "roofline_frac": round(mbytes / (msa_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
         del minp, mop
 
+    # Shared-prefix indexer on a high-concurrency FP4 batch (apart from the
+    # metric): 64 single-row requests at 256K whose first 192K tokens are one
+    # shared prefix (the same physical pages), plain call against the call
+    # that streams the shared pages once for the whole group.
+    pre = None
+    if args.prefix and not prefill:
+        pspec = synth.CONFIGS["fp4_decode_256k"]
+        pwl = synth.make_workload(pspec, device=dev)
+        L = 196608
+        gsz = args.prefix_group  # requests per group (one request = one row here)
+        bt = pwl.block_table.clone()
+        for a0 in range(0, pwl.R, gsz):
+            bt[a0:a0 + gsz, :L // pwl.P] = bt[a0, :L // pwl.P].clone()
+        pwl.block_table = bt.contiguous()
+        pst = dsa.make_step(key_pool=pwl.key_pool, lat_pool=pwl.lat_pool, page_size=pwl.P, key_fmt=pspec.key_fmt,
+                            lat_fmt=pspec.lat_fmt, req_row_start=pwl.req_token_start, tok_req=pwl.tok_req,
+                            tok_vis=pwl.tok_vis, block_table=pwl.block_table, q_idx=pwl.q_idx, w=pwl.w,
+                            q_mla=pwl.q_mla, k=pspec.k, sm_scale=pspec.sm_scale, q_idx_scale=pwl.q_idx_scale,
+                            max_vis=pspec.N, max_rows_per_req=pspec.q_per_req)
+        starts = list(range(0, pwl.R, gsz))
+        grs = torch.tensor(starts + [pwl.T], dtype=torch.int32, device=dev)
+        gfr = torch.tensor(starts, dtype=torch.int32, device=dev)
+        pargs, pws = dsa.indexer_prefix_args(dsa.IndexerArgs.from_buffer_copy(pst.iargs), grs, gfr, L, gsz, dev)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a0, a1 = E(enable_timing=True), E(enable_timing=True)
+            a0.record()
+            for _ in range(K):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / K
+
+        plain_ms = timed(pst.indexer)
+        ref = pst.scores.clone()
+        pre_ms = timed(lambda: dsa.dsa_indexer_scores_prefix(pargs))
+        pvis = pwl.tok_vis.cpu().tolist()
+        diff = max(float((pst.scores[t, :v] - ref[t, :v]).abs().max() / ref[t, :v].abs().max())
+                   for t, v in enumerate(pvis))
+        kb = 68
+        plain_bytes = sum(pvis) * kb
+        # the shared pages are streamed once per pass of at most 12 rows
+        n_pass = sum(-(-min(gsz, pwl.R - a0) // 12) for a0 in starts)
+        shared_bytes = n_pass * L * kb + sum(v - L for v in pvis) * kb
+        pre = {"workload": f"fp4_decode_256k, groups of {gsz} requests sharing a 196,608-token prefix",
+               "plain_us": round(plain_ms * 1e3, 2),
+               "prefix_us": round(pre_ms * 1e3, 2), "plain_key_bytes": plain_bytes, "prefix_key_bytes": shared_bytes,
+               "max_rel_diff": diff}
+        del pwl, pst, ref
+
     cpu = None
     if args.cpu_seconds > 0:
         def bytes_of_rows(nreq, rows):
@@ -350,6 +406,7 @@ def main():
         "front_end": fe,
         "sharded_topk": shard,
         "msa": msa,
+        "shared_prefix_indexer": pre,
     }
     print(json.dumps(rec), flush=True)
 

@@ -299,20 +299,27 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
 
 namespace {
 struct PrefixPlan {
-  int npfx;
-  size_t off_vis1, off_vis2, off_ptab, total;
+  int npfx, ns_max;
+  size_t off_vis1, off_vis2, off_sub, off_src, off_ptab, total;
 };
 PrefixPlan plan_prefix(const dsa_indexer_prefix_args& a) {
   PrefixPlan pl;
   const int P = 1 << a.base.keys.page_size_log2;
+  const int T = a.base.batch.num_rows;
   pl.npfx = a.prefix_len / P;
+  // every group adds at most one partial sub-group
+  pl.ns_max = std::max(1, a.num_groups) + (T + dsa::kPrefixSubRows - 1) / dsa::kPrefixSubRows;
   size_t off = 0;
   pl.off_vis1 = off;
-  off = align_up(off + (size_t)a.base.batch.num_rows * 4, 256);
+  off = align_up(off + (size_t)T * 4, 256);
   pl.off_vis2 = off;
-  off = align_up(off + (size_t)a.base.batch.num_rows * 4, 256);
+  off = align_up(off + (size_t)T * 4, 256);
+  pl.off_sub = off;
+  off = align_up(off + (size_t)(pl.ns_max + 1) * 4, 256);
+  pl.off_src = off;
+  off = align_up(off + (size_t)pl.ns_max * 4, 256);
   pl.off_ptab = off;
-  off = align_up(off + (size_t)std::max(1, a.num_groups) * std::max(1, pl.npfx) * 4, 256);
+  off = align_up(off + (size_t)pl.ns_max * std::max(1, pl.npfx) * 4, 256);
   pl.total = off;
   return pl;
 }
@@ -345,20 +352,22 @@ dsa_status dsa_indexer_scores_prefix(const dsa_indexer_prefix_args* a, hipStream
   int32_t* vis1 = reinterpret_cast<int32_t*>(ws + pl.off_vis1);
   int32_t* vis2 = reinterpret_cast<int32_t*>(ws + pl.off_vis2);
   int32_t* ptab = reinterpret_cast<int32_t*>(ws + pl.off_ptab);
+  int32_t* sub_start = reinterpret_cast<int32_t*>(ws + pl.off_sub);
+  int32_t* sub_src = reinterpret_cast<int32_t*>(ws + pl.off_src);
   const int L = a->prefix_len;
   st = dsa::launch_prefix_prep(base.batch.tok_vis, base.batch.num_rows, base.batch.max_vis, L, base.batch.block_table,
-                               base.batch.bt_stride, base.batch.num_requests, a->group_first_req, a->num_groups,
-                               pl.npfx, vis1, vis2, ptab, stream);
+                               base.batch.bt_stride, base.batch.num_requests, a->group_row_start, a->group_first_req,
+                               a->num_groups, pl.ns_max, pl.npfx, sub_start, sub_src, vis1, vis2, ptab, stream);
   if (st != DSA_OK) return fail(st, "indexer_prefix: launch failed: %s", hipGetErrorString(hipGetLastError()));
   if (L > 0) {  // shared pages, once per group for all of its rows
     dsa_indexer_args a1 = base;
-    a1.batch.num_requests = a->num_groups;
-    a1.batch.req_row_start = a->group_row_start;
+    a1.batch.num_requests = pl.ns_max;  // sub-groups of at most kPrefixSubRows rows (empty ones at the end)
+    a1.batch.req_row_start = sub_start;
     a1.batch.tok_vis = vis1;
     a1.batch.block_table = ptab;
     a1.batch.bt_stride = pl.npfx;
     a1.batch.max_vis = L;
-    a1.batch.max_rows_per_req = a->max_rows_per_group;
+    a1.batch.max_rows_per_req = std::min(a->max_rows_per_group, dsa::kPrefixSubRows);
     st = dsa_indexer_scores(&a1, stream);
     if (st != DSA_OK) return st;
   }

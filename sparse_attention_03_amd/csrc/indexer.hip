@@ -509,32 +509,58 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
   for (int i = tid; i < kend - k0; i += 256) out[k0 + i] = sc_out[i];
 }
 
-// Shared-prefix plan: the visible counts of the prefix and suffix passes, and
-// the prefix pages of every group (read from the block-table row of one of
-// its requests).
+// Shared-prefix plan.  Groups are cut into sub-groups of at most
+// kPrefixSubRows rows (serially, one thread: there are few groups), padded
+// with empty sub-groups up to the bound the host sized the grid for; then the
+// visible counts of the prefix and suffix passes, and every sub-group's copy
+// of its group's prefix pages (read from the block-table row of one of its
+// requests; a bad request id gives absent pages).
+__global__ void prefix_groups_kernel(const int32_t* __restrict__ grs, int G, int T, int ns_max,
+                                     int32_t* __restrict__ sub_start, int32_t* __restrict__ sub_src) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  int ns = 0;
+  for (int g = 0; g < G && ns < ns_max; ++g) {
+    const int s = min(max(grs[g], 0), T), e = min(max(grs[g + 1], s), T);
+    for (int x = s; x < e && ns < ns_max; x += kPrefixSubRows) {
+      sub_start[ns] = x;
+      sub_src[ns] = g;
+      ++ns;
+    }
+  }
+  for (; ns < ns_max; ++ns) {
+    sub_start[ns] = T;
+    sub_src[ns] = -1;
+  }
+  sub_start[ns_max] = T;
+}
+
 __global__ void prefix_prep_kernel(const int32_t* __restrict__ tok_vis, int T, int max_vis, int L,
                                    const int32_t* __restrict__ bt, int bt_stride, int R,
-                                   const int32_t* __restrict__ first_req, int G, int npfx, int32_t* __restrict__ vis1,
-                                   int32_t* __restrict__ vis2, int32_t* __restrict__ ptab) {
+                                   const int32_t* __restrict__ first_req, const int32_t* __restrict__ sub_src,
+                                   int ns, int npfx, int32_t* __restrict__ vis1, int32_t* __restrict__ vis2,
+                                   int32_t* __restrict__ ptab) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < T) {
     const int v = min(max(tok_vis[i], 0), max_vis);
     vis1[i] = min(v, L);
     vis2[i] = max(v - L, 0);
   }
-  if (i < G * npfx) {
-    const int g = i / npfx, j = i - g * npfx;
-    const int r = first_req[g];
-    ptab[i] = (r >= 0 && r < R) ? bt[(int64_t)r * bt_stride + j] : -1;  // (a bad request id: absent pages)
+  if (i < ns * npfx) {
+    const int q = i / npfx, j = i - q * npfx;
+    const int g = sub_src[q];
+    const int r = g >= 0 ? first_req[g] : -1;
+    ptab[i] = (r >= 0 && r < R) ? bt[(int64_t)r * bt_stride + j] : -1;
   }
 }
 
 dsa_status launch_prefix_prep(const int32_t* tok_vis, int T, int max_vis, int L, const int32_t* bt, int bt_stride,
-                              int R, const int32_t* first_req, int G, int npfx, int32_t* vis1, int32_t* vis2,
-                              int32_t* ptab, hipStream_t stream) {
-  const int n = max(T, G * npfx);
+                              int R, const int32_t* grs, const int32_t* first_req, int G, int ns_max, int npfx,
+                              int32_t* sub_start, int32_t* sub_src, int32_t* vis1, int32_t* vis2, int32_t* ptab,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(prefix_groups_kernel, dim3(1), dim3(64), 0, stream, grs, G, T, ns_max, sub_start, sub_src);
+  const int n = max(T, ns_max * npfx);
   hipLaunchKernelGGL(prefix_prep_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, tok_vis, T, max_vis, L, bt,
-                     bt_stride, R, first_req, G, npfx, vis1, vis2, ptab);
+                     bt_stride, R, first_req, sub_src, ns_max, npfx, vis1, vis2, ptab);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 
