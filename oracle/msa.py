@@ -24,7 +24,10 @@ Readings (where the page leaves a step open; the design notes list them):
     same for V (2 * Hkv * 128 bytes), each tensor with one fp32 scale;
   * attention: query head h belongs to group h // (Hq / Hkv) and uses that
     group's K and V head; logits sm_scale * q_h . k_s over the visible keys of
-    the selected blocks; natural-base softmax; o_h = sum p_s v_s, lse in nats.
+    the selected blocks; natural-base softmax; o_h = sum p_s v_s, lse in nats;
+  * an absent block (block-table entry < 0 or past the pool) has score -inf
+    and its tokens are never attended; a row with no attended token gives
+    o = 0 and lse = -inf.
 """
 from __future__ import annotations
 
@@ -76,13 +79,23 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float):
     return (e @ np.asarray(v, np.float64)) / z[:, None], mx + np.log(z)
 
 
-def request_index_keys(idx_pool: np.ndarray, block_table: np.ndarray, r: int, n: int) -> np.ndarray:
-    """Dequantised index keys of tokens 0..n-1 of request r: [n, 128].  The
-    pool is [pool_blocks, 128 * 128] E4M3 bytes (128 tokens per block)."""
-    nb = -(-n // BLOCK)
+def present(block_table: np.ndarray, r: int, nb: int, pool_blocks: int) -> np.ndarray:
+    """Which of request r's first nb logical blocks map into the pool."""
     pages = block_table[r, :nb]
-    codes = idx_pool[pages].reshape(nb * BLOCK, DIM)[:n]
-    return e4m3(codes)
+    return (pages >= 0) & (pages < pool_blocks)
+
+
+def request_index_keys(idx_pool: np.ndarray, block_table: np.ndarray, r: int, n: int) -> np.ndarray:
+    """Dequantised index keys of tokens 0..n-1 of request r: [n, 128] (zeros
+    for tokens of absent blocks).  The pool is [pool_blocks, 128 * 128] E4M3
+    bytes (128 tokens per block)."""
+    nb = -(-n // BLOCK)
+    ok = present(block_table, r, nb, idx_pool.shape[0])
+    pages = np.where(ok, block_table[r, :nb], 0)
+    codes = idx_pool[pages].reshape(nb * BLOCK, DIM)
+    vals = e4m3(codes)
+    vals[np.repeat(~ok, BLOCK)] = 0.0
+    return vals[:n]
 
 
 def request_kv(kv_pool: np.ndarray, block_table: np.ndarray, r: int, blocks: np.ndarray, n: int, hkv: int,
@@ -90,7 +103,9 @@ def request_kv(kv_pool: np.ndarray, block_table: np.ndarray, r: int, blocks: np.
     """K and V of group g for the tokens of the given logical blocks that are
     < n, in token order: ([m, 128], [m, 128]).  kv_pool is [pool_blocks,
     128 * 2 * hkv * 128] E4M3 bytes."""
-    parts = [np.arange(b * BLOCK, min(n, (b + 1) * BLOCK)) for b in blocks]
+    nb_all = block_table.shape[1]
+    ok = present(block_table, r, nb_all, kv_pool.shape[0])
+    parts = [np.arange(b * BLOCK, min(n, (b + 1) * BLOCK)) for b in blocks if ok[b]]
     tok = np.concatenate(parts) if parts else np.zeros(0, np.int64)
     per_page = kv_pool.reshape(kv_pool.shape[0], BLOCK, 2, hkv, DIM)
     pages = block_table[r, tok // BLOCK]
@@ -101,7 +116,7 @@ def request_kv(kv_pool: np.ndarray, block_table: np.ndarray, r: int, blocks: np.
 
 def msa_row(inp: dict, t: int):
     """One query row through the whole MSA decode step.  Returns (sel [Hkv,
-    top_blocks] with -1 padding, o [Hq, 128], lse [Hq])."""
+    top_blocks] with -1 padding, o [Hq, 128], lse [Hq], block scores [Hkv, nb])."""
     r = int(inp["tok_req"][t])
     n = int(inp["tok_vis"][t])
     hkv, hq, top = int(inp["hkv"]), int(inp["hq"]), int(inp["top_blocks"])
@@ -110,6 +125,7 @@ def msa_row(inp: dict, t: int):
     keys = request_index_keys(inp["idx_pool"], bt, r, n)
     sc = index_scores(inp["q_idx"][t], keys)
     bs = block_max(sc)
+    bs[:, ~present(bt, r, bs.shape[1], inp["idx_pool"].shape[0])] = -np.inf
     sel = np.full((hkv, top), -1, np.int64)
     o = np.zeros((hq, DIM))
     lse = np.zeros(hq)

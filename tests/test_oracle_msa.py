@@ -165,3 +165,19 @@ def test_planted_blocks_are_selected():
         top = np.sort(bs[g][:-1])[::-1]
         assert top[14] > 2 * max(top[15], 0) + 100  # the gap below the 15 planted blocks
         assert sel[g][-1] == 40
+
+
+def test_absent_blocks():
+    # block 2 of request 0 absent: its score is -inf, it is never attended;
+    # a row whose every selected block is absent gives o = 0, lse = -inf
+    spec, inp = _tiny(seed=11, N=128 * 6, rows=1, top=3)
+    inp["block_table"] = inp["block_table"].copy()
+    inp["block_table"][0, 2] = -1
+    sel, o, lse, bs = M.msa_row(inp, 0)
+    assert np.all(bs[:, 2] == -np.inf)
+    for g in range(spec.hkv):
+        assert 2 not in sel[g].tolist() and sel[g][-1] == 5
+    inp["block_table"][0, :] = -1
+    sel, o, lse, bs = M.msa_row(inp, 0)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+    assert [x for x in sel[0] if x >= 0] == [0, 1, 5]     # ties at -inf: the lower ids
