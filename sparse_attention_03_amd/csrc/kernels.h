@@ -82,7 +82,7 @@ struct MergeParams {
   int32_t* count;       // [T] or null
   // workspace
   int32_t* lvis;        // [W*T] local visible counts (shard row r*T + t)
-  int32_t* lvis2;       // [W*T] round-2 local counts: lvis for flagged shard rows, else 0
+  int32_t* lvis2;       // [W*T] re-send local counts: lvis for flagged shard rows, else 0
   int32_t* lidx;        // [W*T][cand] then [W*T][k]: selected local positions
   uint64_t* xbuf;       // [W*T][k] exchange buffer: composites each shard row sent
   int32_t* xcnt;        // [W*T] composites sent

@@ -54,15 +54,16 @@ __global__ __launch_bounds__(256) void shard_vis_kernel(MergeParams p) {
 }
 
 // One workgroup per shard row (r, t): the shard's selected local positions
-// (ascending, `kk` per row: cand in round 1, k in round 2) -> composites in
-// the exchange buffer.  Round 2 packs only the flagged shard rows.
-__global__ __launch_bounds__(kPackThreads) void pack_kernel(MergeParams p, int round) {
+// (ascending, `kk` per row: cand in the first exchange, k in the re-send)
+// -> composites in the exchange buffer.  The re-send packs only the flagged
+// shard rows.
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(MergeParams p, int phase) {
   const int sr = blockIdx.x;  // r * T + t
   const int r = sr / p.T, t = sr - r * p.T;
   const int tid = threadIdx.x;
-  if (round == 2 && p.flags[t * p.W + r] == 0) return;
-  const int kk = round == 1 ? p.cand : p.k;
-  const int m = min(kk, round == 1 ? p.lvis[sr] : p.lvis2[sr]);
+  if (phase == 2 && p.flags[t * p.W + r] == 0) return;
+  const int kk = phase == 1 ? p.cand : p.k;
+  const int m = min(kk, phase == 1 ? p.lvis[sr] : p.lvis2[sr]);
   const int32_t* lidx = p.lidx + (int64_t)sr * kk;
   const float* row = p.scores + (int64_t)sr * p.ld;
   uint64_t* out = p.xbuf + (int64_t)sr * p.k;
@@ -75,8 +76,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(MergeParams p, int r
 }
 
 // One workgroup per query row: select from the union of the shards' messages,
-// decide the re-sends (round 1), emit the ascending global indices.
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int round) {
+// decide the re-sends (first exchange), emit the ascending global indices.
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int phase) {
   __shared__ RadixLds<uint64_t, kMergeThreads> L;
   __shared__ int s_pre[kMaxShards + 1];
   __shared__ int s_sel[kMaxShards];
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int W = p.W;
-  if (round == 2 && p.rowflag[t] == 0) return;
+  if (phase == 2 && p.rowflag[t] == 0) return;
   const int vis = clamp_vis(p, t);
   const int K = min(p.k, vis);
   int32_t* idx = p.idx + (int64_t)t * p.k;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
     });
   }
   __syncthreads();
-  if (round == 1 && tid < W) {
+  if (phase == 1 && tid < W) {
     const int r = tid;
     const int n = shard_count(vis, r, W);
     const int sent = s_pre[r + 1] - s_pre[r];
@@ -150,9 +151,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
     if (flag) atomicOr(&s_any, 1);
   }
   __syncthreads();
-  if (round == 1) {
+  if (phase == 1) {
     if (tid == 0) p.rowflag[t] = s_any;
-    if (s_any) return;  // emitted by round 2
+    if (s_any) return;  // emitted after the re-send
   }
 
   // ascending global indices: gather the winners into 2048 slots (padding
@@ -216,7 +217,7 @@ dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hi
   const int n = p.W * p.T;
   hipLaunchKernelGGL(shard_vis_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
-  // round 1: every shard row selects its cand best positions
+  // first exchange: every shard row selects its cand best positions
   TopkParams l1 = local;
   l1.tok_vis = p.lvis;
   l1.k = p.cand;
@@ -224,7 +225,7 @@ dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hi
   if (st != DSA_OK) return st;
   hipLaunchKernelGGL(pack_kernel, dim3(n), dim3(kPackThreads), 0, stream, p, 1);
   hipLaunchKernelGGL(merge_kernel, dim3(p.T), dim3(kMergeThreads), 0, stream, p, 1);
-  // round 2: flagged shard rows select their full local top-k (every other
+  // re-send: flagged shard rows select their full local top-k (every other
   // shard row has lvis2 = 0 and its workgroups return at once)
   TopkParams l2 = local;
   l2.tok_vis = p.lvis2;

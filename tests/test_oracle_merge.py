@@ -21,7 +21,7 @@ def brute_topk(row, vis, k):
 
 
 def brute_flags(row, vis, W, k, cand):
-    """Round-1 detection written out with Python sorting only."""
+    """First-exchange detection written out with Python sorting only."""
     K = min(k, vis)
     sent = []
     for r in range(W):
@@ -80,7 +80,7 @@ def test_all_equal_scores_flag_every_shard():
 
 
 def test_one_shard_holds_the_top():
-    # W=4, k=8, cand=3, vis=1000, score 1 on tokens 0 mod 4, else 0.  Round 1:
+    # W=4, k=8, cand=3, vis=1000, score 1 on tokens 0 mod 4, else 0.  First exchange:
     # shard 0 sends 0,4,8 (all selected: flagged); the other five places go to
     # the lowest score-0 indices 1,2,3,5,6 (shards 1,2,3 keep a loser each).
     # After shard 0 re-sends 8 candidates the result is 0,4,...,28.
