@@ -172,19 +172,18 @@ __global__ __launch_bounds__(256) void msa_select_kernel(MsaParams p) {
     }
   });
   __syncthreads();
-  if (tid == 0) {
-    int n = min(s_n, p.top - 1);
-    s_sel[n++] = nb - 1;
-    for (int i = 1; i < n; ++i) {  // insertion sort of at most 16 ids
-      const int v = s_sel[i];
-      int j = i - 1;
-      while (j >= 0 && s_sel[j] > v) {
-        s_sel[j + 1] = s_sel[j];
-        --j;
-      }
-      s_sel[j + 1] = v;
-    }
-    for (int j = 0; j < p.top; ++j) out[j] = j < n ? s_sel[j] : -1;
+  // the most recent block joins the winners; every id's output slot is its
+  // rank among them (ids are distinct), one thread per id
+  const int n = min(s_n, p.top - 1) + 1;
+  if (tid == 0) s_sel[n - 1] = nb - 1;
+  __syncthreads();
+  if (tid < n) {
+    const int v = s_sel[tid];
+    int rank = 0;
+    for (int i = 0; i < n; ++i) rank += s_sel[i] < v;
+    out[rank] = v;
+  } else if (tid < p.top) {
+    out[tid] = -1;
   }
 }
 
