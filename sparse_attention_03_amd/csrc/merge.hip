@@ -103,17 +103,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
     s_slot = 0;
   }
   __syncthreads();
-  if (tid == 0)
-    for (int r = 1; r <= W; ++r) s_pre[r] += s_pre[r - 1];
+  if (tid < 64) {  // inclusive scan of the counts by the first wave (W <= 16)
+    const uint32_t v = tid < W ? (uint32_t)s_pre[tid + 1] : 0u;
+    const uint32_t inc = wave_incl_scan32(v);
+    if (tid < W) s_pre[tid + 1] = (int)inc;
+  }
   __syncthreads();
   const int ntot = s_pre[W];
+  // shard starts in registers: an element's shard is the number of starts
+  // at or below it (independent compares, no dependent LDS reads)
+  int pre[kMaxShards];
+#pragma unroll
+  for (int q = 0; q < kMaxShards; ++q) pre[q] = q < W ? s_pre[q] : 0x7fffffff;
 
   // the union: staged in LDS when it fits, else read from the exchange buffer
   // (L2-resident) on every pass
   auto comp_at = [&](int e) {
-    int r = 0;
-    while (r + 1 < W && s_pre[r + 1] <= e) ++r;
-    return p.xbuf[(int64_t)(r * p.T + t) * p.k + (e - s_pre[r])];
+    int r = -1, base = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxShards; ++q) {
+      if (pre[q] <= e) {
+        r = q;
+        base = pre[q];
+      }
+    }
+    return p.xbuf[(int64_t)(r * p.T + t) * p.k + (e - base)];
   };
   const bool staged = ntot <= kMergeLdsCap;
   if (staged) {
