@@ -5,11 +5,18 @@ MI355X, on seeded synthetic caches shaped like the serving workloads.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Prints ONE JSON line.  `value` is the algorithmic HBM throughput of the whole
-step (GB/s: bytes the method must move / measured step time, inputs resident in
-HBM); µs per step, query tokens/s and the per-stage split ride along.
-`roofline` covers the dominant kernel (timed with HIP events on the launch
-stream); `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
-same workload.
+step (GB/s: bytes the method must move / the median step time, inputs resident
+in HBM); µs per step, query tokens/s and the per-stage split ride along.
+
+Timing protocol: W untimed warm-up steps, then K timed steps, each preceded by
+a 1 GiB read-modify-write scrub on the same stream (outside the step's events)
+so that no step finds the previous step's data in L2 or the 256 MB MALL; every
+step is bracketed by HIP events on the launch stream, and the median, p10 and
+p90 over the K steps are reported (the back-to-back mean without scrubs rides
+along as `warm_us`).  Besides the headline workload, the other reference
+workloads are timed the same way under `workloads`.  `roofline` covers the
+headline's dominant kernel; `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the headline workload, with all host cores and with one.
 """
 from __future__ import annotations
 
@@ -32,9 +39,12 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="tp8_spec_decode_64k")
+    ap.add_argument("--others", type=int, default=1,
+                    help="also time the other reference workloads under `workloads` (0 = skip)")
+    ap.add_argument("--scrub-mib", type=int, default=1024, help="cache scrub before every timed step (0 = none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--shards", type=int, default=8,
@@ -79,16 +89,19 @@ def measured_traffic(workload: str, stage: str):
     return int(st["fetch_bytes"] + st["write_bytes"])
 
 
-def cpu_baseline(wl, seconds, bytes_of_rows):
-    """Time the oracle, request by request, until `seconds` have elapsed."""
-    from oracle import dsa as O
-    from tests.helpers import oracle_inputs
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
-    inp = oracle_inputs(wl)
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_run(inp, wl, seconds, bytes_of_rows):
+    from oracle import dsa as O
     rts = wl.req_token_start.cpu().tolist()
     done_rows, elapsed, reqs = [], 0.0, 0
     for r in range(wl.R):
@@ -100,10 +113,28 @@ def cpu_baseline(wl, seconds, bytes_of_rows):
         reqs += 1
         if elapsed >= seconds:
             break
-    nbytes = bytes_of_rows(reqs, done_rows)
-    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reqs} of {wl.R} requests ({len(done_rows)} query rows), fp64 NumPy, "
-                      f"{elapsed:.2f} s; same algorithmic-byte accounting as value"}
+    return reqs, done_rows, elapsed, bytes_of_rows(reqs, done_rows) / elapsed / 1e9
+
+
+def cpu_baseline(wl, seconds, bytes_of_rows):
+    """Time the oracle, request by request, until `seconds` have elapsed: once
+    with the BLAS pool at every host core, once on a single thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from tests.helpers import oracle_inputs
+    inp = oracle_inputs(wl)
+    ncpu = os.cpu_count() or 1
+    with threadpool_limits(limits=ncpu):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        reqs, rows, el, gbs = _oracle_run(inp, wl, seconds, bytes_of_rows)
+    with threadpool_limits(limits=1):
+        reqs1, rows1, el1, gbs1 = _oracle_run(inp, wl, seconds, bytes_of_rows)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": ncpu,
+            "one_thread": {"value": round(gbs1, 4), "cores": 1, "requests": reqs1, "rows": len(rows1),
+                           "seconds": round(el1, 2)},
+            "sample": f"{reqs} of {wl.R} requests ({len(rows)} query rows), fp64 NumPy with {threads} BLAS "
+                      f"threads, {el:.2f} s; same algorithmic-byte accounting as value"}
 
 
 def main():
@@ -125,53 +156,94 @@ def main():
 
     dsa.load()
     dev = torch.device("cuda:0")
-    spec = synth.CONFIGS[args.workload]
-    t0 = time.time()
-    wl = synth.make_workload(spec, device=dev)
-    torch.cuda.synchronize()
-    print(f"[bench] workload {spec.name} generated in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
-    prefill = spec.q_per_req > 64
-    step = dsa.make_step(key_pool=wl.key_pool, lat_pool=wl.lat_pool, page_size=wl.P, key_fmt=spec.key_fmt,
-                         lat_fmt=spec.lat_fmt, req_row_start=wl.req_token_start, tok_req=wl.tok_req,
-                         tok_vis=wl.tok_vis, block_table=wl.block_table, q_idx=wl.q_idx, w=wl.w,
-                         q_mla=wl.q_mla, k=spec.k, sm_scale=spec.sm_scale, q_idx_scale=wl.q_idx_scale,
-                         prefill=prefill, max_vis=spec.N, max_rows_per_req=spec.q_per_req)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    K = args.steps
     E = torch.cuda.Event
-    ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    start, end = E(enable_timing=True), E(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        ev[i][0].record()
-        step.indexer()
-        ev[i][1].record()
-        step.topk()
-        ev[i][2].record()
-        step.mla()
-        ev[i][3].record()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
-    st = {n: sum(ev[i][a].elapsed_time(ev[i][b]) for i in range(K)) / K
-          for n, a, b in (("indexer", 0, 1), ("topk", 1, 2), ("mla", 2, 3))}
+    K = args.steps
+    scrub = torch.zeros(args.scrub_mib * (1 << 20) // 4, dtype=torch.float32, device=dev) if args.scrub_mib else None
 
-    vis = wl.tok_vis.cpu().tolist()
-    rts = wl.req_token_start.cpu().tolist()
-    req_vis = [max(vis[rts[r]:rts[r + 1]]) for r in range(wl.R)]
-    page = 0 if spec.page == 0 else wl.P
-    B = BM.step_bytes(req_vis_max=req_vis, row_vis=vis, k=spec.k, H=spec.H, key_fmt=spec.key_fmt,
-                      lat_fmt=spec.lat_fmt, q_fmt=spec.q_fmt, page=page)
-    F = BM.step_flops(row_vis=vis, k=spec.k, H=spec.H)
-    us = ms_step * 1e3
+    def build(spec):
+        t0 = time.time()
+        wl = synth.make_workload(spec, device=dev)
+        torch.cuda.synchronize()
+        print(f"[bench] workload {spec.name} generated in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+        step = dsa.make_step(key_pool=wl.key_pool, lat_pool=wl.lat_pool, page_size=wl.P, key_fmt=spec.key_fmt,
+                             lat_fmt=spec.lat_fmt, req_row_start=wl.req_token_start, tok_req=wl.tok_req,
+                             tok_vis=wl.tok_vis, block_table=wl.block_table, q_idx=wl.q_idx, w=wl.w,
+                             q_mla=wl.q_mla, k=spec.k, sm_scale=spec.sm_scale, q_idx_scale=wl.q_idx_scale,
+                             prefill=spec.q_per_req > 64, max_vis=spec.N, max_rows_per_req=spec.q_per_req)
+        return wl, step
+
+    def time_step(step, n=K, warmup=args.warmup):
+        """n scrubbed steps with per-stage events; then n back-to-back steps."""
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            if scrub is not None:
+                scrub.add_(1.0)  # reads and writes 1 GiB: evicts L2 and the MALL
+            ev[i][0].record()
+            step.indexer()
+            ev[i][1].record()
+            step.topk()
+            ev[i][2].record()
+            step.mla()
+            ev[i][3].record()
+        torch.cuda.synchronize()
+        per = {nm: [ev[i][a].elapsed_time(ev[i][b]) for i in range(n)]
+               for nm, a, b in (("indexer", 0, 1), ("topk", 1, 2), ("mla", 2, 3), ("step", 0, 3))}
+        w0, w1 = E(enable_timing=True), E(enable_timing=True)
+        w0.record()
+        for _ in range(n):
+            step()
+        w1.record()
+        torch.cuda.synchronize()
+        return per, w0.elapsed_time(w1) / n
+
+    def pct(xs, q):
+        ys = sorted(xs)
+        return ys[min(len(ys) - 1, max(0, int(round(q * (len(ys) - 1)))))]
+
+    def summarise(spec, wl, per, warm_ms):
+        vis = wl.tok_vis.cpu().tolist()
+        rts = wl.req_token_start.cpu().tolist()
+        req_vis = [max(vis[rts[r]:rts[r + 1]]) for r in range(wl.R)]
+        page = 0 if spec.page == 0 else wl.P
+        B = BM.step_bytes(req_vis_max=req_vis, row_vis=vis, k=spec.k, H=spec.H, key_fmt=spec.key_fmt,
+                          lat_fmt=spec.lat_fmt, q_fmt=spec.q_fmt, page=page)
+        F = BM.step_flops(row_vis=vis, k=spec.k, H=spec.H)
+        med = pct(per["step"], 0.5)
+        stages = {n: pct(per[n], 0.5) for n in ("indexer", "topk", "mla")}
+        rec = {"us_median": round(med * 1e3, 2), "us_p10": round(pct(per["step"], 0.1) * 1e3, 2),
+               "us_p90": round(pct(per["step"], 0.9) * 1e3, 2), "warm_us": round(warm_ms * 1e3, 2),
+               "tokens_per_s": round(wl.T / (med * 1e-3), 1), "alg_bytes": B["total"],
+               "alg_GB_per_s": round(B["total"] / (med * 1e-3) / 1e9, 2),
+               "roofline_frac": round(B["total"] / (PEAK_HBM_GBS * 1e9) / (med * 1e-3), 4),
+               "literal_formula_roofline_us": round(BM.literal_formula_bytes(wl.T, spec.N, spec.k) / 8e12 * 1e6, 2),
+               "stages_us_median": {n: round(v * 1e3, 2) for n, v in stages.items()},
+               "indexer_flop": F["indexer"], "mla_flop": F["mla"]}
+        if spec.q_per_req > 64:
+            # the prefill chunk is bound by the FP8 matrix instructions of its indexer
+            rec["indexer_fp8_mfma_frac"] = round(F["indexer"] / (stages["indexer"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
+            rec["mla_bf16_mfma_frac"] = round(F["mla"] / (stages["mla"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        return rec, B, F, vis, req_vis, page, stages, med
+
+    spec = synth.CONFIGS[args.workload]
+    wl, step = build(spec)
+    prefill = spec.q_per_req > 64
+    per, warm_ms = time_step(step)
+    head, B, F, vis, req_vis, page, st_med, ms_step = summarise(spec, wl, per, warm_ms)
+    st = st_med
     value = B["total"] / (ms_step * 1e-3) / 1e9
+    # with fewer than 100 timed steps, the same statistics over 100 more
+    # scrubbed steps (after the timed region; not part of `value`)
+    head100 = None
+    if K < 100:
+        per100, warm100 = time_step(step, n=100, warmup=0)
+        head100 = summarise(spec, wl, per100, warm100)[0]
 
-    # dominant kernel and its roofline
+    # dominant kernel and its roofline (median launch durations over the K
+    # scrubbed steps)
     dom = max(st, key=st.get)
     t_dom = st[dom] * 1e-3
     if dom == "indexer":
@@ -199,6 +271,7 @@ def main():
     roof["traffic"] = measured_traffic(spec.name, dom)
     roof["achieved"] = round(roof["achieved"], 2)
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["launch_us_median"] = round(t_dom * 1e6, 2)
 
     # The step's front end, timed apart from the step (not part of the metric):
     # every query row's own token is the newest visible one of its request, so
@@ -210,7 +283,7 @@ def main():
         key_new = torch.randn(wl.T, 128, generator=g, device=dev).to(torch.bfloat16)
         lat_new = torch.randn(wl.T, 576, generator=g, device=dev).to(torch.bfloat16)
         pos_new = (wl.tok_vis - 1).to(torch.int32).contiguous()
-        q_fmt_fe = "mxfp4" if spec.key_fmt == "mxfp4" else "fp8"
+        q_fmt_fe = "fp8" if spec.key_fmt == "fp8" else "mxfp4"
 
         def front_end():
             dsa.quantize_q(wl.q_idx if wl.q_idx.dtype == torch.bfloat16 else key_new.new_zeros(wl.T, 32, 128),
@@ -238,7 +311,7 @@ def main():
         torch.cuda.synchronize()
         fe_ms = f0.elapsed_time(f1) / K
         backlog_ok = host_ms < n_busy * ms_step
-        key_b = {"fp8": 132, "mxfp4": 68}[spec.key_fmt]
+        key_b = BM.KEY_B[spec.key_fmt]
         lat_b = {"bf16": 1152, "fp8": 580, "nvfp4": 352}[spec.lat_fmt]
         q_out = 32 * (128 + 4 + 4) if q_fmt_fe == "fp8" else 32 * (64 + 4)
         fe_bytes = wl.T * (32 * 128 * 2 + 32 * 4 + q_out + 128 * 2 + 576 * 2 + 8 + key_b + lat_b)
@@ -387,6 +460,25 @@ def main():
                               key_fmt=spec.key_fmt, lat_fmt=spec.lat_fmt, q_fmt=spec.q_fmt, page=page)
             return b["total"]
         cpu = cpu_baseline(wl, args.cpu_seconds, bytes_of_rows)
+    del step, wl
+    torch.cuda.empty_cache()
+
+    # the other reference workloads, timed by the same protocol
+    others = {}
+    if args.others:
+        for name, ospec in synth.CONFIGS.items():
+            if name == spec.name:
+                continue
+            owl, ostep = build(ospec)
+            oper, owarm = time_step(ostep, n=max(K, 100))
+            orec = summarise(ospec, owl, oper, owarm)[0]
+            orec["config"] = {"requests": ospec.R, "rows_per_request": ospec.q_per_req, "context": ospec.N,
+                              "key_fmt": ospec.key_fmt, "latent_fmt": ospec.lat_fmt, "index_q_fmt": ospec.q_fmt,
+                              "mla_heads": ospec.H, "topk": ospec.k}
+            others[name] = orec
+            print(f"[bench] {name}: {orec['us_median']} us median", file=sys.stderr, flush=True)
+            del owl, ostep
+            torch.cuda.empty_cache()
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -395,14 +487,19 @@ def main():
         "config": {"workload": spec.name, "requests": spec.R, "rows_per_request": spec.q_per_req,
                    "context": spec.N, "page": spec.page, "key_fmt": spec.key_fmt, "latent_fmt": spec.lat_fmt,
                    "index_q_fmt": spec.q_fmt, "mla_heads": spec.H, "topk": spec.k},
-        "us_per_step": round(us, 2),
-        "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
+        "timing": {"statistic": "median of K steps, each after a cache scrub", "scrub_mib": args.scrub_mib,
+                   "us_p10": head["us_p10"], "us_p90": head["us_p90"], "warm_us": head["warm_us"],
+                   "steps_100": None if head100 is None else
+                   {k2: head100[k2] for k2 in ("us_median", "us_p10", "us_p90", "warm_us", "stages_us_median")}},
+        "us_per_step": head["us_median"],
+        "tokens_per_s": head["tokens_per_s"],
         "alg_bytes": B["total"],
-        "step_roofline_frac": round(B["total"] / (PEAK_HBM_GBS * 1e9) / (ms_step * 1e-3), 4),
-        "literal_formula_roofline_us": round(BM.literal_formula_bytes(wl.T, spec.N, spec.k) / 8e12 * 1e6, 2),
-        "stages_us": {k2: round(v * 1e3, 2) for k2, v in st.items()},
+        "step_roofline_frac": head["roofline_frac"],
+        "literal_formula_roofline_us": head["literal_formula_roofline_us"],
+        "stages_us": head["stages_us_median"],
         "roofline": roof,
         "cpu_baseline": cpu,
+        "workloads": others,
         "front_end": fe,
         "sharded_topk": shard,
         "msa": msa,

@@ -22,9 +22,13 @@
  *     fallback to another path.  dsa_last_error() describes the last failure
  *     of the calling thread.
  *   - Device-resident metadata (visible counts, block-table entries, row ids)
- *     cannot be checked on the host.  Kernels bound every access by them: a
- *     block-table entry outside [0, num_pages) makes its keys score -inf and
- *     its latent rows count as absent; visible counts are clamped to max_vis.
+ *     cannot be checked on the host.  Kernels bound every access by them;
+ *     visible counts are clamped to max_vis.  A block-table entry outside
+ *     [0, num_pages) names no page (an absent page) and nothing is read from
+ *     it: the indexer writes -inf as the score of its tokens, the top-k ranks
+ *     -inf below every finite score (equal -inf scores by lower index, like
+ *     any tie) and translation turns its tokens into row -1, which attention
+ *     skips, as it skips any row id < 0 or past the pool's last row.
  *   - No global mutable state: calls are re-entrant and may run concurrently
  *     on different streams with different buffers.
  *
@@ -35,6 +39,11 @@
  * region starting on a 16-byte boundary:
  *     key   FP8    [P x 128 E4M3][P x fp32 scale]                     132 B/token
  *     key   MXFP4  [P x 64 B E2M1 pairs, low nibble first][P x 4 E8M0]  68 B/token
+ *     key   NVFP4  [P x 64 B E2M1 pairs, low nibble first]
+ *                  [P x 8 E4M3 block scales, one per 16 dims]            72 B/token
+ * (NVFP4 index keys: MiniMax-M3.1-Flash day-0 page, "Quick start" and AMD
+ * "NVFP4 indexer DCP"; a value is E2M1 x its block scale, no second-level
+ * scale.)
  * Latent rows are gathered one by one, so a latent page is P rows, each row
  * padded to whole 128-byte lines and holding all of its bytes (a gathered row
  * then fetches only its own lines; page_bytes a multiple of 128 keeps rows
@@ -66,7 +75,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 #define DSA_INDEX_HEADS 32
 #define DSA_INDEX_DIM 128
 #define DSA_LATENT_DIM 576
@@ -83,7 +92,7 @@ typedef enum dsa_status {
 } dsa_status;
 
 /* Cache and query formats. */
-enum { DSA_KEY_FP8 = 1, DSA_KEY_MXFP4 = 2 };
+enum { DSA_KEY_FP8 = 1, DSA_KEY_MXFP4 = 2, DSA_KEY_NVFP4 = 3 };
 enum { DSA_LAT_BF16 = 1, DSA_LAT_FP8 = 2, DSA_LAT_NVFP4 = 3 };
 enum { DSA_Q_BF16 = 1, DSA_Q_FP8 = 2, DSA_Q_MXFP4 = 3 };
 
@@ -120,17 +129,28 @@ typedef struct dsa_batch {
  * For every row t and visible key s < tok_vis[t]:
  *     scores[t*ld + s] = sum_{h<32} w[t,h] * max(0, q[t,h,:] . k_s)
  * with k_s the dequantised key (FP8: codes x per-token scale; MXFP4: E2M1 x
- * 2^(E8M0-127) per 32 dims) and q BF16, or FP8 codes x q_scale[t,h].  Products
- * are exact and accumulate in fp32.  Positions >= tok_vis[t] are not written.
- * Rows of one request share each key load (speculative verify rows reuse keys,
- * same page, AMD "native MXFP4 indexer").  BF16 q runs on BF16 MFMA; FP8 q
- * runs on FP8 MFMA (the compute-bound prefill shape). */
+ * 2^(E8M0-127) per 32 dims; NVFP4: E2M1 x its E4M3 block scale per 16 dims)
+ * and q BF16, FP8 codes x q_scale[t,h], or MXFP4 (E2M1 x 2^(E8M0-127) per 32
+ * dims).  Products are exact and accumulate in fp32; keys on absent pages
+ * score -inf.  Positions >= tok_vis[t] are not written.  Rows of one request
+ * share each key load (speculative verify rows reuse keys, same page, AMD
+ * "native MXFP4 indexer").  BF16 q (any key format) runs on BF16 MFMA over
+ * keys dequantised exactly in registers; FP8 q (FP8 keys) on FP8 MFMA, the
+ * compute-bound prefill shape; MXFP4 q (MXFP4 keys) on the FP4 MFMA with the
+ * E8M0 scales applied by the instruction (the AMD section's native FP4 matrix
+ * instructions).  A request with more rows than max_rows_per_req still has
+ * every row scored.  Errors: DSA_ERR_INVALID_ARG for a bad batch or cache,
+ * null or unaligned pointers, ld below max_vis or not a multiple of 4;
+ * DSA_ERR_UNSUPPORTED for an unknown format or a q / key pairing other than
+ * the three above. */
 typedef struct dsa_indexer_args {
   dsa_batch batch;
-  dsa_cache keys;                /* fmt DSA_KEY_FP8 or DSA_KEY_MXFP4           */
-  const void* q;                 /* device [T,32,128]: bf16, or E4M3 codes     */
-  int32_t q_fmt;                 /* DSA_Q_BF16 or DSA_Q_FP8                    */
-  const float* q_scale;          /* device fp32 [T,32] for FP8 q, else NULL    */
+  dsa_cache keys;                /* fmt DSA_KEY_FP8, _MXFP4 or _NVFP4          */
+  const void* q;                 /* device: bf16 [T,32,128], E4M3 [T,32,128],
+                                    or E2M1 pairs [T,32,64], 16-byte aligned   */
+  int32_t q_fmt;                 /* DSA_Q_BF16, DSA_Q_FP8 or DSA_Q_MXFP4       */
+  const void* q_scale;           /* device: fp32 [T,32] (FP8 q), E8M0 uint8
+                                    [T,32,4] (MXFP4 q), else NULL              */
   const float* w;                /* device fp32 [T,32] head weights            */
   float* scores;                 /* device fp32 [T, ld]                        */
   int64_t ld;                    /* row stride of scores, >= max_vis, %4 == 0  */
@@ -184,18 +204,24 @@ typedef struct dsa_topk_args {
   int32_t* idx;                  /* device int32 [T, k]                        */
   int32_t* rows;                 /* device int32 [T, k] or NULL                */
   int32_t page_size_log2;        /* page size of the latent pool (rows != NULL)*/
+  int32_t num_pages;             /* pages of the latent pool (rows != NULL)    */
   int32_t* count;                /* device int32 [T] or NULL                   */
   void* workspace;               /* device, 256-byte aligned                   */
   size_t workspace_bytes;
 } dsa_topk_args;
 dsa_status dsa_topk(const dsa_topk_args* args, hipStream_t stream);
 
-/* dsa_translate_pages -- logical selected indices -> physical rows.
+/* dsa_translate_pages -- logical selected indices -> physical rows (Kimi K3.1
+ * Pro day-0 page, "One KV cache, three states": the block table becomes kernel
+ * page addresses before each step).
  * rows[t*k+j] = page * P + (i & (P-1)) with page = block_table[r*bt_stride +
- * (i >> p)], r = tok_req[t], i = idx[t*k+j]; -1 (or an index outside the
- * request's block-table row) stays -1.  Non-paged (block_table NULL): page = r. */
+ * (i >> p)], r = tok_req[t], i = idx[t*k+j]; -1, an index outside the
+ * request's block-table row, or a page outside [0, num_pages) gives -1.
+ * Non-paged (block_table NULL): page = r.  Errors: DSA_ERR_INVALID_ARG for a
+ * null pointer, k outside [1, 2048], num_rows < 1, page_size_log2 outside
+ * [4, 24], num_pages < 1 or num_pages x P above 2^31 - 1. */
 dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* batch,
-                               int32_t page_size_log2, int32_t* rows, hipStream_t stream);
+                               int32_t page_size_log2, int32_t num_pages, int32_t* rows, hipStream_t stream);
 
 /* dsa_topk_sharded -- the exact top-k merge of decode context parallelism,
  * its W shards emulated on this device (Kimi K3.1 Pro day-0 page, "Long

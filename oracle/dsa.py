@@ -22,14 +22,24 @@ taken here is the lightning-indexer form
 with k_s the dequantised key (codes x per-token scale).  MLA latents are 576-d
 (512 "nope" + 64 "rope"), V = the first 512 dims, softmax scale 1/sqrt(192).
 
-Page layout read here (structure-of-arrays inside a page of P tokens):
+Page layout read here (structure-of-arrays inside a key page of P tokens;
+latent pages are P padded rows, see lat_rows):
   key FP8    [P x 128 E4M3][P x fp32]
   key MXFP4  [P x 64 B E2M1 pairs][P x 4 E8M0]
-  lat BF16   [P x 576 bf16]
-  lat FP8    [P x 576 E4M3][P x fp32]
-  lat NVFP4  [P x 256 B E2M1 pairs][P x 32 E4M3 scales][P x 64 E4M3 rope]
+  key NVFP4  [P x 64 B E2M1 pairs][P x 8 E4M3 block scales, one per 16 dims]
 Logical token s of request r lives in physical page bt[r][s // P], slot s % P
 (non-paged caches: page r, slot s).  A physical row id is page * P + slot.
+
+Absent pages.  A block-table entry outside [0, num_pages) names no page
+("One KV cache, three states" gives the block table as the only map from a
+request's tokens to pages, so such an entry maps its tokens nowhere): the
+indexer scores its tokens -inf, so they rank below every present token (and
+among themselves by index), and translation gives their rows -1, which
+attention skips.  K_t = min(k, vis_t) is unchanged.
+
+MiniMax-M3.1 page ("Quick start": indexer_kv_dtype nvfp4; AMD "NVFP4 indexer
+DCP") keeps the index keys in NVFP4: E2M1 values with one E4M3 scale per 16
+values; no second-level scale is stored here (72 B per 128-d key).
 """
 from __future__ import annotations
 
@@ -45,8 +55,11 @@ HI, DI, D_LAT, D_V = 32, 128, 576, 512
 
 # ---------------------------------------------------------------- dequantise
 def key_pages(pool: np.ndarray, fmt: str, P: int, pages: np.ndarray) -> np.ndarray:
-    """Dequantise whole key pages -> fp64 [len(pages)*P, 128]."""
-    pg = pool[np.asarray(pages, dtype=np.int64)]
+    """Dequantise whole key pages -> fp64 [len(pages)*P, 128].  Every id must
+    name a page of the pool (absent pages are handled by request_keys)."""
+    pages = np.asarray(pages, dtype=np.int64)
+    assert np.all((pages >= 0) & (pages < pool.shape[0])), "page id outside the pool"
+    pg = pool[pages]
     n = pg.shape[0]
     if fmt == "fp8":
         codes = pg[:, : 128 * P].reshape(n, P, 128)
@@ -56,6 +69,10 @@ def key_pages(pool: np.ndarray, fmt: str, P: int, pages: np.ndarray) -> np.ndarr
         codes = pg[:, : 64 * P].reshape(n, P, 64)
         e = C.e8m0(pg[:, 64 * P: 68 * P].reshape(n, P, 4))
         vals = C.e2m1_packed(codes) * np.repeat(e, 32, axis=-1)
+    elif fmt == "nvfp4":
+        codes = pg[:, : 64 * P].reshape(n, P, 64)
+        sc = C.e4m3(pg[:, 64 * P: 72 * P].reshape(n, P, 8))
+        vals = C.e2m1_packed(codes) * np.repeat(sc, 16, axis=-1)
     else:
         raise ValueError(fmt)
     return vals.reshape(n * P, DI)
@@ -91,30 +108,49 @@ def lat_rows(pool: np.ndarray, fmt: str, P: int, rows: np.ndarray) -> np.ndarray
     raise ValueError(fmt)
 
 
-def request_pages(block_table: Optional[np.ndarray], r: int, n: int, P: int) -> np.ndarray:
+def request_pages(block_table: Optional[np.ndarray], r: int, n: int, P: int,
+                  num_pages: Optional[int] = None) -> np.ndarray:
     """Address translation for the scan side: logical pages 0..ceil(n/P)-1 of
-    request r -> physical page ids ([K31] "One KV cache, three states")."""
+    request r -> physical page ids ([K31] "One KV cache, three states"); an
+    entry outside [0, num_pages) is absent and returned as -1."""
     npg = (n + P - 1) // P
     if block_table is None:
         assert npg == 1, "non-paged cache holds a request in one page"
-        return np.array([r], dtype=np.int64)
-    return np.asarray(block_table[r, :npg], dtype=np.int64)
+        pages = np.array([r], dtype=np.int64)
+    else:
+        pages = np.asarray(block_table[r, :npg], dtype=np.int64)
+    if num_pages is not None:
+        pages = np.where((pages >= 0) & (pages < num_pages), pages, -1)
+    return pages
 
 
-def request_keys(pool, fmt, P, block_table, r, n) -> np.ndarray:
-    """Dequantised keys of logical tokens 0..n-1 of request r, fp64 [n, 128]."""
-    return key_pages(pool, fmt, P, request_pages(block_table, r, n, P))[:n]
+def request_keys(pool, fmt, P, block_table, r, n, with_present: bool = False):
+    """Dequantised keys of logical tokens 0..n-1 of request r, fp64 [n, 128].
+    Tokens on an absent page read as zeros; with_present=True also returns the
+    bool mask [n] of tokens whose page is present."""
+    pages = request_pages(block_table, r, n, P, num_pages=pool.shape[0])
+    ok = pages >= 0
+    keys = np.zeros((pages.shape[0] * P, DI))
+    if ok.any():
+        keys.reshape(pages.shape[0], P, DI)[ok] = key_pages(pool, fmt, P, pages[ok]).reshape(-1, P, DI)
+    present = np.repeat(ok, P)[:n]
+    return (keys[:n], present) if with_present else keys[:n]
 
 
-def translate(idx: np.ndarray, block_table: Optional[np.ndarray], r: int, P: int) -> np.ndarray:
-    """Selected logical indices -> physical rows page*P + slot; -1 stays -1."""
+def translate(idx: np.ndarray, block_table: Optional[np.ndarray], r: int, P: int,
+              num_pages: Optional[int] = None) -> np.ndarray:
+    """Selected logical indices -> physical rows page*P + slot; -1 stays -1,
+    and so does an index whose page is absent (outside [0, num_pages))."""
     idx = np.asarray(idx, dtype=np.int64)
     out = np.full(idx.shape, -1, dtype=np.int64)
     ok = idx >= 0
     li = idx[ok]
     page = np.full(li.shape, r, dtype=np.int64) if block_table is None \
         else np.asarray(block_table[r], dtype=np.int64)[li // P]
-    out[ok] = page * P + li % P
+    row = page * P + li % P
+    if num_pages is not None:
+        row = np.where((page >= 0) & (page < num_pages), row, -1)
+    out[ok] = row
     return out
 
 
@@ -178,9 +214,18 @@ def dense_mla(q: np.ndarray, lat_all: np.ndarray, sm_scale: float):
 
 # ---------------------------------------------------------------- one layer
 def dequant_q_idx(inp: dict, t: int) -> np.ndarray:
+    """Index query of row t as fp64 [32, 128]: BF16; FP8 codes x the per-head
+    fp32 scale; or MXFP4 (E2M1 pairs [32, 64] x 2^(E8M0 - 127) per 32 dims,
+    scales uint8 [32, 4]) -- the quantised query forms of [K31] "Low-latency
+    decoding: the fused DSA decode path" and AMD "native MXFP4 indexer"."""
     if inp["q_fmt"] == "bf16":
         return C.bf16(inp["q_idx"][t])
-    return C.e4m3(inp["q_idx"][t]) * np.asarray(inp["q_idx_scale"][t], np.float64)[:, None]
+    if inp["q_fmt"] == "fp8":
+        return C.e4m3(inp["q_idx"][t]) * np.asarray(inp["q_idx_scale"][t], np.float64)[:, None]
+    if inp["q_fmt"] == "mxfp4":
+        e = C.e8m0(inp["q_idx_scale"][t])                       # [32, 4]
+        return C.e2m1_packed(inp["q_idx"][t]) * np.repeat(e, 32, axis=-1)
+    raise ValueError(inp["q_fmt"])
 
 
 def layer(inp: dict, k: int = 2048, tokens=None, want_scores: bool = True):
@@ -204,15 +249,16 @@ def layer(inp: dict, k: int = 2048, tokens=None, want_scores: bool = True):
     key_cache = {}
     for t in tokens:
         r, n = int(tok_req[t]), int(vis[t])
-        if r not in key_cache or key_cache[r].shape[0] < n:
+        if r not in key_cache or key_cache[r][0].shape[0] < n:
             key_cache.clear()
             nmax = int(vis[rts[r]:rts[r + 1]].max())
-            key_cache[r] = request_keys(inp["key_pool"], inp["key_fmt"], P, bt, r, nmax)
-        keys = key_cache[r][:n]
+            key_cache[r] = request_keys(inp["key_pool"], inp["key_fmt"], P, bt, r, nmax, with_present=True)
+        keys, present = key_cache[r][0][:n], key_cache[r][1][:n]
         sc = indexer_scores(dequant_q_idx(inp, t), np.asarray(inp["w"][t], np.float64), keys)
+        sc = np.where(present, sc, -math.inf)
         sel, tau = topk(sc, k)
-        rows = translate(sel, bt, r, P)
-        lat = lat_rows(inp["lat_pool"], inp["lat_fmt"], P, rows)
+        rows = translate(sel, bt, r, P, num_pages=inp["lat_pool"].shape[0])
+        lat = lat_rows(inp["lat_pool"], inp["lat_fmt"], P, rows[rows >= 0])
         o, lse = sparse_mla(C.bf16(inp["q_mla"][t]), lat, inp["sm_scale"])
         out["t"].append(t)
         out["scores"].append(sc if want_scores else None)
@@ -225,12 +271,14 @@ def layer(inp: dict, k: int = 2048, tokens=None, want_scores: bool = True):
 
 
 def mla_on_rows(inp: dict, rows: np.ndarray, tokens=None):
-    """Sparse MLA alone, on given physical rows per query row ([T,k], -1 = none)."""
+    """Sparse MLA alone, on given physical rows per query row ([T,k]); entries
+    < 0 or past the pool's last row name no row and are skipped."""
     T = rows.shape[0]
     tokens = range(T) if tokens is None else tokens
     os, lses = [], []
+    n_rows = inp["lat_pool"].shape[0] * inp["P"]
     for t in tokens:
-        rr = rows[t][rows[t] >= 0]
+        rr = rows[t][(rows[t] >= 0) & (rows[t] < n_rows)]
         lat = lat_rows(inp["lat_pool"], inp["lat_fmt"], inp["P"], rr)
         o, lse = sparse_mla(C.bf16(inp["q_mla"][t]), lat, inp["sm_scale"])
         os.append(o)

@@ -16,7 +16,9 @@ pages give none; the readings table lists them):
              exponent field; E8M0 code = X + 127 clamped to 0..254;
              code = E2M1(x / 2^(E8M0 - 127))
   NVFP4      per 16 values s = E4M3(amax / 6); code = E2M1(x / value(s)),
-             0 when s decodes to 0; rope dims E4M3(x), unscaled
+             0 when s decodes to 0; rope dims E4M3(x), unscaled (latents);
+             index keys the same rule over their 128 dims (MiniMax-M3.1 page,
+             "Quick start": NVFP4 index keys)
   folding    FP8 query rows: w' = w * s, so that w' * ReLU(code . k) equals
              w * ReLU((s * code) . k) for s > 0 (ReLU is positively
              homogeneous)
@@ -154,8 +156,8 @@ def quantize_q(q_bits: np.ndarray, w: np.ndarray | None, fmt: str):
     raise ValueError(fmt)
 
 
-KEY_CODE_BYTES = {"fp8": 128, "mxfp4": 64}
-KEY_SIDE_BYTES = {"fp8": 4, "mxfp4": 4}
+KEY_CODE_BYTES = {"fp8": 128, "mxfp4": 64, "nvfp4": 64}
+KEY_SIDE_BYTES = {"fp8": 4, "mxfp4": 4, "nvfp4": 8}
 LAT_ROW_STRIDE = {"bf16": 1152, "fp8": 640, "nvfp4": 384}
 
 
@@ -163,14 +165,16 @@ def insert_key(pool: np.ndarray, fmt: str, P: int, page: int, slot: int, vals_bi
     """Write one token's index key (bf16 bits [128]) into page `page`, slot
     `slot` of a key pool [pages, page_bytes] (in place)."""
     x = bf16_to_f32(vals_bits)
-    cb = KEY_CODE_BYTES[fmt]
+    cb, sb = KEY_CODE_BYTES[fmt], KEY_SIDE_BYTES[fmt]
     if fmt == "fp8":
         codes, scale = fp8_row(x)
         side = np.asarray([scale], np.float32).view(np.uint8)
-    else:
+    elif fmt == "mxfp4":
         codes, side = mxfp4_blocks(x, 32)
+    else:
+        codes, side = nvfp4_blocks(x, 16)
     pool[page, slot * cb:(slot + 1) * cb] = codes
-    pool[page, P * cb + slot * 4:P * cb + slot * 4 + 4] = side
+    pool[page, P * cb + slot * sb:P * cb + (slot + 1) * sb] = side
 
 
 def insert_latent(pool: np.ndarray, fmt: str, P: int, page: int, slot: int, vals_bits: np.ndarray):

@@ -23,16 +23,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-KEY_FP8, KEY_MXFP4 = 1, 2
+KEY_FP8, KEY_MXFP4, KEY_NVFP4 = 1, 2, 3
 LAT_BF16, LAT_FP8, LAT_NVFP4 = 1, 2, 3
 Q_BF16, Q_FP8, Q_MXFP4 = 1, 2, 3
 OP_INDEXER, OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_TOPK_SHARDED, OP_MSA_DECODE = 1, 2, 3, 4, 5, 6
 OP_INDEXER_PREFIX = 7
 
-KEY_FMT = {"fp8": KEY_FP8, "mxfp4": KEY_MXFP4}
+KEY_FMT = {"fp8": KEY_FP8, "mxfp4": KEY_MXFP4, "nvfp4": KEY_NVFP4}
 LAT_FMT = {"bf16": LAT_BF16, "fp8": LAT_FP8, "nvfp4": LAT_NVFP4}
 Q_FMT = {"bf16": Q_BF16, "fp8": Q_FP8, "mxfp4": Q_MXFP4}
-KEY_TOKEN_BYTES = {KEY_FP8: 132, KEY_MXFP4: 68}
+KEY_TOKEN_BYTES = {KEY_FP8: 132, KEY_MXFP4: 68, KEY_NVFP4: 72}
 LAT_TOKEN_BYTES = {LAT_BF16: 1152, LAT_FP8: 580, LAT_NVFP4: 352}   # data bytes per token
 LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per latent row in a page
 
@@ -78,7 +78,7 @@ class IndexerPrefixArgs(ctypes.Structure):
 class TopkArgs(ctypes.Structure):
     _fields_ = [("batch", Batch), ("scores", ctypes.c_void_p), ("ld", ctypes.c_int64),
                 ("k", ctypes.c_int32), ("idx", ctypes.c_void_p), ("rows", ctypes.c_void_p),
-                ("page_size_log2", ctypes.c_int32), ("count", ctypes.c_void_p),
+                ("page_size_log2", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("count", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -138,7 +138,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        ("dsa_topk", [ctypes.POINTER(TopkArgs), vp]),
                        ("sparse_mla_decode", [ctypes.POINTER(MlaArgs), vp]),
                        ("sparse_mla_prefill", [ctypes.POINTER(MlaArgs), vp]),
-                       ("dsa_translate_pages", [vp, i32, ctypes.POINTER(Batch), i32, vp, vp]),
+                       ("dsa_translate_pages", [vp, i32, ctypes.POINTER(Batch), i32, i32, vp, vp]),
                        ("dsa_quantize_q", [ctypes.POINTER(QuantQArgs), vp]),
                        ("dsa_cache_insert", [ctypes.POINTER(InsertArgs), vp]),
                        ("dsa_topk_sharded", [ctypes.POINTER(TopkShardedArgs), vp]),
@@ -223,10 +223,10 @@ def dsa_topk(args: TopkArgs, stream=None):
     _check(load().dsa_topk(ctypes.byref(args), _stream(stream)), "dsa_topk")
 
 
-def dsa_translate_pages(idx: torch.Tensor, k: int, batch: Batch, page_size_log2: int,
+def dsa_translate_pages(idx: torch.Tensor, k: int, batch: Batch, page_size_log2: int, num_pages: int,
                         rows: torch.Tensor, stream=None):
     _check(load().dsa_translate_pages(idx.data_ptr(), int(k), ctypes.byref(batch), int(page_size_log2),
-                                      rows.data_ptr(), _stream(stream)), "dsa_translate_pages")
+                                      int(num_pages), rows.data_ptr(), _stream(stream)), "dsa_translate_pages")
 
 
 def sparse_mla_decode(args: MlaArgs, stream=None):
@@ -267,16 +267,22 @@ def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 def indexer_args(batch: Batch, keys: Cache, q: torch.Tensor, w: torch.Tensor, scores: torch.Tensor,
                  q_scale: Optional[torch.Tensor] = None) -> IndexerArgs:
-    q_fmt = Q_BF16 if q.dtype == torch.bfloat16 else Q_FP8
+    """q: bf16 [T,32,128]; E4M3 codes uint8 [T,32,128] with fp32 q_scale [T,32];
+    or E2M1 pairs uint8 [T,32,64] with E8M0 q_scale uint8 [T,32,4]."""
+    if q.dtype == torch.bfloat16:
+        q_fmt = Q_BF16
+    else:
+        assert q.dtype == torch.uint8 and q_scale is not None
+        q_fmt = Q_FP8 if q.shape[-1] == 128 else Q_MXFP4
     return IndexerArgs(batch, keys, q.data_ptr(), q_fmt, _ptr(q_scale), w.data_ptr(),
                        scores.data_ptr(), int(scores.stride(0)))
 
 
 def topk_args(batch: Batch, scores: torch.Tensor, k: int, idx: torch.Tensor,
-              rows: Optional[torch.Tensor] = None, page_size_log2: int = 0,
+              rows: Optional[torch.Tensor] = None, page_size_log2: int = 0, num_pages: int = 0,
               count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> TopkArgs:
     return TopkArgs(batch, scores.data_ptr(), int(scores.stride(0)), int(k), idx.data_ptr(), _ptr(rows),
-                    int(page_size_log2), _ptr(count), _ptr(ws), 0 if ws is None else ws.numel())
+                    int(page_size_log2), int(num_pages), _ptr(count), _ptr(ws), 0 if ws is None else ws.numel())
 
 
 def mla_args(q: torch.Tensor, latents: Cache, rows: torch.Tensor, out: torch.Tensor,
@@ -409,10 +415,11 @@ class DecodeStep:
         self.out = torch.empty(T, H, 512, dtype=torch.float32, device=dev)
         self.lse = torch.empty(T, H, dtype=torch.float32, device=dev)
         self.iargs = indexer_args(batch, keys, q_idx, w, self.scores, q_idx_scale)
-        self.targs = topk_args(batch, self.scores, k, self.idx, self.rows, keys.page_size_log2, self.count)
+        self.targs = topk_args(batch, self.scores, k, self.idx, self.rows, latents.page_size_log2,
+                               latents.num_pages, self.count)
         self.tws = workspace(dsa_workspace_size(OP_TOPK, self.targs), dev)
-        self.targs = topk_args(batch, self.scores, k, self.idx, self.rows, keys.page_size_log2, self.count,
-                               self.tws)
+        self.targs = topk_args(batch, self.scores, k, self.idx, self.rows, latents.page_size_log2,
+                               latents.num_pages, self.count, self.tws)
         self.margs = mla_args(q_mla, latents, self.rows, self.out, self.lse, sm_scale, num_splits)
         op = OP_MLA_PREFILL if prefill else OP_MLA_DECODE
         self.mws = workspace(dsa_workspace_size(op, self.margs), dev)

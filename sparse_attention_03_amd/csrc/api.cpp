@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -26,7 +27,9 @@ dsa_status fail(dsa_status st, const char* fmt, ...) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int key_token_bytes(int fmt) { return fmt == DSA_KEY_FP8 ? 132 : fmt == DSA_KEY_MXFP4 ? 68 : 0; }
+int key_token_bytes(int fmt) {
+  return fmt == DSA_KEY_FP8 ? 132 : fmt == DSA_KEY_MXFP4 ? 68 : fmt == DSA_KEY_NVFP4 ? 72 : 0;
+}
 // bytes per latent row inside a page (the row's data padded to whole 128-byte lines)
 int lat_row_bytes(int fmt) {
   return fmt == DSA_LAT_BF16 ? 1152 : fmt == DSA_LAT_FP8 ? 640 : fmt == DSA_LAT_NVFP4 ? 384 : 0;
@@ -245,6 +248,8 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
   if (a->q_fmt == DSA_Q_FP8 && (int64_t)a->batch.max_rows_per_req > 16 * 65535)
     return fail(DSA_ERR_INVALID_ARG, "indexer: too many rows per request");
   if (a->q_fmt != DSA_Q_BF16 && a->q_fmt != DSA_Q_FP8) return fail(DSA_ERR_UNSUPPORTED, "indexer: q_fmt %d", a->q_fmt);
+  if (a->q_fmt == DSA_Q_FP8 && a->keys.fmt != DSA_KEY_FP8)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: FP8 q runs against FP8 keys only");
   if (a->q_fmt == DSA_Q_FP8 && (!a->q_scale || !aligned(a->q_scale, 16)))
     return fail(DSA_ERR_INVALID_ARG, "indexer: FP8 q needs a 16-byte aligned q_scale");
 
@@ -274,7 +279,7 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     // two per CU) amortise that.
     int64_t target = (int64_t)b.max_vis * b.num_requests / (b.max_rows_per_req == 1 ? 2048 : 512);
     const int cap = b.max_rows_per_req > 1 ? 4096
-                    : a->keys.fmt == DSA_KEY_FP8 ? dsa::kIndexerRowChunkFp8 : dsa::kIndexerRowChunkMxfp4;
+                    : a->keys.fmt == DSA_KEY_FP8 ? dsa::kIndexerRowChunkFp8 : dsa::kIndexerRowChunkFp4;
     int chunk = 256;
     while (chunk < cap && chunk * 2 <= target) chunk *= 2;
     p.chunk = chunk;
@@ -282,9 +287,8 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     p.max_rows_per_req = b.max_rows_per_req;
     st = dsa::launch_indexer_bf16(p, stream);
   } else {
-    if (a->keys.fmt != DSA_KEY_FP8) return fail(DSA_ERR_UNSUPPORTED, "indexer: FP8 q runs against FP8 keys only");
     p.q8 = static_cast<const uint8_t*>(a->q);
-    p.q_scale = a->q_scale;
+    p.q_scale = static_cast<const float*>(a->q_scale);
     p.max_rows_per_req = b.max_rows_per_req;
     // key segment per workgroup: about 2048 workgroups over rows x keys
     const int64_t row_groups = (int64_t)b.num_requests * ((b.max_rows_per_req + 15) / 16);
@@ -395,6 +399,8 @@ dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   if (!a->idx) return fail(DSA_ERR_INVALID_ARG, "topk: idx is null");
   if (a->rows) {
     if (a->page_size_log2 < 4 || a->page_size_log2 > 24) return fail(DSA_ERR_INVALID_ARG, "topk: page_size_log2");
+    if (a->num_pages < 1 || ((int64_t)a->num_pages << a->page_size_log2) > INT32_MAX)
+      return fail(DSA_ERR_INVALID_ARG, "topk: num_pages %d (rows of the pool must fit int32)", a->num_pages);
     if (!b.tok_req) return fail(DSA_ERR_INVALID_ARG, "topk: rows need tok_req");
     dsa_status st = check_batch(b, a->page_size_log2, false);
     if (st != DSA_OK) return st;
@@ -416,6 +422,7 @@ dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   p.block_table = b.block_table;
   p.bt_stride = b.bt_stride;
   p.plog2 = a->page_size_log2;
+  p.num_pages = a->num_pages;
   p.idx = a->idx;
   p.rows = a->rows;
   p.count = a->count;
@@ -548,15 +555,17 @@ dsa_status dsa_msa_decode(const dsa_msa_args* a, hipStream_t stream) {
 }
 
 dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* b, int32_t page_size_log2,
-                               int32_t* rows, hipStream_t stream) {
+                               int32_t num_pages, int32_t* rows, hipStream_t stream) {
   g_err[0] = 0;
   if (!idx || !rows || !b) return fail(DSA_ERR_INVALID_ARG, "translate: null pointer");
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "translate: k %d", k);
   if (b->num_rows < 1 || !b->tok_req) return fail(DSA_ERR_INVALID_ARG, "translate: bad batch");
   if (page_size_log2 < 4 || page_size_log2 > 24) return fail(DSA_ERR_INVALID_ARG, "translate: page_size_log2");
   if (b->block_table && b->bt_stride < 1) return fail(DSA_ERR_INVALID_ARG, "translate: bt_stride");
+  if (num_pages < 1 || ((int64_t)num_pages << page_size_log2) > INT32_MAX)
+    return fail(DSA_ERR_INVALID_ARG, "translate: num_pages %d (rows of the pool must fit int32)", num_pages);
   dsa_status st = dsa::launch_translate(idx, k, b->num_rows, b->tok_req, b->block_table, b->bt_stride,
-                                        page_size_log2, rows, stream);
+                                        page_size_log2, num_pages, rows, stream);
   if (st != DSA_OK) return fail(st, "translate: launch failed: %s", hipGetErrorString(hipGetLastError()));
   return DSA_OK;
 }
@@ -606,7 +615,7 @@ dsa_status dsa_cache_insert(const dsa_insert_args* a, hipStream_t stream) {
   if (a->num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "cache_insert: num_tokens < 0");
   if (!a->key_vals && !a->lat_vals) return fail(DSA_ERR_INVALID_ARG, "cache_insert: neither keys nor latents given");
   if (a->key_vals) {
-    if (a->keys.fmt != DSA_KEY_FP8 && a->keys.fmt != DSA_KEY_MXFP4)
+    if (a->keys.fmt != DSA_KEY_FP8 && a->keys.fmt != DSA_KEY_MXFP4 && a->keys.fmt != DSA_KEY_NVFP4)
       return fail(DSA_ERR_UNSUPPORTED, "cache_insert: key fmt %d", a->keys.fmt);
     dsa_status st = check_cache(a->keys, key_token_bytes(a->keys.fmt), "cache_insert keys");
     if (st != DSA_OK) return st;

@@ -1,11 +1,14 @@
-// Lightning indexer, decode shape: BF16 queries against FP8 or MXFP4 paged keys.
+// Lightning indexer, decode shape: BF16 queries against FP8, MXFP4 or NVFP4
+// paged keys.
 //
 //   score(t, s) = sum_{h<32} w[t,h] * max(0, q[t,h,:] . k_s)
 //
 // (Kimi K3.1 Pro day-0 page, "Sparse attention in K3.1 Pro": 32 light heads
 // score every earlier token against a 132-byte FP8 key; AMD section "native
 // MXFP4 indexer": FP32 accumulation, weighted reduction across heads, keys
-// reused across the speculative query rows of a request.)
+// reused across the speculative query rows of a request.  MiniMax-M3.1-Flash
+// day-0 page, "Quick start" and AMD "NVFP4 indexer DCP": NVFP4 index keys,
+// E2M1 with one E4M3 scale per 16 dims.)
 //
 // Work split: one workgroup = one request x one chunk of keys.  The rows of
 // the request (q, 8 KiB each as bf16) are staged once in LDS; each wave streams
@@ -32,46 +35,23 @@ constexpr int kIdxKT = 4;              // 16-key tiles per wave per round
 constexpr int kIdxRound = kIdxWaves * kIdxKT * 16;  // 256 keys per round
 constexpr int kQPad = 136;             // bf16 per head row in LDS (272 B: conflict-free reads)
 
-// Raw key codes of one round (kIdxKT tiles of 16 keys) for one lane.  The
-// per-key side data (FP8 scale, MXFP4 E8M0 codes) is staged in LDS for the
-// whole chunk up front, so the round loop issues nothing but these 16-byte
-// code loads.
+// Raw key bytes of one round (kIdxKT tiles of 16 keys) for one lane: the
+// codes of the lane's 32 dims of key c of each tile and their side data.
 template <int KFMT> struct RawKeys {
   i32x4 v[kIdxKT][KFMT == DSA_KEY_FP8 ? 2 : 1];
   bool ok[kIdxKT];       // page present and tile inside the chunk
-  uint32_t sc[kIdxKT];   // (side data read in the loop) MXFP4: E8M0 codes of key c of tile kt
+  uint32_t sc[kIdxKT];   // (side data read in the loop) MXFP4: E8M0 codes of key c of tile kt;
+                         // NVFP4: the two E4M3 block scales of this lane's 32 dims
   float own_scale;       // (side data read in the loop) FP8 scale of the key this lane stores
 };
-
-// Side data of the chunk's keys in LDS, one word per key: the FP8 scale (-inf
-// on an absent page, so the key is never selected) or the four E8M0 codes of
-// an MXFP4 key.  Loaded with all of a thread's loads in flight at once.
-constexpr int kIdxMaxChunk = 4096;
-template <int KFMT>
-__device__ __forceinline__ void stage_side(const IndexerParams& p, const int* pg_lds, int lp0, int k0, int kend, int P,
-                                           uint32_t* side) {
-  constexpr int kPer = kIdxMaxChunk / 256;
-  uint32_t v[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int s = k0 + (int)threadIdx.x + 256 * i;
-    const int pg_read = pg_lds[min(s, kend - 1) - (lp0 << p.plog2) >> p.plog2];
-    const int pg = s < kend ? pg_read : -1;
-    const uint8_t* page = p.keys + (int64_t)max(pg, 0) * p.page_bytes;
-    const int slot = s & (P - 1);
-    const uint32_t x = *reinterpret_cast<const uint32_t*>(page + P * (KFMT == DSA_KEY_FP8 ? 128 : 64) + slot * 4);
-    v[i] = KFMT == DSA_KEY_FP8 ? (pg >= 0 ? x : __float_as_uint(-__builtin_inff())) : x;
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) side[threadIdx.x + 256 * i] = v[i];
-}
 
 // The 8 dims lane group g supplies at k-step kk of the 128-dim dot product
 // (the same assignment for the query A and the key B fragments, so the
 // k-sum is the full dot product).  FP8 keys: the four lane groups of a key
 // read its first 64 bytes in one instruction and its last 64 in a second
 // (16 bytes each, contiguous per key); MXFP4: lane group g holds the 32
-// codes under E8M0 scale g.
+// codes under E8M0 scale g; NVFP4: the same 32 codes under block scales 2g
+// and 2g+1.
 // (COAL = false: FP8 lane group g reads bytes 32g .. 32g+31 of each key, as
 // the multi-row kernel does, whose A fragments come from LDS.)
 template <int KFMT, bool COAL>
@@ -89,9 +69,7 @@ constexpr int kIdxMaxRows = kIndexerMaxRowsPerPass;  // rows staged in LDS per p
 // absent page reads page 0 instead and its scores are masked afterwards):
 // loads under a branch would make the compiler wait for all of them before
 // any is used, so the next round's loads could not overlap this round.
-// SIDE: the side data comes from the LDS copy (stage_side) instead of loads
-// issued with the round.
-template <int KFMT, bool SIDE>
+template <int KFMT>
 __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg_lds, int lp0, int base, int kend,
                                            int wave, int g, int c, int P, RawKeys<KFMT>& raw) {
   const int last = ((kend - 1) >> p.plog2) - lp0;  // last staged page entry
@@ -100,28 +78,26 @@ __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg
   for (int kt = 0; kt < kIdxKT; ++kt) {
     const int s0 = base + (wave * kIdxKT + kt) * 16;
     const int e = min((s0 >> p.plog2) - lp0, last);
-    int pg;
-    if (SIDE) {
-      const int pg_read = pg_lds[e];  // read unconditionally: no branch around the loads below
-      pg = s0 < kend ? pg_read : -1;
-    } else {
-      pg = s0 < kend ? pg_lds[e] : -1;
-    }
+    const int pg = s0 < kend ? pg_lds[e] : -1;
     pgs[kt] = pg;
     raw.ok[kt] = pg >= 0;
     const uint8_t* page = p.keys + (int64_t)max(pg, 0) * p.page_bytes;
     const int slot = (s0 & (P - 1)) + c;
     if (KFMT == DSA_KEY_FP8) {
-      // SIDE (single-row kernel): the coalesced lane-to-byte map of kdim<FP8, true>
-      const uint8_t* kp = page + slot * 128 + (SIDE ? 16 : 32) * g;
+      const uint8_t* kp = page + slot * 128 + 32 * g;
       raw.v[kt][0] = ld16(kp);
-      raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16(kp + (SIDE ? 64 : 16));
-    } else {
+      raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0] = ld16(kp + 16);
+    } else if (KFMT == DSA_KEY_MXFP4) {
       raw.v[kt][0] = ld16(page + slot * 64 + 16 * g);
-      if (!SIDE) raw.sc[kt] = *reinterpret_cast<const uint32_t*>(page + P * 64 + slot * 4);
+      raw.sc[kt] = *reinterpret_cast<const uint32_t*>(page + P * 64 + slot * 4);
+    } else {
+      // NVFP4: dims 32g .. 32g+31 lie in blocks 2g and 2g+1, whose scales are
+      // bytes 2g, 2g+1 of the key's eight
+      raw.v[kt][0] = ld16(page + slot * 64 + 16 * g);
+      raw.sc[kt] = *reinterpret_cast<const uint16_t*>(page + P * 64 + slot * 8 + 2 * g);
     }
   }
-  if (KFMT == DSA_KEY_FP8 && !SIDE) {
+  if (KFMT == DSA_KEY_FP8) {
     // one load for the scale of the key this lane stores (tile g, key c)
     int pg = pgs[0];
 #pragma unroll
@@ -132,10 +108,7 @@ __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg
   }
 }
 
-// Dequantise a round into B fragments.  Returns the multiplier of the score
-// this lane stores (key c of tile g): the FP8 key scale, 1 for MXFP4 (whose
-// power-of-two block scales are applied exactly during dequantisation), or
-// -inf for an absent page so the key is never selected.
+// Dequantise tile kt of a round into B fragments (exact in bf16).
 template <int KFMT>
 __device__ __forceinline__ void dequant_tile(const RawKeys<KFMT>& raw, int kt, bf16x8 (&b)[4], uint32_t e8m0x4 = 0,
                                              int g = 0) {
@@ -145,24 +118,31 @@ __device__ __forceinline__ void dequant_tile(const RawKeys<KFMT>& raw, int kt, b
     b[1] = e4m3x8_to_bf16x8(x[2], x[3]);
     b[2] = e4m3x8_to_bf16x8(y[0], y[1]);
     b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
-  } else {
+  } else if (KFMT == DSA_KEY_MXFP4) {
     const i32x4 x = raw.v[kt][0];
     const float sc = e8m0_to_f32((e8m0x4 >> (8 * g)) & 0xFFu);
     b[0] = e2m1x8_to_bf16x8(x[0], sc);
     b[1] = e2m1x8_to_bf16x8(x[1], sc);
     b[2] = e2m1x8_to_bf16x8(x[2], sc);
     b[3] = e2m1x8_to_bf16x8(x[3], sc);
+  } else {
+    // NVFP4: e8m0x4 holds this lane's two E4M3 block scales (dims 32g..+15,
+    // 32g+16..+31); E2M1 x E4M3 is exact in bf16
+    const i32x4 x = raw.v[kt][0];
+    const float s0 = e4m3_to_f32(e8m0x4 & 0xFFu), s1 = e4m3_to_f32((e8m0x4 >> 8) & 0xFFu);
+    b[0] = e2m1x8_times(x[0], s0);
+    b[1] = e2m1x8_times(x[1], s0);
+    b[2] = e2m1x8_times(x[2], s1);
+    b[3] = e2m1x8_times(x[3], s1);
   }
 }
 
 // Multiplier of the score this lane stores (key s_own = tile g, key c): the
-// FP8 key scale from the staged side data (-inf on an absent page), 1 for
-// MXFP4 (whose power-of-two block scales are applied exactly during
-// dequantisation) or -inf on an absent page.  A tile on an absent page holds
+// FP8 key scale, 1 for MXFP4 / NVFP4 (whose block scales are applied exactly
+// during dequantisation), or -inf on an absent page.  A tile on an absent page holds
 // page 0's bytes; every score it produces is replaced by this -inf.
-template <int KFMT, bool SIDE>
-__device__ __forceinline__ float own_multiplier(const RawKeys<KFMT>& raw, int g, const uint32_t* side, int i_own) {
-  if (KFMT == DSA_KEY_FP8 && SIDE) return __uint_as_float(side[i_own]);
+template <int KFMT>
+__device__ __forceinline__ float own_multiplier(const RawKeys<KFMT>& raw, int g) {
   bool own_ok = raw.ok[0];
 #pragma unroll
   for (int kt = 1; kt < kIdxKT; ++kt)
@@ -284,8 +264,8 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
 #pragma unroll
       for (int kt = 0; kt < kIdxKT; ++kt) dequant_tile<KFMT>(raw, kt, bfr[kt], raw.sc[kt], g);
       const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
-      const float own_mul = own_multiplier<KFMT, false>(raw, g, nullptr, 0);
-      if (next < kend) load_round<KFMT, false>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
+      const float own_mul = own_multiplier<KFMT>(raw, g);
+      if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
       f32x4 acc[kIdxKT][2];
       for (int j = 0; j < nr; ++j) {
         mfma_row(j, bfr, acc);
@@ -296,7 +276,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
     // Software pipeline: the raw key bytes of round i+1 are in flight while
     // round i is dequantised and multiplied.
     RawKeys<KFMT> raw;
-    load_round<KFMT, false>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
+    load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
     for (int base = k0; base < kend; base += kIdxRound) do_round(base, raw, base + kIdxRound);
 
     t0 += p.qrows;
@@ -355,15 +335,19 @@ template <int KFMT> struct KeyStream {
   static constexpr int kKeyBytes = KFMT == DSA_KEY_FP8 ? 128 : 64;  // code bytes per key
   static constexpr int kChunks = kKeyBytes / 16;                     // 16-byte chunks per key
   static constexpr int kCopies = 64 * kKeyBytes / 1024;              // code copies per round
-  static constexpr int kOps = kCopies + 1;                           // + the side copy
-  static constexpr int kRoundBytes = 64 * kKeyBytes + 256;           // codes, then 64 side words
+  static constexpr int kSideWords = KFMT == DSA_KEY_NVFP4 ? 2 : 1;   // side dwords per key
+  static constexpr int kOps = kCopies + kSideWords;                  // + the side copies
+  static constexpr int kRoundBytes = 64 * kKeyBytes + 256 * kSideWords;  // codes, then side words
   static constexpr int kDepth = 2;                                   // rounds per wave ring
-  static constexpr int kMaxChunk = KFMT == DSA_KEY_FP8 ? kIndexerRowChunkFp8 : kIndexerRowChunkMxfp4;
+  static constexpr int kMaxChunk = KFMT == DSA_KEY_FP8 ? kIndexerRowChunkFp8 : kIndexerRowChunkFp4;
   // swizzle of key c's chunks (c = key within its tile)
   __device__ static int swz(int c) { return KFMT == DSA_KEY_FP8 ? (c >> 1) & 7 : (c >> 2) & 3; }
   // LDS bytes of one workgroup: 4 rings, the chunk's scores, its page ids
   static constexpr size_t kLds = 4 * kDepth * kRoundBytes + kMaxChunk * 4 + (kMaxChunk / 16 + 1) * 4;
 };
+// FP4 keys fit the default 64 KiB of dynamic LDS; FP8 keys raise the limit
+static_assert(KeyStream<DSA_KEY_MXFP4>::kLds <= 65536 && KeyStream<DSA_KEY_NVFP4>::kLds <= 65536, "LDS");
+static_assert(KeyStream<DSA_KEY_FP8>::kLds <= 160 * 1024, "LDS");
 
 template <int KFMT>
 __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) {
@@ -387,15 +371,16 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
   for (int i = tid; i <= ((kcap - 1) >> p.plog2) - lp0; i += 256)
     pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
   // (loaded values are uniform; saying so keeps the round bookkeeping scalar)
-  const int t = __builtin_amdgcn_readfirstlane(p.req_row_start[r]);
+  const int t_first = __builtin_amdgcn_readfirstlane(p.req_row_start[r]);
   const int t_end = __builtin_amdgcn_readfirstlane(p.req_row_start[r + 1]);
   __syncthreads();
-  if (t_end <= t) return;
 
   uint8_t* ring = lds + wave * KS::kDepth * KS::kRoundBytes;
   const uint32_t ring_l = idx_lds_addr(ring);
   // Copies of round `it` into ring slot it % kDepth.  Keys at or past `kc`
   // are clamped onto key kc - 1, so every round issues the same copies.
+  // Side words: the FP8 scale or MXFP4 E8M0 word of the lane's key at word
+  // `lane`; NVFP4 scale bytes 0..3 at word `lane`, 4..7 at word 64 + lane.
   auto issue = [&](int it, int kc) {
     const int kb = k0 + it * kIdxRound + wave * 64;  // first key of the wave's share
     const int own = min(kb + lane, kc - 1);           // this lane's key (clamped)
@@ -414,99 +399,120 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
                                    : g_idx_zero;
       idx_dma16(src, slot_l + d * 1024);
     }
-    const uint8_t* sw = pg_own >= 0 ? p.keys + (int64_t)pg_own * p.page_bytes + P * KS::kKeyBytes + (own & (P - 1)) * 4
-                                    : g_idx_zero;
-    idx_dma4(sw, slot_l + 64 * KS::kKeyBytes);
+    constexpr int kSideBytes = 4 * KS::kSideWords;
+#pragma unroll
+    for (int w = 0; w < KS::kSideWords; ++w) {
+      const uint8_t* sw = pg_own >= 0 ? p.keys + (int64_t)pg_own * p.page_bytes + P * KS::kKeyBytes +
+                                            (own & (P - 1)) * kSideBytes + 4 * w
+                                      : g_idx_zero;
+      idx_dma4(sw, slot_l + 64 * KS::kKeyBytes + 256 * w);
+    }
   };
   // rounds the chunk can have before its visible count is known
   const int nround_cap = (kcap - k0 + kIdxRound - 1) / kIdxRound;
   const int nfirst = min(KS::kDepth, nround_cap);
-  for (int d = 0; d < nfirst; ++d) issue(d, kcap);
-  int issued = nfirst;  // rounds issued so far (round i uses ring slot i % kDepth)
 
-  // the row's visible count, query fragments and head weights
-  const int vis = __builtin_amdgcn_readfirstlane(min(p.tok_vis[t], p.max_vis));
-  bf16x8 qa[2][4];
-  const __bf16* qrow = p.q + (int64_t)t * 32 * 128;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
-  const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
-  const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
-  // These loads must be complete, and known to the compiler to be, before the
-  // loop: one still pending there would make the compiler wait for every copy
-  // in flight on every round.  (This wait also covers the first copies.)
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (k0 >= vis) return;                // nothing in flight
-  const int kend = min(kcap, vis);
-  const int nround = (kend - k0 + kIdxRound - 1) / kIdxRound;
+  // One row per request is the intended shape; further rows of the request
+  // (more than the host bound promised) are scored the same way in turn.
+  for (int t = t_first; t < t_end; ++t) {
+    for (int d = 0; d < nfirst; ++d) issue(d, kcap);
+    int issued = nfirst;  // rounds issued so far (round i uses ring slot i % kDepth)
 
-  static_assert(KS::kDepth >= 2 && KS::kDepth <= 4, "wait counts for 1 .. 3 rounds behind");
-  for (int it = 0; it < nround; ++it) {
-    // rounds it+1 .. issued-1 are the copies issued after round it's
-    switch (issued - 1 - it) {
-      case 0: idx_wait_vmcnt<0>(); break;
-      case 1: idx_wait_vmcnt<KS::kOps>(); break;
-      case 2: idx_wait_vmcnt<2 * KS::kOps>(); break;
-      default: idx_wait_vmcnt<3 * KS::kOps>(); break;
-    }
-    const uint8_t* rd = ring + (it % KS::kDepth) * KS::kRoundBytes;
-    const uint32_t* side = reinterpret_cast<const uint32_t*>(rd + 64 * KS::kKeyBytes);
-    float v[kIdxKT];
+    // the row's visible count, query fragments and head weights
+    const int vis = __builtin_amdgcn_readfirstlane(min(p.tok_vis[t], p.max_vis));
+    bf16x8 qa[2][4];
+    const __bf16* qrow = p.q + (int64_t)t * 32 * 128;
 #pragma unroll
-    for (int kt = 0; kt < kIdxKT; ++kt) {
-      const uint8_t* tile = rd + kt * 16 * KS::kKeyBytes + c * KS::kKeyBytes;
-      bf16x8 b[4];
-      if (KFMT == DSA_KEY_FP8) {
-        const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
-        const i32x4 y = *reinterpret_cast<const i32x4*>(tile + ((4 + g) ^ KS::swz(c)) * 16);
-        b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
-        b[1] = e4m3x8_to_bf16x8(x[2], x[3]);
-        b[2] = e4m3x8_to_bf16x8(y[0], y[1]);
-        b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
-      } else {
-        const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
-        const float sc = e8m0_to_f32((side[kt * 16 + c] >> (8 * g)) & 0xFFu);
-        b[0] = e2m1x8_to_bf16x8(x[0], sc);
-        b[1] = e2m1x8_to_bf16x8(x[1], sc);
-        b[2] = e2m1x8_to_bf16x8(x[2], sc);
-        b[3] = e2m1x8_to_bf16x8(x[3], sc);
-      }
-      f32x4 a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int kk = 1; kk < 4; ++kk) {
-        a0 = mfma16x16x32(qa[0][kk], b[kk], a0);
-        a1 = mfma16x16x32(qa[1][kk], b[kk], a1);
+      for (int kk = 0; kk < 4; ++kk)
+        qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
+    // These loads must be complete, and known to the compiler to be, before the
+    // loop: one still pending there would make the compiler wait for every copy
+    // in flight on every round.  (This wait also covers the first copies.)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (k0 >= vis) continue;              // nothing in flight (vis is uniform)
+    const int kend = min(kcap, vis);
+    const int nround = (kend - k0 + kIdxRound - 1) / kIdxRound;
+
+    static_assert(KS::kDepth >= 2 && KS::kDepth <= 4, "wait counts for 1 .. 3 rounds behind");
+    for (int it = 0; it < nround; ++it) {
+      // rounds it+1 .. issued-1 are the copies issued after round it's
+      switch (issued - 1 - it) {
+        case 0: idx_wait_vmcnt<0>(); break;
+        case 1: idx_wait_vmcnt<KS::kOps>(); break;
+        case 2: idx_wait_vmcnt<2 * KS::kOps>(); break;
+        default: idx_wait_vmcnt<3 * KS::kOps>(); break;
       }
-      float x = 0.f;
+      const uint8_t* rd = ring + (it % KS::kDepth) * KS::kRoundBytes;
+      const uint32_t* side = reinterpret_cast<const uint32_t*>(rd + 64 * KS::kKeyBytes);
+      float v[kIdxKT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x += w0[i] * relu(a0[i]);
-        x += w1[i] * relu(a1[i]);
+      for (int kt = 0; kt < kIdxKT; ++kt) {
+        const uint8_t* tile = rd + kt * 16 * KS::kKeyBytes + c * KS::kKeyBytes;
+        bf16x8 b[4];
+        if (KFMT == DSA_KEY_FP8) {
+          const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
+          const i32x4 y = *reinterpret_cast<const i32x4*>(tile + ((4 + g) ^ KS::swz(c)) * 16);
+          b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
+          b[1] = e4m3x8_to_bf16x8(x[2], x[3]);
+          b[2] = e4m3x8_to_bf16x8(y[0], y[1]);
+          b[3] = e4m3x8_to_bf16x8(y[2], y[3]);
+        } else if (KFMT == DSA_KEY_MXFP4) {
+          const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
+          const float sc = e8m0_to_f32((side[kt * 16 + c] >> (8 * g)) & 0xFFu);
+          b[0] = e2m1x8_to_bf16x8(x[0], sc);
+          b[1] = e2m1x8_to_bf16x8(x[1], sc);
+          b[2] = e2m1x8_to_bf16x8(x[2], sc);
+          b[3] = e2m1x8_to_bf16x8(x[3], sc);
+        } else {
+          // NVFP4: dims 32g .. 32g+31 are blocks 2g, 2g+1: scale bytes 2g, 2g+1
+          // of the key, i.e. half (g & 1) of side word (g >> 1)
+          const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
+          const uint32_t sw = side[(g >> 1) * 64 + kt * 16 + c] >> (16 * (g & 1));
+          const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32((sw >> 8) & 0xFFu);
+          b[0] = e2m1x8_times(x[0], s0);
+          b[1] = e2m1x8_times(x[1], s0);
+          b[2] = e2m1x8_times(x[2], s1);
+          b[3] = e2m1x8_times(x[3], s1);
+        }
+        f32x4 a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int kk = 1; kk < 4; ++kk) {
+          a0 = mfma16x16x32(qa[0][kk], b[kk], a0);
+          a1 = mfma16x16x32(qa[1][kk], b[kk], a1);
+        }
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x += w0[i] * relu(a0[i]);
+          x += w1[i] * relu(a1[i]);
+        }
+        v[kt] = x;
       }
-      v[kt] = x;
+      // lane stores key k0 + it * 256 + wave * 64 + lane: its multiplier is the
+      // FP8 scale (1 for MXFP4 / NVFP4) on a present page, -inf otherwise
+      const int s_own = k0 + it * kIdxRound + wave * 64 + lane;
+      const int pg_own = pg_lds[(min(s_own, kend - 1) >> p.plog2) - lp0];
+      const float mul = pg_own < 0 ? -__builtin_inff() : (KFMT == DSA_KEY_FP8 ? __uint_as_float(side[lane]) : 1.f);
+      const float tot = rows_reduce_scatter4(v, g);
+      if (s_own < kend) sc_out[s_own - k0] = mul == -__builtin_inff() ? mul : tot * mul;
+      // the slot is read; refill it with the next round (if the chunk has one)
+      if (issued < nround) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        issue(issued, kend);
+        ++issued;
+      }
     }
-    // lane stores key k0 + it * 256 + wave * 64 + lane: its multiplier is the
-    // FP8 scale (1 for MXFP4) on a present page, -inf otherwise
-    const int s_own = k0 + it * kIdxRound + wave * 64 + lane;
-    const int pg_own = pg_lds[(min(s_own, kend - 1) >> p.plog2) - lp0];
-    const float mul = pg_own < 0 ? -__builtin_inff() : (KFMT == DSA_KEY_FP8 ? __uint_as_float(side[lane]) : 1.f);
-    const float tot = rows_reduce_scatter4(v, g);
-    if (s_own < kend) sc_out[s_own - k0] = mul == -__builtin_inff() ? mul : tot * mul;
-    // the slot is read; refill it with the next round (if the chunk has one)
-    if (issued < nround) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      issue(issued, kend);
-      ++issued;
-    }
+    idx_wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
+    __syncthreads();
+    float* out = p.scores + (int64_t)t * p.ld;
+    for (int i = tid; i < kend - k0; i += 256) out[k0 + i] = sc_out[i];
+    if (t + 1 < t_end) __syncthreads();  // the next row rewrites the rings and sc_out
   }
-  idx_wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
-  __syncthreads();
-  float* out = p.scores + (int64_t)t * p.ld;
-  for (int i = tid; i < kend - k0; i += 256) out[k0 + i] = sc_out[i];
 }
 
 // Shared-prefix plan.  Groups are cut into sub-groups of at most
@@ -570,17 +576,24 @@ dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
   if (p.max_rows_per_req == 1) {
     if (p.key_fmt == DSA_KEY_FP8) {
       // above the default 64 KiB of dynamic LDS (idempotent, host-side)
-      hipFuncSetAttribute(reinterpret_cast<const void*>(indexer_bf16_row_kernel<DSA_KEY_FP8>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)KeyStream<DSA_KEY_FP8>::kLds);
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(indexer_bf16_row_kernel<DSA_KEY_FP8>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)KeyStream<DSA_KEY_FP8>::kLds) != hipSuccess)
+        return DSA_ERR_HIP;
       hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_FP8>, grid, dim3(256), KeyStream<DSA_KEY_FP8>::kLds, stream, p);
-    } else {
+    } else if (p.key_fmt == DSA_KEY_MXFP4) {
       hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_MXFP4>, grid, dim3(256), KeyStream<DSA_KEY_MXFP4>::kLds,
+                         stream, p);
+    } else {
+      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_NVFP4>, grid, dim3(256), KeyStream<DSA_KEY_NVFP4>::kLds,
                          stream, p);
     }
   } else if (p.key_fmt == DSA_KEY_FP8) {
     hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_FP8>, grid, dim3(256), lds, stream, p);
-  } else {
+  } else if (p.key_fmt == DSA_KEY_MXFP4) {
     hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_MXFP4>, grid, dim3(256), lds, stream, p);
+  } else {
+    hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_NVFP4>, grid, dim3(256), lds, stream, p);
   }
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

@@ -11,9 +11,9 @@ namespace dsa {
 // Query rows of a request the BF16 indexer stages in LDS per pass.
 constexpr int kIndexerMaxRowsPerPass = 6;
 // Keys per workgroup of the single-row BF16 indexer (its LDS holds the
-// chunk's scores): FP8 keys, MXFP4 keys.
+// chunk's scores): FP8 keys, MXFP4 / NVFP4 keys.
 constexpr int kIndexerRowChunkFp8 = 2048;
-constexpr int kIndexerRowChunkMxfp4 = 4096;
+constexpr int kIndexerRowChunkFp4 = 4096;
 
 struct IndexerParams {
   int R, T;
@@ -31,8 +31,9 @@ struct IndexerParams {
   int key_fmt;
   // queries
   const __bf16* q;          // bf16 q (BF16 path)
-  const uint8_t* q8;        // E4M3 q (FP8 path)
+  const uint8_t* q8;        // E4M3 q (FP8 path), E2M1 pairs (MXFP4 path)
   const float* q_scale;     // [T,32] (FP8 path)
+  const uint8_t* q_e8m0;    // [T,32,4] (MXFP4 path)
   const float* w;           // [T,32]
   float* scores;
   int64_t ld;
@@ -56,6 +57,7 @@ struct TopkParams {
   const int32_t* block_table;
   int bt_stride;
   int plog2;
+  int num_pages;        // latent pool pages: translation maps other pages to -1
   int32_t* idx;
   int32_t* rows;
   int32_t* count;
@@ -198,7 +200,7 @@ dsa_status launch_prefix_prep(const int32_t* tok_vis, int T, int max_vis, int L,
                               hipStream_t stream);
 dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hipStream_t stream);
 dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req,
-                            const int32_t* block_table, int bt_stride, int plog2, int32_t* rows,
+                            const int32_t* block_table, int bt_stride, int plog2, int num_pages, int32_t* rows,
                             hipStream_t stream);
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream);
 

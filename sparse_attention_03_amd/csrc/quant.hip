@@ -11,7 +11,9 @@
 //   MXFP4     per 32 values E8M0 = (fp32 exponent field of amax) - 2, clamped
 //             to 0..254, code = E2M1(x / 2^(E8M0 - 127))
 //   NVFP4     per 16 values s = E4M3(amax / 6), code = E2M1(x / value(s)) (0
-//             when s decodes to 0); the 64 rope dims are E4M3(x), unscaled
+//             when s decodes to 0); the 64 rope dims of a latent are E4M3(x),
+//             unscaled; NVFP4 index keys (MiniMax-M3.1-Flash page, "Quick
+//             start") take the same rule over their 128 dims
 //   folding   FP8 query rows also give w' = w * s: w' ReLU(code . k) equals
 //             w ReLU((s code) . k) because s > 0
 // E4M3 / E2M1 codes are the nearest value, ties to the even code, saturating
@@ -161,12 +163,18 @@ __global__ __launch_bounds__(64) void cache_insert_kernel(InsertParams p) {
         const float s = am > 0.f ? am / 448.f : 1.f;
         reinterpret_cast<uint16_t*>(page + slot * 128)[l] = (uint16_t)(e4m3_code(x0 / s) | (e4m3_code(x1 / s) << 8));
         if (l == 0) *reinterpret_cast<float*>(page + P * 128 + slot * 4) = s;
-      } else {
+      } else if (KFMT == DSA_KEY_MXFP4) {
         const float am = amax_lanes(a, 16);  // 32 dims = 16 lanes
         const uint32_t e8 = mx_code(am);
         const float s = pow2f((int)e8 - 127);
         page[slot * 64 + l] = (uint8_t)(e2m1_code(x0 / s) | (e2m1_code(x1 / s) << 4));
         if ((l & 15) == 0) page[P * 64 + slot * 4 + (l >> 4)] = (uint8_t)e8;
+      } else {
+        const float am = amax_lanes(a, 8);  // 16 dims = 8 lanes
+        const uint32_t sc = e4m3_code(am / 6.f);
+        const float sv = e4m3_to_f32(sc);
+        page[slot * 64 + l] = sv > 0.f ? (uint8_t)(e2m1_code(x0 / sv) | (e2m1_code(x1 / sv) << 4)) : (uint8_t)0;
+        if ((l & 7) == 0) page[P * 64 + slot * 8 + (l >> 3)] = (uint8_t)sc;
       }
     }
   }
@@ -238,6 +246,10 @@ dsa_status launch_cache_insert(const InsertParams& p, hipStream_t stream) {
   DSA_INSERT(DSA_KEY_MXFP4, DSA_LAT_BF16);
   DSA_INSERT(DSA_KEY_MXFP4, DSA_LAT_FP8);
   DSA_INSERT(DSA_KEY_MXFP4, DSA_LAT_NVFP4);
+  DSA_INSERT(DSA_KEY_NVFP4, 0);
+  DSA_INSERT(DSA_KEY_NVFP4, DSA_LAT_BF16);
+  DSA_INSERT(DSA_KEY_NVFP4, DSA_LAT_FP8);
+  DSA_INSERT(DSA_KEY_NVFP4, DSA_LAT_NVFP4);
 #undef DSA_INSERT
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

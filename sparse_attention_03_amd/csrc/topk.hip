@@ -381,8 +381,11 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - idx);
 }
 
+// Logical index li of request r -> physical row page * P + slot, or -1 for
+// no index, an index past the request's block-table row, or a page outside
+// [0, num_pages) (an absent page: nothing of it may be read).
 __device__ __forceinline__ int translate_one(int li, int r, const int32_t* __restrict__ bt, int bt_stride,
-                                             int plog2) {
+                                             int plog2, int num_pages) {
   if (li < 0) return -1;
   const int lp = li >> plog2;
   int pg;
@@ -392,7 +395,7 @@ __device__ __forceinline__ int translate_one(int li, int r, const int32_t* __res
   } else {
     pg = r;
   }
-  if (pg < 0) return -1;
+  if (pg < 0 || pg >= num_pages) return -1;
   return (pg << plog2) | (li & ((1 << plog2) - 1));
 }
 
@@ -513,7 +516,7 @@ __device__ __forceinline__ void order_and_store(const TopkParams& p, const int* 
   for (int j = tid; j < p.k; j += 1024) {
     const int li = j < K ? ord[j] : -1;
     idx[j] = li;
-    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2, p.num_pages);
   }
   if (p.count && tid == 0) p.count[t] = K;
 }
@@ -524,7 +527,7 @@ __device__ __forceinline__ void store_all(const TopkParams& p, int vis, int t, i
   for (int j = threadIdx.x; j < p.k; j += blockDim.x) {
     const int li = j < vis ? j : -1;
     idx[j] = li;
-    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2, p.num_pages);
   }
   if (p.count && threadIdx.x == 0) p.count[t] = vis;
 }
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
     for (int j = tid; j < p.k; j += 1024) {
       const int li = j < K ? ord[j] : -1;
       idx[j] = li;
-      if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+      if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2, p.num_pages);
     }
     if (p.count && tid == 0) p.count[t] = K;
     return;
@@ -959,7 +962,7 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
       for (int j = tid; j < p.k; j += 1024) {
         const int li = j < K ? L.ord[j] : -1;
         idx[j] = li;
-        if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+        if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2, p.num_pages);
       }
       if (p.count && tid == 0) p.count[t] = K;
       return;
@@ -979,7 +982,7 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
   for (int j = tid; j < p.k; j += 1024) {
     const int li = j < K ? L.ord[j] : -1;
     idx[j] = li;
-    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2);
+    if (rows) rows[j] = translate_one(li, r, p.block_table, p.bt_stride, p.plog2, p.num_pages);
   }
   if (p.count && tid == 0) p.count[t] = K;
 }
@@ -1059,7 +1062,7 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkParams p)
       if (take) {
         const int j = j0 + i;
         idx[pos] = j;
-        if (rows) rows[pos] = translate_one(j, r, p.block_table, p.bt_stride, p.plog2);
+        if (rows) rows[pos] = translate_one(j, r, p.block_table, p.bt_stride, p.plog2, p.num_pages);
         ++pos;
       }
     }
@@ -1072,11 +1075,12 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkParams p)
 }
 
 __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, const int32_t* __restrict__ tok_req,
-                                 const int32_t* __restrict__ bt, int bt_stride, int plog2, int32_t* __restrict__ rows) {
+                                 const int32_t* __restrict__ bt, int bt_stride, int plog2, int num_pages,
+                                 int32_t* __restrict__ rows) {
   const int64_t n = (int64_t)T * k;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int t = (int)(i / k);
-    rows[i] = translate_one(idx[i], tok_req[t], bt, bt_stride, plog2);
+    rows[i] = translate_one(idx[i], tok_req[t], bt, bt_stride, plog2, num_pages);
   }
 }
 
@@ -1097,10 +1101,10 @@ dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
 }
 
 dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req, const int32_t* block_table,
-                            int bt_stride, int plog2, int32_t* rows, hipStream_t stream) {
+                            int bt_stride, int plog2, int num_pages, int32_t* rows, hipStream_t stream) {
   const int64_t n = (int64_t)T * k;
   hipLaunchKernelGGL(translate_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 8192)), dim3(256), 0,
-                     stream, idx, k, T, tok_req, block_table, bt_stride, plog2, rows);
+                     stream, idx, k, T, tok_req, block_table, bt_stride, plog2, num_pages, rows);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

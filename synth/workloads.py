@@ -18,6 +18,7 @@ structure-of-arrays (every region 16-byte aligned for P a multiple of 4):
 
   key  FP8     [P x 128 E4M3 codes][P x fp32 scale]                 132 B/token
   key  MXFP4   [P x 64 B packed E2M1][P x 4 E8M0 (one per 32)]        68 B/token
+  key  NVFP4   [P x 64 B packed E2M1][P x 8 E4M3 (one per 16)]        72 B/token
 
 Latent rows are gathered one by one, so a latent page is P rows, each padded
 to a whole number of 128-byte lines with all of the row's bytes inside it:
@@ -47,11 +48,11 @@ D_LAT = 576      # latent dims (512 nope + 64 rope)
 D_V = 512        # value dims
 TOPK = 2048
 
-KEY_FP8, KEY_MXFP4 = "fp8", "mxfp4"
+KEY_FP8, KEY_MXFP4, KEY_NVFP4 = "fp8", "mxfp4", "nvfp4"
 LAT_BF16, LAT_FP8, LAT_NVFP4 = "bf16", "fp8", "nvfp4"
-Q_BF16, Q_FP8 = "bf16", "fp8"
+Q_BF16, Q_FP8, Q_MXFP4 = "bf16", "fp8", "mxfp4"
 
-KEY_TOKEN_BYTES = {KEY_FP8: 132, KEY_MXFP4: 68}
+KEY_TOKEN_BYTES = {KEY_FP8: 132, KEY_MXFP4: 68, KEY_NVFP4: 72}
 LAT_TOKEN_BYTES = {LAT_BF16: 1152, LAT_FP8: 580, LAT_NVFP4: 352}   # data bytes per token
 LAT_ROW_STRIDE = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}    # bytes per row in a page
 
@@ -62,6 +63,8 @@ def key_regions(fmt: str, P: int):
         return 0, 128, 128 * P, 4
     if fmt == KEY_MXFP4:
         return 0, 64, 64 * P, 4
+    if fmt == KEY_NVFP4:
+        return 0, 64, 64 * P, 8
     raise ValueError(fmt)
 
 
@@ -91,6 +94,7 @@ class Spec:
     causal_rows: bool = True    # row j of a request sees N - (q_per_req-1) + j tokens
     lat_std: float = 1.0        # std of latent values before quantisation
     plant_gap: bool = False     # plant a score gap at rank k (per query row)
+    w_signed: bool = False      # head weights U(-1, 1) instead of U(0, 1)
     sm_scale: float = 1.0 / math.sqrt(192.0)
     seed: int = 0
 
@@ -128,8 +132,8 @@ class Workload:
     block_table: Optional[torch.Tensor] # int32 [R, pages_per_req] or None (non-paged)
     key_pool: torch.Tensor              # uint8 [num_pages, P*key_bytes]
     lat_pool: torch.Tensor              # uint8 [num_pages, P*lat_row_stride]
-    q_idx: torch.Tensor                 # bf16 [T,32,128] or uint8 E4M3 codes
-    q_idx_scale: Optional[torch.Tensor] # fp32 [T,32] (FP8 q only)
+    q_idx: torch.Tensor                 # bf16 [T,32,128], uint8 E4M3 codes, or uint8 E2M1 pairs [T,32,64]
+    q_idx_scale: Optional[torch.Tensor] # fp32 [T,32] (FP8 q), uint8 E8M0 [T,32,4] (MXFP4 q)
     w: torch.Tensor                     # fp32 [T,32]
     q_mla: torch.Tensor                 # bf16 [T,H,576]
     hot: Optional[torch.Tensor]         # int64 [T, k] planted top-k sets (sorted), or None
@@ -165,10 +169,14 @@ def _write_key_rows(pool, fmt, P, phys_pages, vals):
         codes, scale = codecs.fp8_rowwise(vals)
         pool[phys_pages, c_off:c_off + P * c_b] = codes.reshape(npg, P * c_b)
         pool[phys_pages, s_off:s_off + P * s_b] = scale.contiguous().view(torch.uint8).reshape(npg, P * s_b)
-    else:
+    elif fmt == KEY_MXFP4:
         codes, e8 = codecs.mxfp4_blocks(vals, 32)
         pool[phys_pages, c_off:c_off + P * c_b] = codes.reshape(npg, P * c_b)
         pool[phys_pages, s_off:s_off + P * s_b] = e8.reshape(npg, P * s_b)
+    else:
+        codes, sc = codecs.nvfp4_blocks(vals, 16)
+        pool[phys_pages, c_off:c_off + P * c_b] = codes.reshape(npg, P * c_b)
+        pool[phys_pages, s_off:s_off + P * s_b] = sc.reshape(npg, P * s_b)
 
 
 def _write_lat_rows(pool, fmt, P, phys_pages, vals):
@@ -239,10 +247,17 @@ def make_workload(spec: Spec, device="cpu", seed: Optional[int] = None) -> Workl
         q_idx = codecs.bf16_bits(qf)
         q_idx_scale = None
         q_eff = q_idx.float()
-    else:
+    elif spec.q_fmt == Q_FP8:
         q_idx, q_idx_scale = codecs.fp8_rowwise(qf)
         q_eff = codecs.e4m3_value(q_idx) * q_idx_scale.unsqueeze(-1)
+    else:
+        # MXFP4 query (E2M1 pairs + E8M0 per 32 dims); the planting direction
+        # only needs an approximation of the query, so the BF16 values serve
+        q_idx, q_idx_scale = codecs.mxfp4_blocks(qf, 32)
+        q_eff = codecs.bf16_bits(qf).float()
     w = torch.rand(T, HI, generator=g, device=device)
+    if spec.w_signed:
+        w = 2.0 * w - 1.0
     q_mla = codecs.bf16_bits(torch.randn(T, spec.H, D_LAT, generator=g, device=device))
 
     # planted sets: row t gets its own k keys (disjoint within a request),
@@ -315,3 +330,21 @@ def random_logical(wl: Workload, k: int, seed: int = 11, device=None):
         m = min(k, n)
         idx[t, :m] = torch.sort(torch.randperm(n, generator=g)[:m]).values.to(torch.int32)
     return idx.to(device)
+
+
+def mark_absent(wl: Workload, n_entries: int, seed: int = 5):
+    """Seeded damage to the block table for tests of absent pages: n_entries
+    distinct (request, logical page) entries are set, alternately, to -1 and
+    to num_pages + j (outside the pool).  Returns the new block table (int32,
+    on the workload's device) and the list of (request, logical page) hit."""
+    assert wl.block_table is not None
+    g = _gen("cpu", seed)
+    bt = wl.block_table.cpu().clone()
+    R, npg = bt.shape
+    pick = torch.randperm(R * npg, generator=g)[:n_entries]
+    hit = []
+    for j, e in enumerate(pick.tolist()):
+        r, lp = divmod(e, npg)
+        bt[r, lp] = -1 if j % 2 == 0 else wl.num_pages + j
+        hit.append((r, lp))
+    return bt.to(wl.block_table.device), hit

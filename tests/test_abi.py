@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert hasattr(lib, n), n
     assert set(declared_functions()) == set(dsa.EXPORTS)
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
 
 
 def test_struct_layouts_match_the_c_compiler(tmp_path):
@@ -83,6 +83,9 @@ def _idx_args(**kw):
     (dict(ld=8194), dsa.DSA_ERR_INVALID_ARG),
     (dict(q_fmt=7), dsa.DSA_ERR_UNSUPPORTED),
     (dict(q_fmt=dsa.Q_FP8), dsa.DSA_ERR_INVALID_ARG),            # FP8 q without q_scale
+    (dict(q_fmt=dsa.Q_FP8, q_scale=FAKE, keys=_cache(fmt=dsa.KEY_MXFP4, page_bytes=68 * 8192)),
+     dsa.DSA_ERR_UNSUPPORTED),                                    # FP8 q runs against FP8 keys only
+    (dict(keys=_cache(fmt=dsa.KEY_NVFP4, page_bytes=71 * 8192)), dsa.DSA_ERR_INVALID_ARG),  # NVFP4 page < 72 B/token
     (dict(keys=_cache(fmt=9)), dsa.DSA_ERR_UNSUPPORTED),
     (dict(keys=_cache(plog2=3)), dsa.DSA_ERR_INVALID_ARG),
     (dict(keys=_cache(page_bytes=1000)), dsa.DSA_ERR_INVALID_ARG),
@@ -139,8 +142,8 @@ def test_indexer_prefix_rejects_fp8_q_and_missing_table():
 
 
 def _topk_args(**kw):
-    a = dict(batch=_batch(), scores=FAKE, ld=8192, k=2048, idx=FAKE, rows=None, page_size_log2=0, count=None,
-             workspace=FAKE, workspace_bytes=1 << 40)
+    a = dict(batch=_batch(), scores=FAKE, ld=8192, k=2048, idx=FAKE, rows=None, page_size_log2=0, num_pages=0,
+             count=None, workspace=FAKE, workspace_bytes=1 << 40)
     a.update(kw)
     return dsa.TopkArgs(**a)
 
@@ -153,7 +156,9 @@ def _topk_args(**kw):
     (dict(workspace=None), dsa.DSA_ERR_WORKSPACE),
     (dict(workspace_bytes=100), dsa.DSA_ERR_WORKSPACE),
     (dict(workspace=FAKE + 64), dsa.DSA_ERR_WORKSPACE),
-    (dict(rows=FAKE, page_size_log2=2), dsa.DSA_ERR_INVALID_ARG),
+    (dict(rows=FAKE, page_size_log2=2, num_pages=4), dsa.DSA_ERR_INVALID_ARG),
+    (dict(rows=FAKE, page_size_log2=13, num_pages=0), dsa.DSA_ERR_INVALID_ARG),           # pool size needed
+    (dict(rows=FAKE, page_size_log2=13, num_pages=1 << 18), dsa.DSA_ERR_INVALID_ARG),     # rows past int32
 ])
 def test_topk_rejects_bad_arguments(mut, status):
     assert dsa.load().dsa_topk(ctypes.byref(_topk_args(**mut)), None) == status
@@ -267,9 +272,11 @@ def test_mla_rejects_bad_arguments(mut, status):
 def test_translate_rejects_bad_arguments():
     lib = dsa.load()
     b = _batch()
-    assert lib.dsa_translate_pages(None, 2048, ctypes.byref(b), 6, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_translate_pages(FAKE, 0, ctypes.byref(b), 6, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_translate_pages(FAKE, 2048, ctypes.byref(b), 30, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_translate_pages(None, 2048, ctypes.byref(b), 6, 10, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_translate_pages(FAKE, 0, ctypes.byref(b), 6, 10, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_translate_pages(FAKE, 2048, ctypes.byref(b), 30, 10, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_translate_pages(FAKE, 2048, ctypes.byref(b), 6, 0, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_translate_pages(FAKE, 2048, ctypes.byref(b), 6, 1 << 25, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
 
 
 def test_workspace_sizes():
@@ -327,6 +334,7 @@ def _ins_args(**kw):
     (dict(num_tokens=-1), dsa.DSA_ERR_INVALID_ARG),
     (dict(key_vals=None, lat_vals=None), dsa.DSA_ERR_INVALID_ARG),
     (dict(keys=_cache(fmt=7, plog2=6, page_bytes=132 * 64, pages=8)), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(keys=_cache(fmt=dsa.KEY_NVFP4, plog2=6, page_bytes=68 * 64, pages=8)), dsa.DSA_ERR_INVALID_ARG),
     (dict(keys=_cache(fmt=dsa.KEY_FP8, plog2=6, page_bytes=131 * 64, pages=8)), dsa.DSA_ERR_INVALID_ARG),
     (dict(latents=_cache(fmt=dsa.LAT_NVFP4, plog2=6, page_bytes=352 * 64, pages=8)), dsa.DSA_ERR_INVALID_ARG),
     (dict(latents=_cache(fmt=dsa.LAT_FP8, plog2=5, page_bytes=640 * 64, pages=8)), dsa.DSA_ERR_INVALID_ARG),

@@ -57,7 +57,7 @@ def test_quantize_q_bit_exact(fmt, gpu):
 
 def _pools(gpu, key_fmt, lat_fmt, P, npg, seed):
     g = np.random.default_rng(seed)
-    kb = {"fp8": 132, "mxfp4": 68}[key_fmt] * P
+    kb = {"fp8": 132, "mxfp4": 68, "nvfp4": 72}[key_fmt] * P
     lb = Q.LAT_ROW_STRIDE[lat_fmt] * P
     kp = g.integers(0, 256, (npg, kb)).astype(np.uint8)
     lp = g.integers(0, 256, (npg, lb)).astype(np.uint8)
@@ -65,7 +65,8 @@ def _pools(gpu, key_fmt, lat_fmt, P, npg, seed):
 
 
 @pytest.mark.parametrize("key_fmt,lat_fmt", [("fp8", "fp8"), ("fp8", "bf16"), ("fp8", "nvfp4"),
-                                             ("mxfp4", "nvfp4"), ("mxfp4", "fp8"), ("mxfp4", "bf16")])
+                                             ("mxfp4", "nvfp4"), ("mxfp4", "fp8"), ("mxfp4", "bf16"),
+                                             ("nvfp4", "nvfp4"), ("nvfp4", "fp8")])
 @pytest.mark.parametrize("paged", [True, False])
 def test_cache_insert_bit_exact(key_fmt, lat_fmt, paged, gpu):
     print(f"[gpu] cache_insert {key_fmt}/{lat_fmt} paged={paged}", flush=True)
@@ -86,6 +87,7 @@ def test_cache_insert_bit_exact(key_fmt, lat_fmt, paged, gpu):
     kv = g.standard_normal((n, 128)) * np.exp(g.uniform(-4, 4, (n, 1)))
     lv = g.standard_normal((n, 576)) * np.exp(g.uniform(-4, 4, (n, 1)))
     kv[1] = 0.0
+    kv[3, 16:32] = 0.0                       # a zero NVFP4 key block
     lv[2, :16] = 0.0                         # a zero NVFP4 block
     kvt, lvt = _bf16(kv, gpu), _bf16(lv, gpu)
     dsa.cache_insert(torch.from_numpy(tok_req).to(gpu), torch.from_numpy(tok_pos).to(gpu), R,

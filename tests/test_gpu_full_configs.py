@@ -6,7 +6,8 @@ oracle recomputes one by one.
   tp8_spec_decode_64k  rows of 3 requests (all 6 speculative rows each)
   long_decode_1m       2 of 4 rows (planted gap: bit-exact top-k sets)
   prefill_chunk_32k    8 rows spread over the chunk (first, last, ragged tail)
-  fp4_decode_256k      4 of 64 rows
+  fp4_decode_256k      4 of 64 rows (and 3 rows of the same workload with
+                       NVFP4 index keys)
 Tolerances as in test_gpu_parity.
 """
 import numpy as np
@@ -15,7 +16,7 @@ import torch
 
 import synth
 from oracle import dsa as O
-from tests.helpers import gpu_step, oracle_inputs
+from tests.helpers import assert_scores_close, gpu_step, oracle_inputs
 from tests.test_gpu_parity import _check_attention
 
 pytestmark = pytest.mark.gpu
@@ -26,12 +27,17 @@ SAMPLES = {
     "long_decode_1m": [0, 3],
     "prefill_chunk_32k": [0, 1, 517, 2048, 3001, 4094, 4095, 2],
     "fp4_decode_256k": [0, 17, 40, 63],
+    # the FP4 workload with NVFP4 index keys (72 B per key) in place of MXFP4
+    "fp4_decode_256k_nvfp4_keys": [0, 33, 63],
 }
+SPECS = dict(synth.CONFIGS)
+SPECS["fp4_decode_256k_nvfp4_keys"] = synth.CONFIGS["fp4_decode_256k"].replace(
+    name="fp4_decode_256k_nvfp4_keys", key_fmt="nvfp4", seed=1006)
 
 
 @pytest.mark.parametrize("name", list(SAMPLES))
 def test_full_size_sampled(name, gpu):
-    spec = synth.CONFIGS[name]
+    spec = SPECS[name]
     print(f"[gpu] full-size {name}", flush=True)
     wl = synth.make_workload(spec, device=gpu)
     step = gpu_step(wl, prefill=spec.q_per_req > 64)
@@ -43,13 +49,11 @@ def test_full_size_sampled(name, gpu):
     sc = step.scores
     idx = step.idx.cpu().numpy()
     cnt = step.count.cpu().numpy()
-    rel = 5e-5 if spec.q_fmt == "fp8" else 1e-5
     same = []
     for j, t in enumerate(res["t"]):
         n = int(wl.tok_vis[t])
         ref = res["scores"][j]
-        got = sc[t, :n].cpu().numpy().astype(np.float64)
-        assert np.abs(got - ref).max() <= rel * np.abs(ref).max(), f"row {t} scores"
+        assert_scores_close(sc[t, :n].cpu().numpy(), ref, inp, t, what=name)
         K = len(res["idx"][j])
         assert cnt[t] == K and np.all(idx[t, K:] == -1)
         sel = idx[t, :K]
