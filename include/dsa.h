@@ -295,6 +295,23 @@ typedef struct dsa_mla_args {
 dsa_status sparse_mla_decode(const dsa_mla_args* args, hipStream_t stream);
 dsa_status sparse_mla_prefill(const dsa_mla_args* args, hipStream_t stream);
 
+/* sparse_mla_decode_noalloc -- sparse_mla_decode for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, kernels and results as
+ * sparse_mla_decode, except that args->workspace / workspace_bytes are
+ * ignored: the split partials live in a device array inside the library, 32
+ * MiB per GPU (DSA_MLA_SCRATCH_BYTES), held until the process ends.  The call
+ * allocates nothing; its first call on a device resolves that device's copy
+ * of the array (a symbol-address query, no allocation).  With num_splits = 0
+ * the automatic split count is lowered until the partials, T x splits x H x
+ * 2052 bytes, fit; an explicit num_splits whose partials do not fit returns
+ * DSA_ERR_WORKSPACE.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (different streams, or different threads) race and
+ * must be serialised by the caller.  Errors as sparse_mla_decode, plus
+ * DSA_ERR_HIP when the scratch address cannot be resolved. */
+#define DSA_MLA_SCRATCH_BYTES (32u << 20)
+dsa_status sparse_mla_decode_noalloc(const dsa_mla_args* args, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Front end of a step (Kimi K3.1 Pro day-0 page, "Low-latency decoding: the
  * fused DSA decode path": the indexer front end quantises the index query to

@@ -39,7 +39,7 @@ LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per l
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
            "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
            "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded",
-           "dsa_msa_decode", "dsa_indexer_scores_prefix")
+           "dsa_msa_decode", "dsa_indexer_scores_prefix", "sparse_mla_decode_noalloc")
 
 
 class DsaError(RuntimeError):
@@ -138,6 +138,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        ("dsa_topk", [ctypes.POINTER(TopkArgs), vp]),
                        ("sparse_mla_decode", [ctypes.POINTER(MlaArgs), vp]),
                        ("sparse_mla_prefill", [ctypes.POINTER(MlaArgs), vp]),
+                       ("sparse_mla_decode_noalloc", [ctypes.POINTER(MlaArgs), vp]),
                        ("dsa_translate_pages", [vp, i32, ctypes.POINTER(Batch), i32, i32, vp, vp]),
                        ("dsa_quantize_q", [ctypes.POINTER(QuantQArgs), vp]),
                        ("dsa_cache_insert", [ctypes.POINTER(InsertArgs), vp]),
@@ -235,6 +236,12 @@ def sparse_mla_decode(args: MlaArgs, stream=None):
 
 def sparse_mla_prefill(args: MlaArgs, stream=None):
     _check(load().sparse_mla_prefill(ctypes.byref(args), _stream(stream)), "sparse_mla_prefill")
+
+
+def sparse_mla_decode_noalloc(args: MlaArgs, stream=None):
+    """sparse_mla_decode with the split partials in the library's own device
+    scratch (args.workspace is ignored); nothing is allocated."""
+    _check(load().sparse_mla_decode_noalloc(ctypes.byref(args), _stream(stream)), "sparse_mla_decode_noalloc")
 
 
 def dsa_quantize_q(args: QuantQArgs, stream=None):

@@ -133,7 +133,7 @@ struct MlaPlan {
   int Hpad, ntiles, nsplit, split_len;
   size_t off_po, off_pl, total;
 };
-MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
+MlaPlan plan_mla(const dsa_mla_args& a, bool prefill, int max_splits = 64) {
   MlaPlan pl;
   pl.Hpad = (a.num_heads + 15) / 16 * 16;
   pl.ntiles = pl.Hpad / 16;
@@ -149,6 +149,7 @@ MlaPlan plan_mla(const dsa_mla_args& a, bool prefill) {
     const int64_t resident = 256 * sh.resident_per_cu;
     const int64_t per_split = (int64_t)a.num_rows * sh.groups;
     want = (int)std::min<int64_t>(64, std::max<int64_t>(1, resident / per_split));
+    want = std::min(want, max_splits);
   }
   want = std::max(1, std::min({want, (a.k + 15) / 16, 64}));
   pl.split_len = ((a.k + want - 1) / want + 15) / 16 * 16;
@@ -178,11 +179,27 @@ dsa_status check_mla(const dsa_mla_args* a) {
   return check_cache(a->latents, lat_row_bytes(a->latents.fmt), "mla latents");
 }
 
-dsa_status run_mla(const dsa_mla_args* a, hipStream_t stream, bool prefill) {
+// Split count of an allocation-free decode call: the automatic count,
+// lowered until the partials fit the device scratch (an explicit count is
+// kept and checked by the caller).
+MlaPlan plan_mla_in_scratch(const dsa_mla_args& a) {
+  MlaPlan pl = plan_mla(a, false);
+  for (int cap = pl.nsplit - 1; a.num_splits == 0 && pl.total > dsa::kMlaScratchBytes && cap >= 1; --cap)
+    pl = plan_mla(a, false, cap);
+  return pl;
+}
+
+// scratch != NULL: the partials go to that device scratch (the
+// allocation-free entry point), and the workspace arguments are ignored.
+dsa_status run_mla(const dsa_mla_args* a, hipStream_t stream, bool prefill, void* scratch = nullptr) {
   dsa_status st = check_mla(a);
   if (st != DSA_OK) return st;
-  const MlaPlan pl = plan_mla(*a, prefill);
-  if (pl.total > 0) {
+  const MlaPlan pl = scratch ? plan_mla_in_scratch(*a) : plan_mla(*a, prefill);
+  if (scratch) {
+    if (pl.total > dsa::kMlaScratchBytes)
+      return fail(DSA_ERR_WORKSPACE, "mla_noalloc: %d splits need %zu bytes of partials, above the %zu-byte scratch",
+                  pl.nsplit, pl.total, dsa::kMlaScratchBytes);
+  } else if (pl.total > 0) {
     if (!a->workspace || !aligned(a->workspace, 256))
       return fail(DSA_ERR_WORKSPACE, "mla: workspace null or not 256-byte aligned (%zu bytes needed)", pl.total);
     if (a->workspace_bytes < pl.total)
@@ -206,7 +223,7 @@ dsa_status run_mla(const dsa_mla_args* a, hipStream_t stream, bool prefill) {
   p.split_len = pl.split_len;
   p.out = a->out;
   p.lse = a->lse;
-  char* ws = static_cast<char*>(a->workspace);
+  char* ws = static_cast<char*>(scratch ? scratch : a->workspace);
   p.part_o = pl.nsplit > 1 ? reinterpret_cast<float*>(ws + pl.off_po) : nullptr;
   p.part_lse = pl.nsplit > 1 ? reinterpret_cast<float*>(ws + pl.off_pl) : nullptr;
   st = dsa::launch_mla(p, stream);
@@ -578,6 +595,21 @@ dsa_status sparse_mla_decode(const dsa_mla_args* a, hipStream_t stream) {
 dsa_status sparse_mla_prefill(const dsa_mla_args* a, hipStream_t stream) {
   g_err[0] = 0;
   return run_mla(a, stream, true);
+}
+
+dsa_status sparse_mla_decode_noalloc(const dsa_mla_args* a, hipStream_t stream) {
+  g_err[0] = 0;
+  dsa_status st = check_mla(a);
+  if (st != DSA_OK) return st;
+  const MlaPlan pl = plan_mla_in_scratch(*a);
+  if (pl.total > dsa::kMlaScratchBytes)
+    return fail(DSA_ERR_WORKSPACE, "mla_noalloc: %d splits need %zu bytes of partials, above the %zu-byte scratch",
+                pl.nsplit, pl.total, dsa::kMlaScratchBytes);
+  void* scratch = nullptr;
+  if (dsa::mla_scratch(&scratch) != DSA_OK)
+    return fail(DSA_ERR_HIP, "mla_noalloc: the device scratch address could not be resolved: %s",
+                hipGetErrorString(hipGetLastError()));
+  return run_mla(a, stream, false, scratch);
 }
 
 dsa_status dsa_quantize_q(const dsa_quant_q_args* a, hipStream_t stream) {

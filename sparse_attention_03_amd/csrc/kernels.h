@@ -203,5 +203,9 @@ dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok
                             const int32_t* block_table, int bt_stride, int plog2, int num_pages, int32_t* rows,
                             hipStream_t stream);
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream);
+// Bytes of the device-resident scratch of sparse_mla_decode_noalloc (split
+// partials), and its address on the current device (resolved on first use).
+constexpr size_t kMlaScratchBytes = DSA_MLA_SCRATCH_BYTES;
+dsa_status mla_scratch(void** ptr);
 
 }  // namespace dsa

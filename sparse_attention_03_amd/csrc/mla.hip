@@ -38,6 +38,8 @@
 //            column per lane, which one transposing LDS read
 //            (ds_read_b64_tr_b16) delivers per MFMA.  Lane (g, c)
 //            accumulates heads 4g+i at dims 64a + 16u + c.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -603,6 +605,32 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   *reinterpret_cast<f32x4*>(p.out + ((int64_t)t * p.H + h) * 512 + 4 * tid) = acc * inv;
   if (tid == 0 && p.lse) p.lse[(int64_t)t * p.H + h] = tot > 0.f ? mx + __logf(tot) : -__builtin_inff();
+}
+
+// Scratch of the allocation-free decode entry point: the split partials of
+// one call live in this file-scope device array (one copy per GPU, held until
+// the process ends) instead of a caller workspace.  Host code never uses the
+// array's name as an address: its device address is resolved once per device
+// with hipGetSymbolAddress and kept.
+static __device__ __align__(256) uint8_t scratch[kMlaScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+dsa_status mla_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DSA_OK;
 }
 
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     for n in ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
               "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
               "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded", "dsa_msa_decode",
-              "dsa_indexer_scores_prefix"):
+              "dsa_indexer_scores_prefix", "sparse_mla_decode_noalloc"):
         assert n in names
 
 
