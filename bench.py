@@ -466,7 +466,12 @@ def main():
     # the other reference workloads, timed by the same protocol
     others = {}
     if args.others:
-        for name, ospec in synth.CONFIGS.items():
+        extra = dict(synth.CONFIGS)
+        # the FP4 workload with MXFP4 index queries: the indexer on the FP4
+        # matrix instruction (no dequantisation), everything else as above
+        extra["fp4_decode_256k_mxfp4_q"] = synth.CONFIGS["fp4_decode_256k"].replace(
+            name="fp4_decode_256k_mxfp4_q", q_fmt="mxfp4")
+        for name, ospec in extra.items():
             if name == spec.name:
                 continue
             owl, ostep = build(ospec)

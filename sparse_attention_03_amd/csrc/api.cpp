@@ -264,11 +264,16 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
   if (a->batch.num_requests > 65535) return fail(DSA_ERR_INVALID_ARG, "indexer: more than 65535 requests");
   if (a->q_fmt == DSA_Q_FP8 && (int64_t)a->batch.max_rows_per_req > 16 * 65535)
     return fail(DSA_ERR_INVALID_ARG, "indexer: too many rows per request");
-  if (a->q_fmt != DSA_Q_BF16 && a->q_fmt != DSA_Q_FP8) return fail(DSA_ERR_UNSUPPORTED, "indexer: q_fmt %d", a->q_fmt);
+  if (a->q_fmt != DSA_Q_BF16 && a->q_fmt != DSA_Q_FP8 && a->q_fmt != DSA_Q_MXFP4)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: q_fmt %d", a->q_fmt);
   if (a->q_fmt == DSA_Q_FP8 && a->keys.fmt != DSA_KEY_FP8)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: FP8 q runs against FP8 keys only");
+  if (a->q_fmt == DSA_Q_MXFP4 && a->keys.fmt != DSA_KEY_MXFP4)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: MXFP4 q runs against MXFP4 keys only");
   if (a->q_fmt == DSA_Q_FP8 && (!a->q_scale || !aligned(a->q_scale, 16)))
     return fail(DSA_ERR_INVALID_ARG, "indexer: FP8 q needs a 16-byte aligned q_scale");
+  if (a->q_fmt == DSA_Q_MXFP4 && !a->q_scale)
+    return fail(DSA_ERR_INVALID_ARG, "indexer: MXFP4 q needs its E8M0 scales (q_scale)");
 
   dsa::IndexerParams p{};
   const dsa_batch& b = a->batch;
@@ -288,7 +293,17 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
   p.w = a->w;
   p.scores = a->scores;
   p.ld = a->ld;
-  if (a->q_fmt == DSA_Q_BF16) {
+  if (a->q_fmt == DSA_Q_MXFP4) {
+    p.q8 = static_cast<const uint8_t*>(a->q);
+    p.q_e8m0 = static_cast<const uint8_t*>(a->q_scale);
+    // keys per workgroup as for single-row BF16 requests (the streaming kernel)
+    const int64_t target = (int64_t)b.max_vis * b.num_requests / 2048;
+    int chunk = 256;
+    while (chunk < dsa::kIndexerRowChunkFp4 && chunk * 2 <= target) chunk *= 2;
+    p.chunk = chunk;
+    p.max_rows_per_req = b.max_rows_per_req;
+    st = dsa::launch_indexer_bf16(p, stream);
+  } else if (a->q_fmt == DSA_Q_BF16) {
     p.q = static_cast<const __bf16*>(a->q);
     // keys per workgroup, at most 4096.  Single-row requests stream keys and
     // want many workgroups in flight (about 2048); multi-row requests stage

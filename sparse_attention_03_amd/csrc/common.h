@@ -46,6 +46,19 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// D(16x16) += A(16x128) * B(128x16) with E2M1 (FP4) inputs and one E8M0 scale
+// per lane: lane l supplies 32 consecutive k-values of row l%16 of A (16
+// bytes of packed codes) and of column l%16 of B, each with the E8M0 code of
+// its 32-value block (the MX block); products and scales are exact and the
+// results accumulate in fp32.  D layout as above.
+__device__ __forceinline__ f32x4 mfma16x16x128_fp4(i32x4 a, uint32_t scale_a, i32x4 b, uint32_t scale_b, f32x4 c) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  // cbsz = blgp = 4 selects FP4 E2M1 for both operands; opsel 0 takes byte 0
+  // of each scale register
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, (int)scale_a, 0, (int)scale_b);
+}
+
 // ---------------------------------------------------------------- dequant
 // Two E4M3 values (bytes 0,1 or 2,3 of `w`) -> two bf16.  E4M3 has a 3-bit
 // mantissa and exponents 2^-9 .. 2^8, so the conversion is exact.

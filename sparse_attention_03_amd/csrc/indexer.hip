@@ -78,7 +78,10 @@ __device__ __forceinline__ void load_round(const IndexerParams& p, const int* pg
   for (int kt = 0; kt < kIdxKT; ++kt) {
     const int s0 = base + (wave * kIdxKT + kt) * 16;
     const int e = min((s0 >> p.plog2) - lp0, last);
-    const int pg = s0 < kend ? pg_lds[e] : -1;
+    // read unconditionally (e is clamped to a staged entry): a read under a
+    // branch would make each tile wait for its page id before the next is read
+    const int pg_read = pg_lds[e];
+    const int pg = s0 < kend ? pg_read : -1;
     pgs[kt] = pg;
     raw.ok[kt] = pg >= 0;
     const uint8_t* page = p.keys + (int64_t)max(pg, 0) * p.page_bytes;
@@ -349,8 +352,16 @@ template <int KFMT> struct KeyStream {
 static_assert(KeyStream<DSA_KEY_MXFP4>::kLds <= 65536 && KeyStream<DSA_KEY_NVFP4>::kLds <= 65536, "LDS");
 static_assert(KeyStream<DSA_KEY_FP8>::kLds <= 160 * 1024, "LDS");
 
-template <int KFMT>
-__global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) {
+// QF4 = false: BF16 queries on v_mfma_f32_16x16x32_bf16 over keys dequantised
+// exactly to bf16 (any key format).  QF4 = true (MXFP4 keys only): MXFP4
+// queries straight into v_mfma_scale_f32_16x16x128_f8f6f4 with both operands
+// E2M1 and the E8M0 block scales applied by the instruction (Kimi K3.1 Pro
+// page, AMD "native MXFP4 indexer": native FP4 matrix instructions, FP32
+// accumulation) -- one instruction per 16 heads x 16 keys x 128 dims, no
+// dequantisation.
+template <int KFMT, bool QF4>
+__global__ __launch_bounds__(256) void indexer_row_kernel(IndexerParams p) {
+  static_assert(!QF4 || KFMT == DSA_KEY_MXFP4, "FP4 queries run against MXFP4 keys");
   using KS = KeyStream<KFMT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* sc_out = reinterpret_cast<float*>(lds + 4 * KS::kDepth * KS::kRoundBytes);  // [chunk]
@@ -421,12 +432,22 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
     // the row's visible count, query fragments and head weights
     const int vis = __builtin_amdgcn_readfirstlane(min(p.tok_vis[t], p.max_vis));
     bf16x8 qa[2][4];
-    const __bf16* qrow = p.q + (int64_t)t * 32 * 128;
+    i32x4 q4[2];      // QF4: E2M1 codes of head 16hh + c, dims 32g .. 32g+31
+    uint32_t qe[2];   // QF4: their E8M0 scale
+    if (QF4) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh) {
+        q4[hh] = ld16(p.q8 + ((int64_t)t * 32 + 16 * hh + c) * 64 + 16 * g);
+        qe[hh] = p.q_e8m0[((int64_t)t * 32 + 16 * hh + c) * 4 + g];
+      }
+    } else {
+      const __bf16* qrow = p.q + (int64_t)t * 32 * 128;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          qa[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * hh + c) * 128 + kdim<KFMT, true>(kk, g)));
+    }
     const f32x4 w0 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 4 * g);
     const f32x4 w1 = *reinterpret_cast<const f32x4*>(p.w + (int64_t)t * 32 + 16 + 4 * g);
     // These loads must be complete, and known to the compiler to be, before the
@@ -453,7 +474,14 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
       for (int kt = 0; kt < kIdxKT; ++kt) {
         const uint8_t* tile = rd + kt * 16 * KS::kKeyBytes + c * KS::kKeyBytes;
         bf16x8 b[4];
-        if (KFMT == DSA_KEY_FP8) {
+        f32x4 a0, a1;
+        if (QF4) {
+          // key c's codes of dims 32g .. 32g+31 and their E8M0 scale g
+          const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
+          const uint32_t ke = (side[kt * 16 + c] >> (8 * g)) & 0xFFu;
+          a0 = mfma16x16x128_fp4(q4[0], qe[0], x, ke, f32x4{0.f, 0.f, 0.f, 0.f});
+          a1 = mfma16x16x128_fp4(q4[1], qe[1], x, ke, f32x4{0.f, 0.f, 0.f, 0.f});
+        } else if (KFMT == DSA_KEY_FP8) {
           const i32x4 x = *reinterpret_cast<const i32x4*>(tile + (g ^ KS::swz(c)) * 16);
           const i32x4 y = *reinterpret_cast<const i32x4*>(tile + ((4 + g) ^ KS::swz(c)) * 16);
           b[0] = e4m3x8_to_bf16x8(x[0], x[1]);
@@ -478,12 +506,14 @@ __global__ __launch_bounds__(256) void indexer_bf16_row_kernel(IndexerParams p) 
           b[2] = e2m1x8_times(x[2], s1);
           b[3] = e2m1x8_times(x[3], s1);
         }
-        f32x4 a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
-        f32x4 a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (!QF4) {
+          a0 = mfma16x16x32(qa[0][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
+          a1 = mfma16x16x32(qa[1][0], b[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int kk = 1; kk < 4; ++kk) {
-          a0 = mfma16x16x32(qa[0][kk], b[kk], a0);
-          a1 = mfma16x16x32(qa[1][kk], b[kk], a1);
+          for (int kk = 1; kk < 4; ++kk) {
+            a0 = mfma16x16x32(qa[0][kk], b[kk], a0);
+            a1 = mfma16x16x32(qa[1][kk], b[kk], a1);
+          }
         }
         float x = 0.f;
 #pragma unroll
@@ -573,19 +603,25 @@ dsa_status launch_prefix_prep(const int32_t* tok_vis, int T, int max_vis, int L,
 dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
   dim3 grid((p.max_vis + p.chunk - 1) / p.chunk, p.R);
   const size_t lds = (size_t)p.qrows * 32 * (kQPad * sizeof(__bf16) + sizeof(float));
-  if (p.max_rows_per_req == 1) {
+  if (p.q_e8m0) {
+    // MXFP4 queries: the streaming kernel on the FP4 matrix instruction, every
+    // row of a request in turn
+    hipLaunchKernelGGL((indexer_row_kernel<DSA_KEY_MXFP4, true>), grid, dim3(256), KeyStream<DSA_KEY_MXFP4>::kLds,
+                       stream, p);
+  } else if (p.max_rows_per_req == 1) {
     if (p.key_fmt == DSA_KEY_FP8) {
       // above the default 64 KiB of dynamic LDS (idempotent, host-side)
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(indexer_bf16_row_kernel<DSA_KEY_FP8>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(indexer_row_kernel<DSA_KEY_FP8, false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)KeyStream<DSA_KEY_FP8>::kLds) != hipSuccess)
         return DSA_ERR_HIP;
-      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_FP8>, grid, dim3(256), KeyStream<DSA_KEY_FP8>::kLds, stream, p);
+      hipLaunchKernelGGL((indexer_row_kernel<DSA_KEY_FP8, false>), grid, dim3(256), KeyStream<DSA_KEY_FP8>::kLds,
+                         stream, p);
     } else if (p.key_fmt == DSA_KEY_MXFP4) {
-      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_MXFP4>, grid, dim3(256), KeyStream<DSA_KEY_MXFP4>::kLds,
+      hipLaunchKernelGGL((indexer_row_kernel<DSA_KEY_MXFP4, false>), grid, dim3(256), KeyStream<DSA_KEY_MXFP4>::kLds,
                          stream, p);
     } else {
-      hipLaunchKernelGGL(indexer_bf16_row_kernel<DSA_KEY_NVFP4>, grid, dim3(256), KeyStream<DSA_KEY_NVFP4>::kLds,
+      hipLaunchKernelGGL((indexer_row_kernel<DSA_KEY_NVFP4, false>), grid, dim3(256), KeyStream<DSA_KEY_NVFP4>::kLds,
                          stream, p);
     }
   } else if (p.key_fmt == DSA_KEY_FP8) {

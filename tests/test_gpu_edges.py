@@ -36,6 +36,9 @@ ABSENT = {
                              seed=65),
     "spec_nvfp4": synth.Spec("spec_nvfp4", R=4, q_per_req=4, N=5000, key_fmt="nvfp4", lat_fmt="nvfp4", H=16,
                              k=512, seed=66),
+    # MXFP4 query rows on the FP4 matrix instruction
+    "row_fp4q": synth.Spec("row_fp4q", R=4, q_per_req=1, N=5000, key_fmt="mxfp4", lat_fmt="nvfp4", q_fmt="mxfp4",
+                           H=12, k=512, seed=70),
     # FP8 query rows (the prefill indexer), causal rows
     "fp8q": synth.Spec("fp8q", R=2, q_per_req=40, N=3000, key_fmt="fp8", lat_fmt="fp8", q_fmt="fp8", H=8,
                        k=512, seed=67),

@@ -6,8 +6,8 @@ oracle recomputes one by one.
   tp8_spec_decode_64k  rows of 3 requests (all 6 speculative rows each)
   long_decode_1m       2 of 4 rows (planted gap: bit-exact top-k sets)
   prefill_chunk_32k    8 rows spread over the chunk (first, last, ragged tail)
-  fp4_decode_256k      4 of 64 rows (and 3 rows of the same workload with
-                       NVFP4 index keys)
+  fp4_decode_256k      4 of 64 rows (and 3 rows each of the same workload
+                       with NVFP4 index keys, and with MXFP4 index queries)
 Tolerances as in test_gpu_parity.
 """
 import numpy as np
@@ -29,10 +29,14 @@ SAMPLES = {
     "fp4_decode_256k": [0, 17, 40, 63],
     # the FP4 workload with NVFP4 index keys (72 B per key) in place of MXFP4
     "fp4_decode_256k_nvfp4_keys": [0, 33, 63],
+    # the FP4 workload with MXFP4 index queries on the FP4 matrix instruction
+    "fp4_decode_256k_mxfp4_q": [1, 30, 62],
 }
 SPECS = dict(synth.CONFIGS)
 SPECS["fp4_decode_256k_nvfp4_keys"] = synth.CONFIGS["fp4_decode_256k"].replace(
     name="fp4_decode_256k_nvfp4_keys", key_fmt="nvfp4", seed=1006)
+SPECS["fp4_decode_256k_mxfp4_q"] = synth.CONFIGS["fp4_decode_256k"].replace(
+    name="fp4_decode_256k_mxfp4_q", q_fmt="mxfp4", seed=1007)
 
 
 @pytest.mark.parametrize("name", list(SAMPLES))
