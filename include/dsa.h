@@ -28,9 +28,14 @@
  *     it: the indexer writes -inf as the score of its tokens, the top-k ranks
  *     -inf below every finite score (equal -inf scores by lower index, like
  *     any tie) and translation turns its tokens into row -1, which attention
- *     skips, as it skips any row id < 0 or past the pool's last row.
- *   - No global mutable state: calls are re-entrant and may run concurrently
- *     on different streams with different buffers.
+ *     skips, as it skips any row id < 0 or past the pool's last row.  A row
+ *     whose tok_req names no request (outside [0, num_requests)) translates
+ *     to no rows (-1) and the MSA variant reads no block for it.  The debug
+ *     build notes every such clamp or skip (dsa_check_debug_flag).
+ *   - Calls are re-entrant and may run concurrently on different streams with
+ *     different buffers.  The only state the library holds is the per-GPU
+ *     scratch of sparse_mla_decode_noalloc (whose calls must not overlap on
+ *     one GPU) and, in the debug build, its status words.
  *
  * Paged caches (same page, "One KV cache, three states": the engine turns the
  * block table into kernel page addresses before each step).  A pool is a
@@ -193,9 +198,16 @@ dsa_status dsa_indexer_scores_prefix(const dsa_indexer_prefix_args* args, hipStr
  * same entries are also translated to physical latent rows (page * P + slot,
  * P = 2^page_size_log2) through batch.block_table, so attention can read them
  * directly (same page, "Low-latency fused DSA decode path": the fused indexer
- * emits physical KV rows).  count[t] = K_t if count != NULL.  Scores must be
- * finite; -0.0 ranks equal to +0.0.  The result of a row does not depend on
- * the other rows of the batch. */
+ * emits physical KV rows).  count[t] = K_t if count != NULL.  Scores are
+ * finite or -inf (the indexer's score of a token on an absent page); -inf
+ * ranks below every finite score and -0.0 equal to +0.0.  The result of a row
+ * does not depend on the other rows of the batch.  Errors: DSA_ERR_INVALID_ARG
+ * for k outside [1, 2048], an empty batch, a null or unaligned scores or idx,
+ * ld below max_vis or not a multiple of 4, and (rows != NULL) page_size_log2
+ * outside [4, 24], num_pages < 1 or num_pages x P above 2^31 - 1, a null
+ * tok_req or a block table too short for max_vis; DSA_ERR_WORKSPACE when the
+ * workspace is missing, unaligned or smaller than dsa_workspace_size(
+ * DSA_OP_TOPK, args). */
 typedef struct dsa_topk_args {
   dsa_batch batch;
   const float* scores;           /* device fp32 [T, ld]                        */
@@ -365,7 +377,7 @@ typedef struct dsa_insert_args {
   const int32_t* block_table;    /* device int32 [R, bt_stride] or NULL         */
   int32_t bt_stride;
   const void* key_vals;          /* device bf16 [n, 128] or NULL, 4-byte aligned */
-  dsa_cache keys;                /* fmt DSA_KEY_FP8 or DSA_KEY_MXFP4            */
+  dsa_cache keys;                /* fmt DSA_KEY_FP8, _MXFP4 or _NVFP4           */
   const void* lat_vals;          /* device bf16 [n, 576] or NULL, 16-byte aligned */
   dsa_cache latents;             /* fmt DSA_LAT_*; same page size as keys       */
 } dsa_insert_args;
@@ -422,6 +434,25 @@ size_t dsa_workspace_size(int32_t op, const void* args);
 const char* dsa_status_str(dsa_status status);
 const char* dsa_last_error(void);
 int32_t dsa_abi_version(void);
+
+/* dsa_check_debug_flag -- debug builds (the library compiled with
+ * DSA_DEBUG=1, libdsa_debug.so) bounds-check the device-resident metadata
+ * every kernel reads and note in a device status word what they had to
+ * clamp or skip (the survey's failure-detection item: explicit errors, no
+ * silent fallback):
+ *   DSA_DEBUG_VIS_CLAMPED    a visible count outside [0, max_vis]
+ *   DSA_DEBUG_ABSENT_PAGE    a block-table entry outside [0, num_pages)
+ *   DSA_DEBUG_ROW_OUTSIDE    a row id >= the pool's rows, or an index past its
+ *                            request's block-table row
+ *   DSA_DEBUG_REQ_OUTSIDE    a request id outside [0, num_requests)
+ * The call waits for the current device, returns the OR of these bits noted
+ * since the previous call and clears them.  Release builds return -1 (the
+ * checks are compiled out). */
+#define DSA_DEBUG_VIS_CLAMPED 1
+#define DSA_DEBUG_ABSENT_PAGE 2
+#define DSA_DEBUG_ROW_OUTSIDE 4
+#define DSA_DEBUG_REQ_OUTSIDE 8
+int32_t dsa_check_debug_flag(void);
 
 #ifdef __cplusplus
 }

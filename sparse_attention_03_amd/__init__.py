@@ -21,6 +21,10 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
+# the debug build (DSA_DEBUG=1): same entry points, plus device notes of the
+# metadata the kernels clamped or skipped (check_debug_flag)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libdsa_debug.so")
+DEBUG_VIS_CLAMPED, DEBUG_ABSENT_PAGE, DEBUG_ROW_OUTSIDE, DEBUG_REQ_OUTSIDE = 1, 2, 4, 8
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 KEY_FP8, KEY_MXFP4, KEY_NVFP4 = 1, 2, 3
@@ -39,7 +43,8 @@ LAT_ROW_BYTES = {LAT_BF16: 1152, LAT_FP8: 640, LAT_NVFP4: 384}     # bytes per l
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
            "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
            "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded",
-           "dsa_msa_decode", "dsa_indexer_scores_prefix", "sparse_mla_decode_noalloc")
+           "dsa_msa_decode", "dsa_indexer_scores_prefix", "sparse_mla_decode_noalloc",
+           "dsa_check_debug_flag")
 
 
 class DsaError(RuntimeError):
@@ -125,11 +130,15 @@ class InsertArgs(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libdsa.so (raises if it has not been built)."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libdsa.so (raises if it has not been built).  The environment
+    variable DSA_DEBUG_LIB=1 selects libdsa_debug.so instead; one process
+    holds one of the two."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = DEBUG_LIB_PATH if os.environ.get("DSA_DEBUG_LIB") == "1" else LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m sparse_attention_03_amd.build`")
     lib = ctypes.CDLL(path)
@@ -156,6 +165,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_abi_version.argtypes = []
     lib.dsa_abi_version.restype = ctypes.c_int32
+    lib.dsa_check_debug_flag.argtypes = []
+    lib.dsa_check_debug_flag.restype = ctypes.c_int32
     _lib = lib
     return lib
 
@@ -228,6 +239,12 @@ def dsa_translate_pages(idx: torch.Tensor, k: int, batch: Batch, page_size_log2:
                         rows: torch.Tensor, stream=None):
     _check(load().dsa_translate_pages(idx.data_ptr(), int(k), ctypes.byref(batch), int(page_size_log2),
                                       int(num_pages), rows.data_ptr(), _stream(stream)), "dsa_translate_pages")
+
+
+def dsa_check_debug_flag() -> int:
+    """Bits (DEBUG_*) the debug library's kernels noted since the last call,
+    cleared; waits for the device.  -1 from the release library."""
+    return int(load().dsa_check_debug_flag())
 
 
 def sparse_mla_decode(args: MlaArgs, stream=None):

@@ -1,4 +1,9 @@
-"""Build the HIP library libdsa.so for gfx950, in-tree (next to this file).
+"""Build the HIP library for gfx950, in-tree (next to this file):
+
+  libdsa.so        the release library;
+  libdsa_debug.so  the same sources with DSA_DEBUG=1: every kernel notes the
+                   device metadata it had to clamp or skip, read back with
+                   dsa_check_debug_flag().
 
     python -m sparse_attention_03_amd.build
 """
@@ -12,6 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
+DEBUG_LIB = os.path.join(HERE, "libdsa_debug.so")
 SOURCES = ["api.cpp", "indexer.hip", "indexer_fp8.hip", "topk.hip", "mla.hip", "quant.hip", "merge.hip", "msa.hip"]
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -28,17 +34,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def _command(out: str, debug: bool) -> list:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-x", "hip", *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("libdsa build failed")
-    os.replace(tmp, LIB)
+    extra = ["-DDSA_DEBUG=1"] if debug else []
+    return [hipcc(), *FLAGS, *extra, "-x", "hip", *srcs, "-o", out]
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile libdsa.so (and libdsa_debug.so unless debug=False), the two
+    compilations side by side; returns the release library's path."""
+    jobs = [(LIB, False)] + ([(DEBUG_LIB, True)] if debug else [])
+    procs = []
+    for out, dbg in jobs:
+        cmd = _command(out + ".tmp", dbg)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for out, pr in procs:
+        log, _ = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(log)
+            failed.append(os.path.basename(out))
+        else:
+            os.replace(out + ".tmp", out)
+    if failed:
+        raise RuntimeError("build failed: " + ", ".join(failed))
     return LIB
 
 

@@ -237,6 +237,18 @@ extern "C" {
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
+int32_t dsa_check_debug_flag(void) {
+#if DSA_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return -1;
+  const uint32_t v = dsa::debug_take_indexer() | dsa::debug_take_indexer_fp8() | dsa::debug_take_topk() |
+                     dsa::debug_take_mla() | dsa::debug_take_quant() | dsa::debug_take_merge() |
+                     dsa::debug_take_msa();
+  return (int32_t)v;
+#else
+  return -1;
+#endif
+}
+
 const char* dsa_last_error(void) { return g_err; }
 
 const char* dsa_status_str(dsa_status s) {
@@ -449,6 +461,7 @@ dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   p.ld = a->ld;
   p.tok_vis = b.tok_vis;
   p.tok_req = b.tok_req;
+  p.R = b.num_requests;
   p.max_vis = b.max_vis;
   p.k = a->k;
   p.block_table = b.block_table;
@@ -591,12 +604,12 @@ dsa_status dsa_translate_pages(const int32_t* idx, int32_t k, const dsa_batch* b
   g_err[0] = 0;
   if (!idx || !rows || !b) return fail(DSA_ERR_INVALID_ARG, "translate: null pointer");
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "translate: k %d", k);
-  if (b->num_rows < 1 || !b->tok_req) return fail(DSA_ERR_INVALID_ARG, "translate: bad batch");
+  if (b->num_rows < 1 || b->num_requests < 1 || !b->tok_req) return fail(DSA_ERR_INVALID_ARG, "translate: bad batch");
   if (page_size_log2 < 4 || page_size_log2 > 24) return fail(DSA_ERR_INVALID_ARG, "translate: page_size_log2");
   if (b->block_table && b->bt_stride < 1) return fail(DSA_ERR_INVALID_ARG, "translate: bt_stride");
   if (num_pages < 1 || ((int64_t)num_pages << page_size_log2) > INT32_MAX)
     return fail(DSA_ERR_INVALID_ARG, "translate: num_pages %d (rows of the pool must fit int32)", num_pages);
-  dsa_status st = dsa::launch_translate(idx, k, b->num_rows, b->tok_req, b->block_table, b->bt_stride,
+  dsa_status st = dsa::launch_translate(idx, k, b->num_rows, b->tok_req, b->num_requests, b->block_table, b->bt_stride,
                                         page_size_log2, num_pages, rows, stream);
   if (st != DSA_OK) return fail(st, "translate: launch failed: %s", hipGetErrorString(hipGetLastError()));
   return DSA_OK;

@@ -141,13 +141,53 @@ __device__ __forceinline__ i32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
 }
 
+// ---------------------------------------------------------------- debug notes
+// Debug builds (DSA_DEBUG=1) record, per translation unit, which kinds of
+// device-resident metadata the kernels had to clamp or skip; the host reads
+// and clears the words with dsa_check_debug_flag().  Release builds compile
+// the notes away.
+#ifndef DSA_DEBUG
+#define DSA_DEBUG 0
+#endif
+#if DSA_DEBUG
+static __device__ uint32_t dsa_debug_word;
+#define DSA_DEBUG_NOTE(cond, bit)                         \
+  do {                                                    \
+    if (cond) atomicOr(&dsa_debug_word, (uint32_t)(bit)); \
+  } while (0)
+// Host side of one translation unit's word: its value, cleared (0 when the
+// address cannot be resolved).
+#define DSA_DEBUG_TAKE(name)                                                          \
+  uint32_t debug_take_##name() {                                                      \
+    void* a = nullptr;                                                                \
+    uint32_t v = 0;                                                                   \
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(dsa_debug_word)) != hipSuccess || !a) return 0; \
+    if (hipMemcpy(&v, a, 4, hipMemcpyDeviceToHost) != hipSuccess) return 0;           \
+    if (hipMemset(a, 0, 4) != hipSuccess) return v;                                   \
+    return v;                                                                         \
+  }
+#else
+#define DSA_DEBUG_NOTE(cond, bit) \
+  do {                            \
+  } while (0)
+#define DSA_DEBUG_TAKE(name) \
+  uint32_t debug_take_##name() { return 0; }
+#endif
+
 // ---------------------------------------------------------------- paging
 // Physical page of logical page `lp` of request `r`, or -1 when the
 // block-table entry is outside the pool.
 __device__ __forceinline__ int phys_page(const int32_t* __restrict__ bt, int bt_stride, int r, int lp,
                                          int num_pages) {
   int pg = bt ? bt[(int64_t)r * bt_stride + lp] : r;
+  DSA_DEBUG_NOTE(pg < 0 || pg >= num_pages, DSA_DEBUG_ABSENT_PAGE);
   return (pg >= 0 && pg < num_pages) ? pg : -1;
+}
+
+// A visible count clamped to [0, max_vis].
+__device__ __forceinline__ int clamp_vis(int v, int max_vis) {
+  DSA_DEBUG_NOTE(v < 0 || v > max_vis, DSA_DEBUG_VIS_CLAMPED);
+  return min(max(v, 0), max_vis);
 }
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0.0 is

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
       if (i < nr * 512) qv[u] = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
     }
     if (tid < nr * 32) wv = p.w[(int64_t)t0 * 32 + tid];
-    if (tid < nr) vv = min(p.tok_vis[t0 + tid], p.max_vis);
+    if (tid < nr) vv = clamp_vis(p.tok_vis[t0 + tid], p.max_vis);
   };
   auto store_rows = [&](int nr) {
 #pragma unroll
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
       }
     }
     if (tid < nr2 * 32) ws[tid] = p.w[(int64_t)t0 * 32 + tid];
-    if (tid < nr2) s_vis[tid] = min(p.tok_vis[t0 + tid], p.max_vis);
+    if (tid < nr2) s_vis[tid] = clamp_vis(p.tok_vis[t0 + tid], p.max_vis);
   }
 }
 
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void indexer_row_kernel(IndexerParams p) {
     int issued = nfirst;  // rounds issued so far (round i uses ring slot i % kDepth)
 
     // the row's visible count, query fragments and head weights
-    const int vis = __builtin_amdgcn_readfirstlane(min(p.tok_vis[t], p.max_vis));
+    const int vis = __builtin_amdgcn_readfirstlane(clamp_vis(p.tok_vis[t], p.max_vis));
     bf16x8 qa[2][4];
     i32x4 q4[2];      // QF4: E2M1 codes of head 16hh + c, dims 32g .. 32g+31
     uint32_t qe[2];   // QF4: their E8M0 scale
@@ -633,5 +633,7 @@ dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
   }
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
+
+DSA_DEBUG_TAKE(indexer)
 
 }  // namespace dsa

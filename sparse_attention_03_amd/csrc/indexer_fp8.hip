@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
 
   // visible range of this workgroup's rows
   int vm = 0;
-  if (tid < nrows) vm = min(p.tok_vis[row0 + tid], p.max_vis);
+  if (tid < nrows) vm = clamp_vis(p.tok_vis[row0 + tid], p.max_vis);
   for (int o = 32; o > 0; o >>= 1) vm = max(vm, __shfl_xor(vm, o));
   if (lane == 0) s_vmax[wave] = vm;
   for (int i = tid; i < kF8BM * 32; i += 256) {
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
       }
       qa[j][hh] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    if (jr < nrows) vis[j] = min(p.tok_vis[row0 + jr], p.max_vis);
+    if (jr < nrows) vis[j] = clamp_vis(p.tok_vis[row0 + jr], p.max_vis);
   }
   f32x4 wv[4][2];
 #pragma unroll
@@ -175,5 +175,7 @@ dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(indexer_fp8_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
+
+DSA_DEBUG_TAKE(indexer_fp8)
 
 }  // namespace dsa

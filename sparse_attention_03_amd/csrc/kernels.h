@@ -52,6 +52,7 @@ struct TopkParams {
   int64_t ld;
   const int32_t* tok_vis;
   const int32_t* tok_req;
+  int R;                // requests: a row whose tok_req is outside [0, R) translates to -1
   int max_vis;
   int k;
   const int32_t* block_table;
@@ -104,7 +105,7 @@ struct MlaParams {
   int k;
   float sm_log2;            // sm_scale * log2(e)
   int nsplit;
-  int split_len;            // list entries per split (multiple of 32)
+  int split_len;            // list entries per split (multiple of 16)
   float* out;
   float* lse;
   float* part_o;            // [T][nsplit][H][512]
@@ -199,7 +200,7 @@ dsa_status launch_prefix_prep(const int32_t* tok_vis, int T, int max_vis, int L,
                               int32_t* sub_start, int32_t* sub_src, int32_t* vis1, int32_t* vis2, int32_t* ptab,
                               hipStream_t stream);
 dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hipStream_t stream);
-dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req,
+dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req, int R,
                             const int32_t* block_table, int bt_stride, int plog2, int num_pages, int32_t* rows,
                             hipStream_t stream);
 dsa_status launch_mla(const MlaParams& p, hipStream_t stream);
@@ -207,5 +208,15 @@ dsa_status launch_mla(const MlaParams& p, hipStream_t stream);
 // partials), and its address on the current device (resolved on first use).
 constexpr size_t kMlaScratchBytes = DSA_MLA_SCRATCH_BYTES;
 dsa_status mla_scratch(void** ptr);
+
+// Debug notes of each source file (dsa_check_debug_flag): the bits noted
+// since the last call, cleared; always 0 in release builds.
+uint32_t debug_take_indexer();
+uint32_t debug_take_indexer_fp8();
+uint32_t debug_take_topk();
+uint32_t debug_take_mla();
+uint32_t debug_take_quant();
+uint32_t debug_take_merge();
+uint32_t debug_take_msa();
 
 }  // namespace dsa

@@ -42,15 +42,15 @@ __device__ __forceinline__ int shard_count(int vis, int r, int W) {
   return vis > r ? (vis - r + W - 1) / W : 0;
 }
 
-__device__ __forceinline__ int clamp_vis(const MergeParams& p, int t) {
-  return min(max(p.tok_vis[t], 0), p.max_vis);
+__device__ __forceinline__ int row_vis(const MergeParams& p, int t) {
+  return clamp_vis(p.tok_vis[t], p.max_vis);
 }
 
 __global__ __launch_bounds__(256) void shard_vis_kernel(MergeParams p) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= p.W * p.T) return;
   const int r = i / p.T, t = i - r * p.T;
-  p.lvis[i] = shard_count(clamp_vis(p, t), r, p.W);
+  p.lvis[i] = shard_count(row_vis(p, t), r, p.W);
 }
 
 // One workgroup per shard row (r, t): the shard's selected local positions
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p, int
   const int tid = threadIdx.x;
   const int W = p.W;
   if (phase == 2 && p.rowflag[t] == 0) return;
-  const int vis = clamp_vis(p, t);
+  const int vis = row_vis(p, t);
   const int K = min(p.k, vis);
   int32_t* idx = p.idx + (int64_t)t * p.k;
   if (tid < W) {
@@ -250,5 +250,7 @@ dsa_status launch_topk_sharded(const MergeParams& p, const TopkParams& local, hi
   hipLaunchKernelGGL(merge_kernel, dim3(p.T), dim3(kMergeThreads), 0, stream, p, 2);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
+
+DSA_DEBUG_TAKE(merge)
 
 }  // namespace dsa

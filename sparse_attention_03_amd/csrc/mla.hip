@@ -79,6 +79,7 @@ struct RowPtr {
 };
 
 __device__ __forceinline__ bool row_ok(int id, const MlaParams& p) {
+  DSA_DEBUG_NOTE((id >> p.plog2) >= p.num_pages, DSA_DEBUG_ROW_OUTSIDE);
   return id >= 0 && (id >> p.plog2) < p.num_pages;
 }
 
@@ -668,5 +669,7 @@ dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
   if (p.nsplit > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(p.H, p.T), dim3(128), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
+
+DSA_DEBUG_TAKE(mla)
 
 }  // namespace dsa

@@ -34,11 +34,13 @@ constexpr int kAttnWaves = 8;
 constexpr int kAttnSplits = kMsaSplits;  // workgroups per (row, group)
 constexpr int kVStride = 136;   // bf16 per LDS V row (272 B)
 
-__device__ __forceinline__ int msa_vis(const MsaParams& p, int t) { return min(max(p.tok_vis[t], 0), p.max_vis); }
+__device__ __forceinline__ int msa_vis(const MsaParams& p, int t) { return clamp_vis(p.tok_vis[t], p.max_vis); }
 
 __device__ __forceinline__ int msa_page(const MsaParams& p, int r, int b) {
-  if (b < 0 || b >= p.bt_stride) return -1;
+  DSA_DEBUG_NOTE(b >= p.bt_stride, DSA_DEBUG_ROW_OUTSIDE);
+  if (r < 0 || b < 0 || b >= p.bt_stride) return -1;
   const int pg = p.bt[(int64_t)r * p.bt_stride + b];
+  DSA_DEBUG_NOTE(pg < 0 || pg >= p.pool_blocks, DSA_DEBUG_ABSENT_PAGE);
   return (pg >= 0 && pg < p.pool_blocks) ? pg : -1;
 }
 
@@ -193,7 +195,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void msa_attn_kernel(MsaParams p) 
   __shared__ float po[kAttnWaves][16][kD];
   const int tg = blockIdx.x, t = tg / p.hkv, grp = tg - t * p.hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
-  const int r = p.tok_req[t];
+  // a row whose tok_req names no request reads no block
+  const int r_raw = p.tok_req[t];
+  DSA_DEBUG_NOTE(r_raw < 0 || r_raw >= p.R, DSA_DEBUG_REQ_OUTSIDE);
+  const int r = (r_raw >= 0 && r_raw < p.R) ? r_raw : -1;
   const int vis = msa_vis(p, t);
   const int hbase = grp * p.G;
   const float lscale = p.sm_scale * p.k_scale;
@@ -368,5 +373,7 @@ dsa_status launch_msa(const MsaParams& p, int nblk_max, hipStream_t stream) {
   hipLaunchKernelGGL(msa_combine_kernel, dim3(p.T * p.hkv), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
+
+DSA_DEBUG_TAKE(msa)
 
 }  // namespace dsa

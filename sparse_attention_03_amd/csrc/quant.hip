@@ -137,11 +137,13 @@ __device__ __forceinline__ int insert_page(const InsertParams& p, int r, int pos
   int pg;
   if (p.block_table) {
     const int lp = pos >> plog2;
+    DSA_DEBUG_NOTE(lp >= p.bt_stride, DSA_DEBUG_ROW_OUTSIDE);
     if (lp >= p.bt_stride) return -1;
     pg = p.block_table[(int64_t)r * p.bt_stride + lp];
   } else {
     pg = r;
   }
+  DSA_DEBUG_NOTE(pg < 0 || pg >= num_pages, DSA_DEBUG_ABSENT_PAGE);
   return (pg >= 0 && pg < num_pages) ? pg : -1;
 }
 
@@ -149,6 +151,7 @@ template <int KFMT, int LFMT>
 __global__ __launch_bounds__(64) void cache_insert_kernel(InsertParams p) {
   const int i = blockIdx.x, l = threadIdx.x;
   const int r = p.tok_req[i], pos = p.tok_pos[i];
+  DSA_DEBUG_NOTE(r < 0 || r >= p.R, DSA_DEBUG_REQ_OUTSIDE);
   if (r < 0 || r >= p.R || pos < 0) return;
   if (KFMT != 0) {
     const int pg = insert_page(p, r, pos, p.key_plog2, p.key_num_pages);
@@ -253,5 +256,7 @@ dsa_status launch_cache_insert(const InsertParams& p, hipStream_t stream) {
 #undef DSA_INSERT
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
+
+DSA_DEBUG_TAKE(quant)
 
 }  // namespace dsa

@@ -39,7 +39,17 @@ constexpr int kMaxSamples = 16384;  // 16 per thread of the threshold workgroup
 constexpr int kRun = 16;            // consecutive scores per sampled block
 
 __device__ __forceinline__ int row_vis(const TopkParams& p, int t) {
-  return min(max(p.tok_vis[t], 0), p.max_vis);
+  return clamp_vis(p.tok_vis[t], p.max_vis);
+}
+
+// Request of row t, or -1 when tok_req names none of the batch's requests
+// (its translated rows are then -1: no block-table row is read).
+__device__ __forceinline__ int req_or_none(int r, int R) {
+  DSA_DEBUG_NOTE(r < 0 || r >= R, DSA_DEBUG_REQ_OUTSIDE);
+  return (r >= 0 && r < R) ? r : -1;
+}
+__device__ __forceinline__ int row_req(const TopkParams& p, int t) {
+  return p.tok_req ? req_or_none(p.tok_req[t], p.R) : 0;
 }
 
 // Wave-wide scans and reductions on DPP lane moves (no LDS round trip): an
@@ -382,19 +392,21 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
 }
 
 // Logical index li of request r -> physical row page * P + slot, or -1 for
-// no index, an index past the request's block-table row, or a page outside
-// [0, num_pages) (an absent page: nothing of it may be read).
+// no index or no request, an index past the request's block-table row, or a
+// page outside [0, num_pages) (an absent page: nothing of it may be read).
 __device__ __forceinline__ int translate_one(int li, int r, const int32_t* __restrict__ bt, int bt_stride,
                                              int plog2, int num_pages) {
-  if (li < 0) return -1;
+  if (li < 0 || r < 0) return -1;
   const int lp = li >> plog2;
   int pg;
   if (bt) {
+    DSA_DEBUG_NOTE(lp >= bt_stride, DSA_DEBUG_ROW_OUTSIDE);
     if (lp >= bt_stride) return -1;
     pg = bt[(int64_t)r * bt_stride + lp];
   } else {
     pg = r;
   }
+  DSA_DEBUG_NOTE(pg < 0 || pg >= num_pages, DSA_DEBUG_ABSENT_PAGE);
   if (pg < 0 || pg >= num_pages) return -1;
   return (pg << plog2) | (li & ((1 << plog2) - 1));
 }
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
   const int tid = threadIdx.x;
   const int vis = row_vis(p, t);
   const int K = min(p.k, vis);
-  const int r = p.tok_req ? p.tok_req[t] : 0;
+  const int r = row_req(p, t);
   int32_t* idx = p.idx + (int64_t)t * p.k;
   int32_t* rows = p.rows ? p.rows + (int64_t)t * p.k : nullptr;
   if (vis <= p.k) {
@@ -821,7 +833,7 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vis = row_vis(p, t);
   const int K = min(p.k, vis);
-  const int r = p.tok_req ? p.tok_req[t] : 0;
+  const int r = row_req(p, t);
   int32_t* idx = p.idx + (int64_t)t * p.k;
   int32_t* rows = p.rows ? p.rows + (int64_t)t * p.k : nullptr;
   if (vis <= p.k) {
@@ -1005,7 +1017,7 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkParams p)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vis = row_vis(p, t);
   const int K = min(p.k, vis);
-  const int r = p.tok_req ? p.tok_req[t] : 0;
+  const int r = row_req(p, t);
   int32_t* idx = p.idx + (int64_t)t * p.k;
   int32_t* rows = p.rows ? p.rows + (int64_t)t * p.k : nullptr;
   if (vis <= p.k) {
@@ -1075,12 +1087,12 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkParams p)
 }
 
 __global__ void translate_kernel(const int32_t* __restrict__ idx, int k, int T, const int32_t* __restrict__ tok_req,
-                                 const int32_t* __restrict__ bt, int bt_stride, int plog2, int num_pages,
+                                 int R, const int32_t* __restrict__ bt, int bt_stride, int plog2, int num_pages,
                                  int32_t* __restrict__ rows) {
   const int64_t n = (int64_t)T * k;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int t = (int)(i / k);
-    rows[i] = translate_one(idx[i], tok_req[t], bt, bt_stride, plog2, num_pages);
+    rows[i] = translate_one(idx[i], req_or_none(tok_req[t], R), bt, bt_stride, plog2, num_pages);
   }
 }
 
@@ -1100,12 +1112,14 @@ dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 
-dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req, const int32_t* block_table,
-                            int bt_stride, int plog2, int num_pages, int32_t* rows, hipStream_t stream) {
+dsa_status launch_translate(const int32_t* idx, int k, int T, const int32_t* tok_req, int R,
+                            const int32_t* block_table, int bt_stride, int plog2, int num_pages, int32_t* rows, hipStream_t stream) {
   const int64_t n = (int64_t)T * k;
   hipLaunchKernelGGL(translate_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 8192)), dim3(256), 0,
-                     stream, idx, k, T, tok_req, block_table, bt_stride, plog2, num_pages, rows);
+                     stream, idx, k, T, tok_req, R, block_table, bt_stride, plog2, num_pages, rows);
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
+
+DSA_DEBUG_TAKE(topk)
 
 }  // namespace dsa

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     for n in ("dsa_indexer_scores", "dsa_topk", "dsa_translate_pages", "sparse_mla_decode",
               "sparse_mla_prefill", "dsa_workspace_size", "dsa_status_str", "dsa_last_error",
               "dsa_abi_version", "dsa_quantize_q", "dsa_cache_insert", "dsa_topk_sharded", "dsa_msa_decode",
-              "dsa_indexer_scores_prefix", "sparse_mla_decode_noalloc"):
+              "dsa_indexer_scores_prefix", "sparse_mla_decode_noalloc", "dsa_check_debug_flag"):
         assert n in names
 
 
@@ -34,6 +34,47 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     assert set(declared_functions()) == set(dsa.EXPORTS)
     assert lib.dsa_abi_version() == 2
+    # the release build compiles the device notes out (no HIP call is made)
+    assert lib.dsa_check_debug_flag() == -1
+
+
+def test_debug_library_exports_every_declared_symbol():
+    """libdsa_debug.so (DSA_DEBUG=1) is built beside libdsa.so with the same
+    entry points; it is opened here without routing any call through it."""
+    assert os.path.exists(dsa.DEBUG_LIB_PATH), "build with python -m sparse_attention_03_amd.build"
+    lib = ctypes.CDLL(dsa.DEBUG_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    lib.dsa_abi_version.restype = ctypes.c_int32
+    assert lib.dsa_abi_version() == 2
+
+
+SANITIZE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sanitize")
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "sparse_attention_03_amd", "csrc")
+
+
+def test_host_abi_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """api.cpp, built for the host alone with ASan + UBSan and linked with
+    launch stubs that touch every buffer extent their kernels would (see
+    tests/sanitize/launch_stubs.cpp), runs every entry point on decode,
+    speculative, prefill, sharded, MSA and shared-prefix shapes with buffers
+    of exactly their documented sizes, and the argument errors.  Any
+    out-of-bounds access of a host plan, undefined behaviour or unexpected
+    status fails the run."""
+    clang = "/opt/rocm/llvm/bin/clang++"
+    if not os.path.exists(clang):
+        pytest.skip("ROCm clang++ is not installed")
+    exe = tmp_path / "abi_driver"
+    cmd = [clang, "-std=c++17", "-g", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-x", "c++",
+           os.path.join(CSRC, "api.cpp"), os.path.join(SANITIZE, "launch_stubs.cpp"),
+           os.path.join(SANITIZE, "abi_driver.cpp"), "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert run.returncode == 0, (run.stdout + run.stderr)[-4000:]
+    assert "abi driver ok" in run.stdout
 
 
 def test_struct_layouts_match_the_c_compiler(tmp_path):

@@ -5,7 +5,8 @@ Block selection: bit for bit on planted-gap inputs; elsewhere every selected
 block's oracle score is >= the oracle's cut - 1e-3 |cut| and the most recent
 block is present.  Attention: per (row, group), the oracle run on the blocks
 the GPU selected; max-abs-err <= 1e-2 x max |oracle output| (FP8 caches), lse
-within 1e-2.
+within 1e-3 (its logits are exact products summed in fp32; only the bf16
+softmax weights of the output carry the 1e-2).
 """
 import numpy as np
 import pytest
@@ -58,7 +59,10 @@ def _run(spec, gpu, rows_to_check=None, mutate=None):
             assert err <= 1e-2 * np.abs(og).max(), (t, g, err)
             gl = lse[t, g * G:(g + 1) * G]
             both_empty = np.isneginf(gl) & np.isneginf(lg)
-            assert np.all(both_empty | (np.abs(gl - lg) <= 1e-2)), (t, g)
+            close = np.zeros_like(both_empty)
+            fin = np.isfinite(gl) & np.isfinite(lg)
+            close[fin] = np.abs(gl[fin] - lg[fin]) <= 1e-3
+            assert np.all(both_empty | close), (t, g)
 
 
 @pytest.mark.parametrize("hkv,hq", [(4, 64), (1, 12), (2, 2), (8, 64)])
