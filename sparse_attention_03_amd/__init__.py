@@ -132,13 +132,13 @@ _lib = None
 
 def load(path: str | None = None) -> ctypes.CDLL:
     """Load libdsa.so (raises if it has not been built).  The environment
-    variable DSA_DEBUG_LIB=1 selects libdsa_debug.so instead; one process
-    holds one of the two."""
+    variable DSA_DEBUG_LIB=1 selects libdsa_debug.so instead, and DSA_LIB=path
+    any other build of the library; one process holds one library."""
     global _lib
     if _lib is not None:
         return _lib
     if path is None:
-        path = DEBUG_LIB_PATH if os.environ.get("DSA_DEBUG_LIB") == "1" else LIB_PATH
+        path = os.environ.get("DSA_LIB") or (DEBUG_LIB_PATH if os.environ.get("DSA_DEBUG_LIB") == "1" else LIB_PATH)
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m sparse_attention_03_amd.build`")
     lib = ctypes.CDLL(path)

@@ -221,6 +221,7 @@ dsa_status run_mla(const dsa_mla_args* a, hipStream_t stream, bool prefill, void
   p.sm_log2 = a->sm_scale * 1.4426950408889634f;
   p.nsplit = pl.nsplit;
   p.split_len = pl.split_len;
+  p.prefill = prefill ? 1 : 0;
   p.out = a->out;
   p.lse = a->lse;
   char* ws = static_cast<char*>(scratch ? scratch : a->workspace);

@@ -110,6 +110,7 @@ struct MlaParams {
   float* lse;
   float* part_o;            // [T][nsplit][H][512]
   float* part_lse;          // [T][nsplit][H]
+  int prefill;              // one split per row over all heads (sparse_mla_prefill)
 };
 
 // Workgroup shape of the sparse-MLA kernels: `groups` workgroups per (row,
@@ -124,6 +125,18 @@ struct MlaShape {
 // the two waves then share; both compute the tile's scores, each multiplies
 // its half of the values).  For FP8 latents the second wave only repeats the
 // score chain that bounds the tile, so it stays at one.
+// Prefill over FP8 latents (the ring kernel, about 20 KB of LDS per workgroup
+// whatever its waves): one wave per head tile, eight waves per CU (two per
+// SIMD, the register limit) -- one workgroup for up to two head tiles, else
+// workgroups of two (96 heads: three per row) or four.
+inline MlaShape mla_shape_fp8(int ntiles) {
+  MlaShape s;
+  s.nw = ntiles <= 2 ? ntiles : (ntiles % 4 == 0 ? 4 : 2);
+  s.groups = (ntiles + s.nw - 1) / s.nw;
+  s.vs = 1;
+  s.resident_per_cu = 8 / s.nw;
+  return s;
+}
 inline MlaShape mla_shape(int ntiles, bool split_values) {
   MlaShape s;
   s.groups = (ntiles + 3) / 4;

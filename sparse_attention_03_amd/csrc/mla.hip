@@ -400,11 +400,20 @@ inline size_t mla_dma_lds_bytes(int segs, int depth, int split_len) {
   return (size_t)kRT * kLPad * 2 + (size_t)depth * (segs * 1024 + 1024) + ((size_t)split_len * 4 + 15) / 16 * 16;
 }
 
+// Direct HBM -> LDS copies.  NT = true sets the nontemporal hint: decode
+// gathers rows no other workgroup reads again, and cached copies would also
+// pay for evicting whatever dirty lines the caches hold (measured: 103 -> 72
+// us on the 64K speculative batch); prefill rows are gathered by many query
+// rows of the same request and keep the default, caching, policy.
+template <bool NT>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+  if (NT) asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds) : "memory", "m0");
+  else asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
+template <bool NT>
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+  if (NT) asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt" : : "v"(src), "s"(lds) : "memory", "m0");
+  else asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -463,14 +472,14 @@ __global__ __launch_bounds__(64 * NW, VS) void mla_dma_kernel(MlaParams p) {
       // row scale of row lane >> 2 (lanes 4r .. 4r+3 carry row r's)
       const int id = id_at(tile, my_row);
       const uint8_t* src = row_ok(id, p) ? row_of(id) + LatRow<FMT>::kScale : g_zero_row;
-      dma4(src, side_l + slot * 1024);
+      dma4<true>(src, side_l + slot * 1024);
     } else {
       // 32 bytes of E4M3 block scales per row: lane l < 32 copies half l & 1
       // of row l >> 1 (lanes 32..63 repeat rows 0..15 into the slot's tail)
       const int r = (lane >> 1) & 15;
       const int id = id_at(tile, r);
       const uint8_t* src = row_ok(id, p) ? row_of(id) + LatRow<FMT>::kScales + (lane & 1) * 16 : g_zero_row;
-      dma16(src, side_l + slot * 1024);
+      dma16<true>(src, side_l + slot * 1024);
     }
     const int id = id_at(tile, my_row);
     // an absent row reads the zero row (never past its 1280 bytes)
@@ -480,7 +489,7 @@ __global__ __launch_bounds__(64 * NW, VS) void mla_dma_kernel(MlaParams p) {
       const int sp = min(wave + i * NW, SEGS - 1);
       // FP8: 9 segments of 64 codes; NVFP4: 4 segments of codes, then the rope
       const int off = (FMT == DSA_LAT_NVFP4 && sp == 4) ? LatRow<FMT>::kRope : sp * 64;
-      dma16(row + off + q * 16, raw_l + slot * kRawBytes + sp * 1024);
+      dma16<true>(row + off + q * 16, raw_l + slot * kRawBytes + sp * 1024);
     }
   };
   // copies still outstanding (tiles it+1 .. it+DP-1) when tile it is consumed
@@ -569,6 +578,197 @@ __global__ __launch_bounds__(64 * NW, VS) void mla_dma_kernel(MlaParams p) {
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
   mla_finish<NA>(p, O, m, l, t, split, ht, g, c, a0);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill over FP8 latents: 16-row tiles computed straight from a small copy
+// ring.  (Decode keeps mla_dma_kernel: there the row gather, not the tile
+// chain, bounds the time, and its deeper copy ring with nontemporal copies
+// gathers faster: 72 against 88 us on the 64K speculative batch.)
+//
+// No BF16 copy of a tile is made: the copies land in LDS in the order the
+// MFMA operands want them and every wave converts the FP8 codes it needs in
+// registers (exact: E4M3 -> BF16).  A workgroup needs under 20 KB of LDS (two
+// ring slots and a ring of row ids), so eight one-wave workgroups share a CU:
+// two waves per SIMD, whose MFMA and VALU work interleave (one wave per SIMD
+// leaves every instruction waiting on its predecessor's latency).
+//
+// Ring slot (one tile): 9 segments of 1 KB and the 16 FP8 row scales.  Copy
+// instruction sp: lane L = 16 j + r copies bytes 64 sp + 16 j .. +15 of row r
+// to slot offset sp * 1024 + 16 L.  The row ids come through a ring of their
+// own (one 4-byte copy per lane, three tiles ahead), so no copy address ever
+// waits on an id load and the list need not be staged whole.
+//   QK  S^T[rows x heads] on v_mfma_f32_16x16x32_bf16: k-step kk (< 18) of
+//       lane (g, c) covers dims 64 (kk/2) + 16 g + 8 (kk%2) .. +7 of latent row
+//       c (its own copy position, 16 bytes for two k-steps) and of head c;
+//       lane (g, c) gets rows 4g+i of head c.
+//   PV  O[heads x 512] += P[heads x 16] . V[16 x 512] on
+//       v_mfma_f32_16x16x16_bf16 (A: the weights of rows 4g+i, in the lanes
+//       that computed them).  One transposing byte read (ds_read_b64_tr_b8:
+//       result lane c, byte j is byte c%8 of the 8 bytes source lane 2j + c/8
+//       points at) gives every lane rows 4g..4g+3 of two dims, d0 + c (bytes
+//       0-3) and d0 + 16 + c (bytes 4-7): the V operands of two MFMAs.
+// The per-row FP8 scale multiplies the logit and the softmax weight.
+constexpr int kF8Depth = 2;                    // ring slots: tile it+1 lands while tile it computes
+constexpr int kF8ScaleOff = 9 * 1024;
+constexpr int kF8Slot = kF8ScaleOff + 256;
+constexpr int kF8IdSlots = 4;                  // id ring: tiles it .. it+3
+constexpr int kF8Lds = kF8Depth * kF8Slot + kF8IdSlots * 256;
+constexpr int kF8Copies = 9 + 1;               // copies per tile: 9 segments, the row scales
+static_assert(kF8Lds <= 160 * 1024 / 8, "eight workgroups per CU");
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
+  constexpr int kPer = (kF8Copies + NW - 1) / NW;  // copies per wave per tile (the last one repeated)
+  static_assert(2 + 2 * kPer < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kF8Lds];
+  uint8_t* idr = ring + kF8Depth * kF8Slot;  // [kF8IdSlots][64 ints]
+
+  const int split = blockIdx.x, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ht = blockIdx.z * NW + wave;
+  const bool active = ht < p.ntiles;  // a wave past the last head tile only copies
+  const int g = lane >> 4, c = lane & 15;
+  const int j_begin = split * p.split_len;
+  const int n_ids = min(j_begin + p.split_len, p.k) - j_begin;  // >= 1
+  const int ntile = (n_ids + kRT - 1) / kRT;
+  const int P = 1 << p.plog2;
+  const int32_t* rlist = p.rows + (int64_t)t * p.k + j_begin;
+  const uint32_t ring_l = lds_addr(ring), idr_l = lds_addr(idr);
+
+  // id copy of tile `tile` (every wave issues it: identical bytes)
+  auto copy_ids = [&](int tile) {
+    dma4<false>(rlist + min(tile * kRT + c, n_ids - 1), idr_l + (tile % kF8IdSlots) * 256);
+  };
+  // id of row r of a tile whose ids have landed (-1 past the split's end)
+  auto id_at = [&](int tile, int r) -> int {
+    const int v = reinterpret_cast<const int*>(idr + (tile % kF8IdSlots) * 256)[r];
+    return tile * kRT + r < n_ids ? v : -1;
+  };
+  auto row_of = [&](int id) -> const uint8_t* {
+    return row_ok(id, p) ? p.lat + (int64_t)(id >> p.plog2) * p.page_bytes + (int64_t)(id & (P - 1)) * 640
+                         : g_zero_row;
+  };
+  // this wave's copies of tile `tile` into ring slot `slot`: kPer of them
+  // whatever the tile, so one vmcnt count is exact
+  auto copy_tile = [&](int tile, int slot) {
+    const uint8_t* row = row_of(id_at(tile, c));
+    const uint32_t base = ring_l + slot * kF8Slot;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int x = min(wave + i * NW, kF8Copies - 1);  // uniform
+      if (x < 9) dma16<false>(row + 64 * x + 16 * g, base + x * 1024);
+      else dma4<false>(row + 576, base + kF8ScaleOff);
+    }
+  };
+
+  // query fragments of head 16 ht + c in the k-step order above
+  bf16x8 qf[18];
+  {
+    const int head = 16 * ht + c;
+    if (active && head < p.H) {
+      const __bf16* qp = p.q + ((int64_t)t * p.H + head) * 576 + 16 * g;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, ld16(qp + 64 * (kk >> 1) + 8 * (kk & 1)));
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qf[kk] = bf16x8{};
+    }
+  }
+  f32x4 O[32];
+#pragma unroll
+  for (int x = 0; x < 32; ++x) O[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), l = 0.f;
+
+  // Prologue.  Issue order per wave from here on: ids(0) ids(1) | copies(0) |
+  // ids(2) copies(1) | then at the end of every tile it: ids(it+3) copies(it+2).
+  copy_ids(0);
+  copy_ids(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the ids and (seen by the compiler) the query loads
+  copy_tile(0, 0);
+  copy_ids(2);
+  copy_tile(1, 1);
+
+  // transposed-read source of this lane: byte slot j = (lane%16)/2 -> row
+  // 4g + j%4 of dim chunk j/4 (+16 dims), half lane%2 of the 16 bytes
+  const int tj = (lane & 15) >> 1;
+  const int t_off = (tj >> 2) * 256 + (4 * g + (tj & 3)) * 16 + 8 * (lane & 1);
+
+  for (int it = 0; it < ntile; ++it) {
+    const int slot = it % kF8Depth;
+    wait_vmcnt<1 + kPer>();  // this wave's copies of tile `it` (ids(it+2), copies(it+1) may fly)
+    __syncthreads();         // ... and every other wave's
+    const uint8_t* sl = ring + slot * kF8Slot;
+    if (active) {
+      // ---- QK: two independent accumulator chains of nine
+      f32x4 s;
+      {
+        const uint8_t* src = sl + lane * 16;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < 9; ++sp) {
+          const i32x4 raw = *reinterpret_cast<const i32x4*>(src + sp * 1024);
+          s0 = mfma16x16x32(e4m3x8_to_bf16x8(raw[0], raw[1]), qf[2 * sp], s0);
+          s1 = mfma16x16x32(e4m3x8_to_bf16x8(raw[2], raw[3]), qf[2 * sp + 1], s1);
+        }
+        s = s0 + s1;
+      }
+      // ---- online softmax for head c over rows 4g+i
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(sl + kF8ScaleOff + 16 * g);
+      float lg[4];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = row_ok(id_at(it, 4 * g + i), p) ? s[i] * p.sm_log2 * sc[i] : -__builtin_inff();
+        lg[i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+      tmax = fmaxf(tmax, xor16(tmax, g));
+      tmax = fmaxf(tmax, xor32(tmax, g));
+      const float mnew = (m == -__builtin_inff() || tmax > m + kRescaleLog2) ? tmax : m;
+      const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - mnew);
+      float psum = 0.f, pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = (lg[i] == -__builtin_inff() || mnew == -__builtin_inff()) ? 0.f : exp2f(lg[i] - mnew);
+        psum += e;
+        pw[i] = e * sc[i];
+      }
+      psum += xor16(psum, g);
+      psum += xor32(psum, g);
+      l = l * alpha + psum;
+      m = mnew;
+      const i32x2 pa2 = {(int)pack_bf16x2(pw[0], pw[1]), (int)pack_bf16x2(pw[2], pw[3])};
+      const bf16x4 pa = __builtin_bit_cast(bf16x4, pa2);
+      if (__ballot(alpha != 1.f)) {
+        float ai[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int x = 0; x < 32; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[x][i] *= ai[i];
+      }
+      // ---- PV: read n covers dims 32 n + c (O[2n]) and 32 n + 16 + c (O[2n+1])
+      const uint8_t* vsrc = sl + t_off;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const auto* a = (const __attribute__((address_space(3))) v2i*)(const void*)(vsrc + (n >> 1) * 1024 +
+                                                                                   (n & 1) * 512);
+        const v2i vb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(const_cast<__attribute__((address_space(3))) v2i*>(a));
+        O[2 * n] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, e4m3x4_to_bf16((uint32_t)vb[0])), O[2 * n]);
+        O[2 * n + 1] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, e4m3x4_to_bf16((uint32_t)vb[1])), O[2 * n + 1]);
+      }
+    }
+    wait_vmcnt<kPer>();  // ids(it+2) have landed (copies(it+1) may fly)
+    __syncthreads();     // every wave is done with the slot and with ids(it-1)
+    copy_ids(it + 3);
+    copy_tile(it + 2, slot);
+  }
+  wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
+  if (active) mla_finish<8>(p, O, m, l, t, split, ht, g, c, 0);
 }
 
 // Merge of the split partials of one (row, head): all split LSEs are read in
@@ -661,7 +861,20 @@ dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
   }
   switch (p.fmt) {
     case DSA_LAT_BF16: DSA_MLA_LAUNCH(DSA_LAT_BF16) break;
-    case DSA_LAT_FP8: DSA_MLA_DMA_LAUNCH(DSA_LAT_FP8) break;
+    case DSA_LAT_FP8: {
+      if (!p.prefill) {
+        DSA_MLA_DMA_LAUNCH(DSA_LAT_FP8)
+        break;
+      }
+      const MlaShape s8 = mla_shape_fp8(p.ntiles);
+      const dim3 g8(p.nsplit, p.T, s8.groups), b8(64 * s8.nw);
+      switch (s8.nw) {
+        case 1: hipLaunchKernelGGL(mla_f8_kernel<1>, g8, b8, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL(mla_f8_kernel<2>, g8, b8, 0, stream, p); break;
+        default: hipLaunchKernelGGL(mla_f8_kernel<4>, g8, b8, 0, stream, p); break;
+      }
+      break;
+    }
     default: DSA_MLA_DMA_LAUNCH(DSA_LAT_NVFP4) break;
   }
 #undef DSA_MLA_LAUNCH

@@ -52,19 +52,10 @@ __device__ __forceinline__ int row_req(const TopkParams& p, int t) {
   return p.tok_req ? req_or_none(p.tok_req[t], p.R) : 0;
 }
 
-// Wave-wide scans and reductions on DPP lane moves (no LDS round trip): an
-// inclusive prefix sum by shifts within 16-lane rows and two row broadcasts
-// (lane 15 of each row into the next row for rows 1 and 3, then lane 31 into
-// rows 2 and 3); the totals are read from lane 63.
-__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
+// Wave-wide scans and reductions on DPP lane moves (no LDS round trip): the
+// inclusive prefix sum is radix.h's wave_incl_scan32; maxima take the same
+// shifts and row broadcasts; totals are read from lane 63.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) { return wave_incl_scan32(v); }
 __device__ __forceinline__ uint32_t wave_total(uint32_t incl) { return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63); }
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
