@@ -609,20 +609,23 @@ __global__ __launch_bounds__(64 * NW, VS) void mla_dma_kernel(MlaParams p) {
 //       points at) gives every lane rows 4g..4g+3 of two dims, d0 + c (bytes
 //       0-3) and d0 + 16 + c (bytes 4-7): the V operands of two MFMAs.
 // The per-row FP8 scale multiplies the logit and the softmax weight.
-constexpr int kF8Depth = 2;                    // ring slots: tile it+1 lands while tile it computes
 constexpr int kF8ScaleOff = 9 * 1024;
 constexpr int kF8Slot = kF8ScaleOff + 256;
-constexpr int kF8IdSlots = 4;                  // id ring: tiles it .. it+3
-constexpr int kF8Lds = kF8Depth * kF8Slot + kF8IdSlots * 256;
 constexpr int kF8Copies = 9 + 1;               // copies per tile: 9 segments, the row scales
-static_assert(kF8Lds <= 160 * 1024 / 8, "eight workgroups per CU");
+// DP ring slots (tiles it+1 .. it+DP-1 in flight while tile it computes) and
+// 2 DP id slots (ids run DP tiles ahead of the copies that need them)
+constexpr int mla_f8_lds(int dp) { return dp * kF8Slot + 2 * dp * 256; }
+static_assert(mla_f8_lds(2) <= 160 * 1024 / 8, "one-wave workgroups: eight per CU");
+static_assert(mla_f8_lds(4) <= 160 * 1024 / 4, "two-wave workgroups: four per CU");
 
-template <int NW>
+template <int NW, int DP>
 __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
   constexpr int kPer = (kF8Copies + NW - 1) / NW;  // copies per wave per tile (the last one repeated)
-  static_assert(2 + 2 * kPer < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kF8Lds];
-  uint8_t* idr = ring + kF8Depth * kF8Slot;  // [kF8IdSlots][64 ints]
+  constexpr int kIdSlots = 2 * DP;
+  constexpr int kBehind = (DP - 1) * (1 + kPer);   // this wave's ops issued after tile it's copies
+  static_assert(kBehind < 64 && DP * (1 + kPer) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[mla_f8_lds(DP)];
+  uint8_t* idr = ring + DP * kF8Slot;  // [kIdSlots][64 ints]
 
   const int split = blockIdx.x, t = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -639,21 +642,20 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
 
   // id copy of tile `tile` (every wave issues it: identical bytes)
   auto copy_ids = [&](int tile) {
-    dma4<false>(rlist + min(tile * kRT + c, n_ids - 1), idr_l + (tile % kF8IdSlots) * 256);
+    dma4<false>(rlist + min(tile * kRT + c, n_ids - 1), idr_l + (tile % kIdSlots) * 256);
   };
   // id of row r of a tile whose ids have landed (-1 past the split's end)
   auto id_at = [&](int tile, int r) -> int {
-    const int v = reinterpret_cast<const int*>(idr + (tile % kF8IdSlots) * 256)[r];
+    const int v = reinterpret_cast<const int*>(idr + (tile % kIdSlots) * 256)[r];
     return tile * kRT + r < n_ids ? v : -1;
   };
   auto row_of = [&](int id) -> const uint8_t* {
     return row_ok(id, p) ? p.lat + (int64_t)(id >> p.plog2) * p.page_bytes + (int64_t)(id & (P - 1)) * 640
                          : g_zero_row;
   };
-  // this wave's copies of tile `tile` into ring slot `slot`: kPer of them
-  // whatever the tile, so one vmcnt count is exact
-  auto copy_tile = [&](int tile, int slot) {
-    const uint8_t* row = row_of(id_at(tile, c));
+  // this wave's copies of a tile (source row `row`, this lane's) into ring
+  // slot `slot`: kPer of them whatever the tile, so one vmcnt count is exact
+  auto copy_tile = [&](const uint8_t* row, int slot) {
     const uint32_t base = ring_l + slot * kF8Slot;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -681,14 +683,18 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
   for (int x = 0; x < 32; ++x) O[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), l = 0.f;
 
-  // Prologue.  Issue order per wave from here on: ids(0) ids(1) | copies(0) |
-  // ids(2) copies(1) | then at the end of every tile it: ids(it+3) copies(it+2).
-  copy_ids(0);
-  copy_ids(1);
+  // Prologue: ids(0 .. DP-1), all landed; then [ids(d + DP), copies(d)] for
+  // d < DP; at the end of every tile it: [ids(it + 2 DP), copies(it + DP)].
+  // The ids a copy needs were issued just before the copies of DP tiles
+  // earlier, which have landed by then.
+#pragma unroll
+  for (int d = 0; d < DP; ++d) copy_ids(d);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the ids and (seen by the compiler) the query loads
-  copy_tile(0, 0);
-  copy_ids(2);
-  copy_tile(1, 1);
+#pragma unroll
+  for (int d = 0; d < DP; ++d) {
+    copy_ids(d + DP);
+    copy_tile(row_of(id_at(d, c)), d);
+  }
 
   // transposed-read source of this lane: byte slot j = (lane%16)/2 -> row
   // 4g + j%4 of dim chunk j/4 (+16 dims), half lane%2 of the 16 bytes
@@ -696,31 +702,38 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
   const int t_off = (tj >> 2) * 256 + (4 * g + (tj & 3)) * 16 + 8 * (lane & 1);
 
   for (int it = 0; it < ntile; ++it) {
-    const int slot = it % kF8Depth;
-    wait_vmcnt<1 + kPer>();  // this wave's copies of tile `it` (ids(it+2), copies(it+1) may fly)
-    __syncthreads();         // ... and every other wave's
+    const int slot = it % DP;
+    wait_vmcnt<kBehind>();  // this wave's copies of tile `it` (later ids and copies may fly)
+    __syncthreads();        // ... and every other wave's
     const uint8_t* sl = ring + slot * kF8Slot;
+    // the source row of this lane's next copies (tile it+DP), ahead of the
+    // products so that its id read and address are ready when they are issued
+    const uint8_t* next_row = row_of(id_at(it + DP, c));
     if (active) {
-      // ---- QK: two independent accumulator chains of nine
+      // the tile's row scales and ids, read before the products
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(sl + kF8ScaleOff + 16 * g);
+      bool ok[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ok[i] = row_ok(id_at(it, 4 * g + i), p);
+      // ---- QK: four independent accumulator chains
       f32x4 s;
       {
         const uint8_t* src = sl + lane * 16;
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int sp = 0; sp < 9; ++sp) {
           const i32x4 raw = *reinterpret_cast<const i32x4*>(src + sp * 1024);
-          s0 = mfma16x16x32(e4m3x8_to_bf16x8(raw[0], raw[1]), qf[2 * sp], s0);
-          s1 = mfma16x16x32(e4m3x8_to_bf16x8(raw[2], raw[3]), qf[2 * sp + 1], s1);
+          sa[(2 * sp) & 3] = mfma16x16x32(e4m3x8_to_bf16x8(raw[0], raw[1]), qf[2 * sp], sa[(2 * sp) & 3]);
+          sa[(2 * sp + 1) & 3] = mfma16x16x32(e4m3x8_to_bf16x8(raw[2], raw[3]), qf[2 * sp + 1], sa[(2 * sp + 1) & 3]);
         }
-        s = s0 + s1;
+        s = (sa[0] + sa[1]) + (sa[2] + sa[3]);
       }
       // ---- online softmax for head c over rows 4g+i
-      const f32x4 sc = *reinterpret_cast<const f32x4*>(sl + kF8ScaleOff + 16 * g);
       float lg[4];
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = row_ok(id_at(it, 4 * g + i), p) ? s[i] * p.sm_log2 * sc[i] : -__builtin_inff();
+        const float v = ok[i] ? s[i] * p.sm_log2 * sc[i] : -__builtin_inff();
         lg[i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -762,10 +775,9 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
         O[2 * n + 1] = mfma16x16x16(pa, __builtin_bit_cast(bf16x4, e4m3x4_to_bf16((uint32_t)vb[1])), O[2 * n + 1]);
       }
     }
-    wait_vmcnt<kPer>();  // ids(it+2) have landed (copies(it+1) may fly)
-    __syncthreads();     // every wave is done with the slot and with ids(it-1)
-    copy_ids(it + 3);
-    copy_tile(it + 2, slot);
+    __syncthreads();  // every wave is done with the slot and with the ids of tile it
+    copy_ids(it + 2 * DP);
+    copy_tile(next_row, slot);
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
   if (active) mla_finish<8>(p, O, m, l, t, split, ht, g, c, 0);
@@ -868,10 +880,12 @@ dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
       }
       const MlaShape s8 = mla_shape_fp8(p.ntiles);
       const dim3 g8(p.nsplit, p.T, s8.groups), b8(64 * s8.nw);
+      // ring depth: all the LDS a CU's eight waves leave (two slots per one-wave
+      // workgroup, four per two-wave one)
       switch (s8.nw) {
-        case 1: hipLaunchKernelGGL(mla_f8_kernel<1>, g8, b8, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL(mla_f8_kernel<2>, g8, b8, 0, stream, p); break;
-        default: hipLaunchKernelGGL(mla_f8_kernel<4>, g8, b8, 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((mla_f8_kernel<1, 2>), g8, b8, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((mla_f8_kernel<2, 4>), g8, b8, 0, stream, p); break;
+        default: hipLaunchKernelGGL((mla_f8_kernel<4, 4>), g8, b8, 0, stream, p); break;
       }
       break;
     }
