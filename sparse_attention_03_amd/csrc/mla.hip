@@ -609,6 +609,7 @@ __global__ __launch_bounds__(64 * NW, VS) void mla_dma_kernel(MlaParams p) {
 //       points at) gives every lane rows 4g..4g+3 of two dims, d0 + c (bytes
 //       0-3) and d0 + 16 + c (bytes 4-7): the V operands of two MFMAs.
 // The per-row FP8 scale multiplies the logit and the softmax weight.
+constexpr int kXcds = 8;  // MI355X: eight XCDs, each with its own L2
 constexpr int kF8ScaleOff = 9 * 1024;
 constexpr int kF8Slot = kF8ScaleOff + 256;
 constexpr int kF8Copies = 9 + 1;               // copies per tile: 9 segments, the row scales
@@ -627,10 +628,17 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[mla_f8_lds(DP)];
   uint8_t* idr = ring + DP * kF8Slot;  // [kIdSlots][64 ints]
 
-  const int split = blockIdx.x, t = blockIdx.y;
+  // XCD-aware order (one split per row): workgroups go to the eight XCDs
+  // round-robin by linear id, so the `groups` workgroups of a query row get
+  // ids 8 apart -- one XCD, dispatched back to back -- and the second and
+  // later ones find the row's latents in that XCD's L2.
+  const int groups = gridDim.x / ((p.T + kXcds - 1) / kXcds * kXcds);
+  const int lin = blockIdx.x, xcd = lin % kXcds, slot_x = lin / kXcds;
+  const int split = 0, t = (slot_x / groups) * kXcds + xcd, grp = slot_x % groups;
+  if (t >= p.T) return;  // padding of the last XCD round (the whole workgroup leaves)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ht = blockIdx.z * NW + wave;
+  const int ht = grp * NW + wave;
   const bool active = ht < p.ntiles;  // a wave past the last head tile only copies
   const int g = lane >> 4, c = lane & 15;
   const int j_begin = split * p.split_len;
@@ -879,7 +887,8 @@ dsa_status launch_mla(const MlaParams& p, hipStream_t stream) {
         break;
       }
       const MlaShape s8 = mla_shape_fp8(p.ntiles);
-      const dim3 g8(p.nsplit, p.T, s8.groups), b8(64 * s8.nw);
+      // one split per row (prefill): a 1-D grid in the XCD-aware order
+      const dim3 g8((p.T + kXcds - 1) / kXcds * kXcds * s8.groups), b8(64 * s8.nw);
       // ring depth: all the LDS a CU's eight waves leave (two slots per one-wave
       // workgroup, four per two-wave one)
       switch (s8.nw) {

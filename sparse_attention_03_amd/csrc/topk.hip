@@ -98,6 +98,30 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return wave_total(wave_scan_incl(v)); }
 
+// Cross-wave combinations of per-wave values (nw <= 64 waves, `wave` the
+// calling wave's index, uniform): lane w of every wave takes wave w's value,
+// and one wave-wide DPP scan or reduction combines them -- no serial loop
+// over the waves.  waves_before: sum of the values of waves < wave; total:
+// sum of all.
+__device__ __forceinline__ uint32_t waves_before(const uint32_t* per_wave, int nw, int wave, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t x = per_wave[lane < nw ? lane : 0];
+  const uint32_t incl = wave_scan_incl(lane < nw ? x : 0u);
+  total = (uint32_t)__builtin_amdgcn_readlane((int)incl, nw - 1);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)incl, wave > 0 ? wave - 1 : 0);
+  return wave > 0 ? b : 0u;
+}
+__device__ __forceinline__ uint32_t waves_max(const uint32_t* per_wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t x = per_wave[lane < nw ? lane : 0];
+  return wave_max(lane < nw ? x : 0u);
+}
+__device__ __forceinline__ uint32_t waves_min(const uint32_t* per_wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t x = per_wave[lane < nw ? lane : 0];
+  return wave_min(lane < nw ? x : 0xFFFFFFFFu);
+}
+
 // Sampling block of a row: B = kRun (every score) for short rows, else the
 // smallest power of two >= 256 with vis / B * kRun <= kMaxSamples.
 __device__ __forceinline__ int sample_block(int vis) {
@@ -114,7 +138,7 @@ __device__ __forceinline__ int sample_block(int vis) {
 __device__ __forceinline__ void rank_bin_1024(const uint32_t* h, uint32_t r, uint32_t* wtot, int* s_bin,
                                               uint32_t* s_need, int& bin, uint32_t& need,
                                               uint32_t* s_count = nullptr, uint32_t* count = nullptr) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t loc[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -127,7 +151,9 @@ __device__ __forceinline__ void rank_bin_1024(const uint32_t* h, uint32_t r, uin
   uint32_t suf = wt - pre_incl + sum;
   if (lane == 0) wtot[wave] = wt;
   __syncthreads();
-  for (int w = wave + 1; w < 16; ++w) suf += wtot[w];
+  uint32_t all;
+  const uint32_t before = waves_before(wtot, 16, wave, all);
+  suf += all - before - wt;  // the waves after this one
   const uint32_t above = suf - sum;
   if (above < r && suf >= r) {
     uint32_t acc = above;
@@ -191,12 +217,8 @@ __global__ __launch_bounds__(1024) void topk_threshold_kernel(TopkParams p) {
   }
   for (int i = tid; i < 4096; i += 1024) h[i] = 0;
   __syncthreads();
-  lo = s_lo[0];
-  hi = s_hi[0];
-  for (int w = 1; w < 16; ++w) {
-    lo = min(lo, s_lo[w]);
-    hi = max(hi, s_hi[w]);
-  }
+  lo = waves_min(s_lo, 16);
+  hi = waves_max(s_hi, 16);
   // number of samples (blocks < kMaxSamples / kRun; the last may be partial)
   // and the rank of the threshold among them
   const int64_t nblk = ((int64_t)vis + B - 1) / B;
@@ -261,24 +283,33 @@ __global__ __launch_bounds__(1024) void topk_threshold_kernel(TopkParams p) {
 __device__ __forceinline__ uint64_t wave_scan_incl_u64(uint64_t v) {
   return (uint64_t)wave_scan_incl((uint32_t)v) | ((uint64_t)wave_scan_incl((uint32_t)(v >> 32)) << 32);
 }
+// 64-bit words whose 32-bit halves never carry into each other (16-bit
+// fields): the halves are combined independently.
+__device__ __forceinline__ uint64_t waves_before_u64(const uint64_t* per_wave, int nw, int wave, uint64_t& total) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t y = per_wave[lane < nw ? lane : 0];
+  const uint64_t x = lane < nw ? y : 0ull;
+  const uint32_t il = wave_scan_incl((uint32_t)x), ih = wave_scan_incl((uint32_t)(x >> 32));
+  total = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)il, nw - 1) |
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ih, nw - 1) << 32);
+  const int src = wave > 0 ? wave - 1 : 0;
+  const uint64_t b = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)il, src) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ih, src) << 32);
+  return wave > 0 ? b : 0ull;
+}
 __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* wsum, uint64_t& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint64_t inc = wave_scan_incl_u64(v);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  uint64_t before = 0;
-  total = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) before += wsum[w];
-    total += wsum[w];
-  }
+  const uint64_t before = waves_before_u64(wsum, (int)(blockDim.x >> 6), wave, total);
   return before + inc - v;
 }
 
 // Four words at once, behind one barrier.  wsum: [16][4].
 __device__ __forceinline__ void block_excl_scan_u64x4(const uint64_t (&v)[4], uint64_t (&ex)[4], uint64_t (&tot)[4],
                                                       uint64_t (*wsum)[4]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint64_t inc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) inc[i] = wave_scan_incl_u64(v[i]);
@@ -286,18 +317,19 @@ __device__ __forceinline__ void block_excl_scan_u64x4(const uint64_t (&v)[4], ui
 #pragma unroll
     for (int i = 0; i < 4; ++i) wsum[wave][i] = inc[i];
   __syncthreads();
+  const int nw = (int)(blockDim.x >> 6);
+  const int ln = lane < nw ? lane : 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ex[i] = inc[i] - v[i];
-    tot[i] = 0;
+    const uint64_t x = lane < nw ? wsum[ln][i] : 0ull;
+    const uint32_t il = wave_scan_incl((uint32_t)x), ih = wave_scan_incl((uint32_t)(x >> 32));
+    tot[i] = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)il, nw - 1) |
+             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ih, nw - 1) << 32);
+    const int src = wave > 0 ? wave - 1 : 0;
+    const uint64_t b = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)il, src) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ih, src) << 32);
+    ex[i] = inc[i] - v[i] + (wave > 0 ? b : 0ull);
   }
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t x = wsum[w][i];
-      if (w < wave) ex[i] += x;
-      tot[i] += x;
-    }
 }
 
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
@@ -432,11 +464,11 @@ __device__ __forceinline__ void select_top(Each each, uint32_t K, SelectLds& sl,
     sl.red[1][wave] = mn;
   }
   __syncthreads();
-  mx = sl.red[0][0];
-  mn = sl.red[1][0];
-  for (int w = 1; w < 16; ++w) {
-    mx = sl.red[0][w] > mx ? sl.red[0][w] : mx;
-    mn = sl.red[1][w] < mn ? sl.red[1][w] : mn;
+  {
+    const int ln = lane < 16 ? lane : 0;
+    const uint64_t a = sl.red[0][ln], b = sl.red[1][ln];
+    mx = wave_max_u64(lane < 16 ? a : 0ull);
+    mn = ~wave_max_u64(lane < 16 ? ~b : 0ull);
   }
   const uint64_t dif = mx ^ mn;
   int hi_sh = dif ? 64 - __clzll((long long)dif) : 1;  // bits >= hi_sh: common prefix
@@ -595,11 +627,11 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
       cnt = info[2 * tid + 1];
     }
     const int inc = (int)wave_scan_incl(cnt);
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += (int)sl.wtot[w];
+    uint32_t all_unused;
+    const int before = (int)waves_before(sl.wtot, 16, wave, all_unused);
     if (tid < p.nslices) {
       sbase[tid] = sb;
       soff[tid] = (uint32_t)(before + inc) - cnt;
@@ -635,12 +667,12 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
       if (i < ncand && (composite(ck[i], ci[i]) >> hi_sh) >= prefix) m |= 1u << u;
     }
     const int inc = (int)wave_scan_incl((uint32_t)__popc(m));
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     __syncthreads();  // sl.wtot was read by select_top
     if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
     __syncthreads();
-    int pos = inc - __popc(m);
-    for (int w = 0; w < wave; ++w) pos += (int)sl.wtot[w];
+    uint32_t all_unused;
+    int pos = inc - __popc(m) + (int)waves_before(sl.wtot, 16, wave, all_unused);
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if (m >> u & 1u) ord[pos++] = (int)ci[kPer * tid + u];
@@ -694,17 +726,14 @@ struct RowLds {
 
 // Block exclusive scan of one int per thread (1024 threads); wsum: 16 ints.
 __device__ __forceinline__ int block_excl_scan_i32(int v, int* wsum, int& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int inc = (int)wave_scan_incl((uint32_t)v);
   __syncthreads();  // wsum may still be read by a previous scan
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  int before = 0;
-  total = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) before += wsum[w];
-    total += wsum[w];
-  }
+  uint32_t tot;
+  const int before = (int)waves_before(reinterpret_cast<const uint32_t*>(wsum), 16, wave, tot);
+  total = (int)tot;
   return before + inc - v;
 }
 
@@ -730,12 +759,8 @@ __device__ __forceinline__ void select32(Get get, int n, uint32_t K, RowLds& L, 
     L.s_hi[wave] = mx;
   }
   __syncthreads();
-  mn = L.s_lo[0];
-  mx = L.s_hi[0];
-  for (int w = 1; w < 16; ++w) {
-    mn = min(mn, L.s_lo[w]);
-    mx = max(mx, L.s_hi[w]);
-  }
+  mn = waves_min(L.s_lo, 16);
+  mx = waves_max(L.s_hi, 16);
   const uint32_t dif = mx ^ mn;
   int sh = dif ? 32 - __clz((int)dif) : 0;
   uint32_t pre = sh >= 32 ? 0u : (mx >> sh);
@@ -885,14 +910,11 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
       L.s_cnt[wave] = ns;
     }
     __syncthreads();
-    lo = L.s_lo[0];
-    hi = L.s_hi[0];
-    int S = L.s_cnt[0];
-    for (int w = 1; w < 16; ++w) {
-      lo = min(lo, L.s_lo[w]);
-      hi = max(hi, L.s_hi[w]);
-      S += L.s_cnt[w];
-    }
+    lo = waves_min(L.s_lo, 16);
+    hi = waves_max(L.s_hi, 16);
+    uint32_t S_all;
+    (void)waves_before(reinterpret_cast<const uint32_t*>(L.s_cnt), 16, 0, S_all);
+    const int S = (int)S_all;
     const float mu = (float)K * (float)S / (float)vis;
     const uint32_t rk = (uint32_t)min<int64_t>(S, (int64_t)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
     const uint32_t diff = lo ^ hi;
