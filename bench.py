@@ -471,6 +471,11 @@ def main():
         # matrix instruction (no dequantisation), everything else as above
         extra["fp4_decode_256k_mxfp4_q"] = synth.CONFIGS["fp4_decode_256k"].replace(
             name="fp4_decode_256k_mxfp4_q", q_fmt="mxfp4")
+        # the 64K speculative workload with FP8 index queries (the front end's
+        # FP8 output, head weight and scale folded): the multi-row indexer on
+        # the FP8 matrix instruction over raw keys
+        extra["tp8_spec_decode_64k_fp8_q"] = synth.CONFIGS["tp8_spec_decode_64k"].replace(
+            name="tp8_spec_decode_64k_fp8_q", q_fmt="fp8")
         for name, ospec in extra.items():
             if name == spec.name:
                 continue

@@ -331,6 +331,18 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     p.qrows = std::min(b.max_rows_per_req, dsa::kIndexerMaxRowsPerPass);
     p.max_rows_per_req = b.max_rows_per_req;
     st = dsa::launch_indexer_bf16(p, stream);
+  } else if (b.max_rows_per_req <= dsa::kIndexerQ8MaxRows) {
+    // FP8 q of few-row (decode) requests: the multi-row kernel on the FP8
+    // instruction, keys read raw; workgroups as for BF16 multi-row requests
+    p.q8 = static_cast<const uint8_t*>(a->q);
+    p.q_scale = static_cast<const float*>(a->q_scale);
+    int64_t target = (int64_t)b.max_vis * b.num_requests / 512;
+    int chunk = 256;
+    while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
+    p.chunk = chunk;
+    p.qrows = std::min(b.max_rows_per_req, dsa::kIndexerMaxRowsPerPass);
+    p.max_rows_per_req = b.max_rows_per_req;
+    st = dsa::launch_indexer_bf16(p, stream);
   } else {
     p.q8 = static_cast<const uint8_t*>(a->q);
     p.q_scale = static_cast<const float*>(a->q_scale);

@@ -34,6 +34,7 @@ constexpr int kIdxWaves = 4;
 constexpr int kIdxKT = 4;              // 16-key tiles per wave per round
 constexpr int kIdxRound = kIdxWaves * kIdxKT * 16;  // 256 keys per round
 constexpr int kQPad = 136;             // bf16 per head row in LDS (272 B: conflict-free reads)
+constexpr int kQ8Pad = 144;            // bytes per FP8 head row in LDS (conflict-free 16-byte reads)
 
 // Raw key bytes of one round (kIdxKT tiles of 16 keys) for one lane: the
 // codes of the lane's 32 dims of key c of each tile and their side data.
@@ -156,9 +157,19 @@ __device__ __forceinline__ float own_multiplier(const RawKeys<KFMT>& raw, int g)
   return own_ok ? (KFMT == DSA_KEY_FP8 ? raw.own_scale : 1.f) : -__builtin_inff();
 }
 
-template <int KFMT>
+// Q8: FP8 queries (codes + per-(row, head) scale, folded into the staged head
+// weight) against FP8 keys on the FP8 matrix instruction: one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads x 16 keys takes the raw key
+// bytes the lane loaded (key c, bytes 32g .. 32g+31) as its B operand, so the
+// keys are never converted.  (AMD section of the K3.1 page: the decode
+// indexer on the 16x16x128 FP8 instruction.)
+template <int KFMT, bool Q8>
 __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
-  extern __shared__ __attribute__((aligned(16))) __bf16 qs[];  // [rows][32][kQPad] bf16, then [rows][32] fp32 w
+  // [rows][32][row bytes] queries (bf16, kQPad elements; or FP8, kQ8Pad bytes), then [rows][32] fp32 w
+  extern __shared__ __attribute__((aligned(16))) uint8_t qsb[];
+  static_assert(!Q8 || KFMT == DSA_KEY_FP8, "FP8 queries run against FP8 keys");
+  constexpr int kRowB = Q8 ? kQ8Pad : kQPad * 2;  // LDS bytes per staged head
+  __bf16* qs = reinterpret_cast<__bf16*>(qsb);
   __shared__ int s_vmax[kIdxWaves];
   __shared__ int s_vis[kIdxMaxRows];
   __shared__ int pg_lds[kIdxMaxChunkPages];
@@ -168,13 +179,25 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int rs = p.req_row_start[r], re = p.req_row_start[r + 1];
-  float* ws = reinterpret_cast<float*>(qs + p.qrows * 32 * kQPad);
+  float* ws = reinterpret_cast<float*>(qsb + p.qrows * 32 * kRowB);
 
   // Rows of a pass are staged with every load issued before the first LDS
   // store (one memory round trip, not one per load); the first pass's loads
   // are issued before the visible-range and page-table reads they do not
   // depend on.
-  constexpr int kQLoads = kIdxMaxRows * 512 / 256;
+  // 16-byte pieces per row: 512 (bf16: 16 per head) or 256 (FP8: 8 per head)
+  constexpr int kPieceLog = Q8 ? 3 : 4;
+  constexpr int kRowPieces = 32 << kPieceLog;
+  constexpr int kQLoads = kIdxMaxRows * kRowPieces / 256;
+  auto q_src = [&](int t, int head, int part) -> const void* {
+    return Q8 ? (const void*)(p.q8 + ((int64_t)t * 32 + head) * 128 + part * 16)
+              : (const void*)(p.q + ((int64_t)t * 32 + head) * 128 + part * 8);
+  };
+  auto q_dst = [&](int row, int head, int part) -> i32x4* {
+    return reinterpret_cast<i32x4*>(qsb + (row * 32 + head) * kRowB + part * 16);
+  };
+  // staged head weight: w, times the FP8 query scale
+  auto w_of = [&](int64_t th) -> float { return Q8 ? p.w[th] * p.q_scale[th] : p.w[th]; };
   i32x4 qv[kQLoads];
   float wv = 0.f;
   int vv = 0;
@@ -182,18 +205,18 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
 #pragma unroll
     for (int u = 0; u < kQLoads; ++u) {
       const int i = tid + 256 * u;
-      const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
-      if (i < nr * 512) qv[u] = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
+      const int row = i >> (5 + kPieceLog), head = (i >> kPieceLog) & 31, part = i & ((1 << kPieceLog) - 1);
+      if (i < nr * kRowPieces) qv[u] = ld16(q_src(t0 + row, head, part));
     }
-    if (tid < nr * 32) wv = p.w[(int64_t)t0 * 32 + tid];
+    if (tid < nr * 32) wv = w_of((int64_t)t0 * 32 + tid);
     if (tid < nr) vv = clamp_vis(p.tok_vis[t0 + tid], p.max_vis);
   };
   auto store_rows = [&](int nr) {
 #pragma unroll
     for (int u = 0; u < kQLoads; ++u) {
       const int i = tid + 256 * u;
-      const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
-      if (i < nr * 512) *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = qv[u];
+      const int row = i >> (5 + kPieceLog), head = (i >> kPieceLog) & 31, part = i & ((1 << kPieceLog) - 1);
+      if (i < nr * kRowPieces) *q_dst(row, head, part) = qv[u];
     }
     if (tid < nr * 32) ws[tid] = wv;
     // visible counts of the pass's rows, read from LDS in the row loop: a
@@ -227,6 +250,7 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
     // round i is dequantised and multiplied.
     auto mfma_row = [&](int j, const bf16x8 (&bfr)[kIdxKT][4], f32x4 (&acc)[kIdxKT][2]) {
       const __bf16* qrow = &qs[(j * 32) * kQPad];
+      (void)qrow;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qrow[c * kQPad + kdim<KFMT, false>(kk, g)]);
@@ -265,17 +289,42 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
       if (s_own < kend && s_own < vis)
         p.scores[(int64_t)t * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
     };
-    auto do_round = [&](int base, RawKeys<KFMT>& raw, int next) {
-      bf16x8 bfr[kIdxKT][4];
+    // FP8 queries: row j's two head tiles against the raw FP8 keys
+    auto mfma_row_q8 = [&](int j, const i32x8 (&kb)[kIdxKT], f32x4 (&acc)[kIdxKT][2]) {
 #pragma unroll
-      for (int kt = 0; kt < kIdxKT; ++kt) dequant_tile<KFMT>(raw, kt, bfr[kt], raw.sc[kt], g);
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint8_t* qh = qsb + (j * 32 + 16 * hh + c) * kRowB + 32 * g;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(qh), hi = *reinterpret_cast<const i32x4*>(qh + 16);
+        const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int kt = 0; kt < kIdxKT; ++kt) acc[kt][hh] = mfma16x16x128_fp8(a, kb[kt], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    };
+    auto do_round = [&](int base, RawKeys<KFMT>& raw, int next) {
       const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
       const float own_mul = own_multiplier<KFMT>(raw, g);
-      if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
       f32x4 acc[kIdxKT][2];
-      for (int j = 0; j < nr; ++j) {
-        mfma_row(j, bfr, acc);
-        epi_row(j, acc, s_own, own_mul);
+      if constexpr (Q8) {
+        i32x8 kb[kIdxKT];
+#pragma unroll
+        for (int kt = 0; kt < kIdxKT; ++kt) {
+          const i32x4 x = raw.v[kt][0], y = raw.v[kt][KFMT == DSA_KEY_FP8 ? 1 : 0];
+          kb[kt] = i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        }
+        if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
+        for (int j = 0; j < nr; ++j) {
+          mfma_row_q8(j, kb, acc);
+          epi_row(j, acc, s_own, own_mul);
+        }
+      } else {
+        bf16x8 bfr[kIdxKT][4];
+#pragma unroll
+        for (int kt = 0; kt < kIdxKT; ++kt) dequant_tile<KFMT>(raw, kt, bfr[kt], raw.sc[kt], g);
+        if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
+        for (int j = 0; j < nr; ++j) {
+          mfma_row(j, bfr, acc);
+          epi_row(j, acc, s_own, own_mul);
+        }
       }
     };
 
@@ -296,17 +345,17 @@ __global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = tid + 256 * (u0 + u);
-        const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
-        if (i < nr2 * 512) b4[u] = ld16(p.q + ((int64_t)(t0 + row) * 32 + head) * 128 + part * 8);
+        const int row = i >> (5 + kPieceLog), head = (i >> kPieceLog) & 31, part = i & ((1 << kPieceLog) - 1);
+        if (i < nr2 * kRowPieces) b4[u] = ld16(q_src(t0 + row, head, part));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = tid + 256 * (u0 + u);
-        const int row = i >> 9, head = (i >> 4) & 31, part = i & 15;
-        if (i < nr2 * 512) *reinterpret_cast<i32x4*>(&qs[(row * 32 + head) * kQPad + part * 8]) = b4[u];
+        const int row = i >> (5 + kPieceLog), head = (i >> kPieceLog) & 31, part = i & ((1 << kPieceLog) - 1);
+        if (i < nr2 * kRowPieces) *q_dst(row, head, part) = b4[u];
       }
     }
-    if (tid < nr2 * 32) ws[tid] = p.w[(int64_t)t0 * 32 + tid];
+    if (tid < nr2 * 32) ws[tid] = w_of((int64_t)t0 * 32 + tid);
     if (tid < nr2) s_vis[tid] = clamp_vis(p.tok_vis[t0 + tid], p.max_vis);
   }
 }
@@ -611,6 +660,10 @@ dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
     // row of a request in turn
     hipLaunchKernelGGL((indexer_row_kernel<DSA_KEY_MXFP4, true>), grid, dim3(256), KeyStream<DSA_KEY_MXFP4>::kLds,
                        stream, p);
+  } else if (p.q8) {
+    // FP8 queries of few-row requests (decode): FP8 keys only (checked by the caller)
+    const size_t lds8 = (size_t)p.qrows * 32 * (kQ8Pad + sizeof(float));
+    hipLaunchKernelGGL((indexer_bf16_kernel<DSA_KEY_FP8, true>), grid, dim3(256), lds8, stream, p);
   } else if (p.max_rows_per_req == 1) {
     if (p.key_fmt == DSA_KEY_FP8) {
       // above the default 64 KiB of dynamic LDS (idempotent, host-side)
@@ -628,11 +681,11 @@ dsa_status launch_indexer_bf16(const IndexerParams& p, hipStream_t stream) {
                          stream, p);
     }
   } else if (p.key_fmt == DSA_KEY_FP8) {
-    hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_FP8>, grid, dim3(256), lds, stream, p);
+    hipLaunchKernelGGL((indexer_bf16_kernel<DSA_KEY_FP8, false>), grid, dim3(256), lds, stream, p);
   } else if (p.key_fmt == DSA_KEY_MXFP4) {
-    hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_MXFP4>, grid, dim3(256), lds, stream, p);
+    hipLaunchKernelGGL((indexer_bf16_kernel<DSA_KEY_MXFP4, false>), grid, dim3(256), lds, stream, p);
   } else {
-    hipLaunchKernelGGL(indexer_bf16_kernel<DSA_KEY_NVFP4>, grid, dim3(256), lds, stream, p);
+    hipLaunchKernelGGL((indexer_bf16_kernel<DSA_KEY_NVFP4, false>), grid, dim3(256), lds, stream, p);
   }
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

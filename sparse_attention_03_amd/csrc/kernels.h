@@ -10,6 +10,10 @@ namespace dsa {
 
 // Query rows of a request the BF16 indexer stages in LDS per pass.
 constexpr int kIndexerMaxRowsPerPass = 6;
+// FP8 queries of requests with at most this many rows run on the multi-row
+// decode kernel (FP8 instruction, raw keys); more rows per request on the
+// prefill kernel
+constexpr int kIndexerQ8MaxRows = 8;
 // Keys per workgroup of the single-row BF16 indexer (its LDS holds the
 // chunk's scores): FP8 keys, MXFP4 / NVFP4 keys.
 constexpr int kIndexerRowChunkFp8 = 2048;

@@ -42,6 +42,9 @@ ABSENT = {
     # FP8 query rows (the prefill indexer), causal rows
     "fp8q": synth.Spec("fp8q", R=2, q_per_req=40, N=3000, key_fmt="fp8", lat_fmt="fp8", q_fmt="fp8", H=8,
                        k=512, seed=67),
+    # FP8 query rows of speculative requests (the multi-row FP8 kernel)
+    "fp8q_spec": synth.Spec("fp8q_spec", R=4, q_per_req=4, N=5000, key_fmt="fp8", lat_fmt="fp8", q_fmt="fp8",
+                            H=12, k=512, seed=71),
 }
 
 
@@ -94,7 +97,7 @@ def test_absent_pages_through_the_layer(name, gpu):
     # 25 damaged (request, page) entries out of 4 x 79, and request 1 with
     # every page absent when there are more than two requests
     wl = _damaged(spec, gpu, 25, all_absent_req=1 if spec.R > 2 else None)
-    prefill = spec.q_fmt == "fp8"
+    prefill = spec.q_per_req > 8
     step = gpu_step(wl, prefill=prefill)
     out, lse = step()
     torch.cuda.synchronize()

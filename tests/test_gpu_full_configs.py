@@ -31,12 +31,16 @@ SAMPLES = {
     "fp4_decode_256k_nvfp4_keys": [0, 33, 63],
     # the FP4 workload with MXFP4 index queries on the FP4 matrix instruction
     "fp4_decode_256k_mxfp4_q": [1, 30, 62],
+    # the 64K speculative workload with FP8 index queries (multi-row FP8 kernel)
+    "tp8_spec_decode_64k_fp8_q": [0, 5, 96, 191],
 }
 SPECS = dict(synth.CONFIGS)
 SPECS["fp4_decode_256k_nvfp4_keys"] = synth.CONFIGS["fp4_decode_256k"].replace(
     name="fp4_decode_256k_nvfp4_keys", key_fmt="nvfp4", seed=1006)
 SPECS["fp4_decode_256k_mxfp4_q"] = synth.CONFIGS["fp4_decode_256k"].replace(
     name="fp4_decode_256k_mxfp4_q", q_fmt="mxfp4", seed=1007)
+SPECS["tp8_spec_decode_64k_fp8_q"] = synth.CONFIGS["tp8_spec_decode_64k"].replace(
+    name="tp8_spec_decode_64k_fp8_q", q_fmt="fp8", seed=1008)
 
 
 @pytest.mark.parametrize("name", list(SAMPLES))

@@ -97,6 +97,10 @@ CASES = {
     "fp4_native_row": synth.CONFIGS["fp4_decode_256k"].replace(R=3, N=9000, q_fmt="mxfp4", seed=12),
     "fp4_native_spec": synth.CONFIGS["fp4_decode_256k"].replace(R=3, q_per_req=3, N=7001, q_fmt="mxfp4",
                                                                  seed=13),
+    # FP8 index queries on the FP8 instruction over raw keys: speculative rows
+    # and one row per request (the multi-row decode kernel)
+    "fp8q_spec": synth.CONFIGS["tp8_spec_decode_64k"].replace(R=3, N=12345, q_fmt="fp8", seed=14),
+    "fp8q_row": synth.CONFIGS["tp8_spec_decode_64k"].replace(R=4, q_per_req=1, N=9000, q_fmt="fp8", seed=15),
     # 96 heads (two head groups), planted gap
     "h96_gap": synth.CONFIGS["long_decode_1m"].replace(R=2, N=20000, seed=7),
 }
@@ -127,7 +131,7 @@ def test_layer_end_to_end(name, gpu):
 
 
 @pytest.mark.parametrize("name", ["tiny_8k_bf16", "spec_fp8_paged", "fp4_paged", "nvfp4_keys_row",
-                                  "nvfp4_keys_spec", "fp4_native_row", "fp4_native_spec"])
+                                  "nvfp4_keys_spec", "fp4_native_row", "fp4_native_spec", "fp8q_spec"])
 def test_layer_end_to_end_planted(name, gpu):
     spec = CASES[name].replace(plant_gap=True, seed=CASES[name].seed + 100)
     print(f"[gpu] planted case {name}", flush=True)
