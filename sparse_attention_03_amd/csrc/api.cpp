@@ -336,7 +336,7 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     // instruction, keys read raw; workgroups as for BF16 multi-row requests
     p.q8 = static_cast<const uint8_t*>(a->q);
     p.q_scale = static_cast<const float*>(a->q_scale);
-    int64_t target = (int64_t)b.max_vis * b.num_requests / 512;
+    int64_t target = (int64_t)b.max_vis * b.num_requests / 768;  // three workgroups per CU (the kernel fits three waves per SIMD)
     int chunk = 256;
     while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
     p.chunk = chunk;

@@ -164,7 +164,7 @@ __device__ __forceinline__ float own_multiplier(const RawKeys<KFMT>& raw, int g)
 // keys are never converted.  (AMD section of the K3.1 page: the decode
 // indexer on the 16x16x128 FP8 instruction.)
 template <int KFMT, bool Q8>
-__global__ __launch_bounds__(256) void indexer_bf16_kernel(IndexerParams p) {
+__global__ __launch_bounds__(256, Q8 ? 3 : 1) void indexer_bf16_kernel(IndexerParams p) {
   // [rows][32][row bytes] queries (bf16, kQPad elements; or FP8, kQ8Pad bytes), then [rows][32] fp32 w
   extern __shared__ __attribute__((aligned(16))) uint8_t qsb[];
   static_assert(!Q8 || KFMT == DSA_KEY_FP8, "FP8 queries run against FP8 keys");

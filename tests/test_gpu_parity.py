@@ -101,6 +101,8 @@ CASES = {
     # and one row per request (the multi-row decode kernel)
     "fp8q_spec": synth.CONFIGS["tp8_spec_decode_64k"].replace(R=3, N=12345, q_fmt="fp8", seed=14),
     "fp8q_row": synth.CONFIGS["tp8_spec_decode_64k"].replace(R=4, q_per_req=1, N=9000, q_fmt="fp8", seed=15),
+    # eight rows per request: two row passes (6 + 2) of the multi-row FP8 kernel
+    "fp8q_8rows": synth.CONFIGS["tp8_spec_decode_64k"].replace(R=2, q_per_req=8, N=7000, q_fmt="fp8", seed=16),
     # 96 heads (two head groups), planted gap
     "h96_gap": synth.CONFIGS["long_decode_1m"].replace(R=2, N=20000, seed=7),
 }
