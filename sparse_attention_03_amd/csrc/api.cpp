@@ -133,6 +133,17 @@ struct MlaPlan {
   int Hpad, ntiles, nsplit, split_len;
   size_t off_po, off_pl, total;
 };
+// Keys per workgroup of the multi-row indexer (a request's rows are staged
+// once per workgroup): the chunk, a multiple of the 256-key round and at most
+// 4096 keys (the staged page ids), that cuts the requests into about one wave
+// of workgroups -- per_cu per CU on 256 CUs, the kernel's occupancy -- so no
+// second, partial wave of workgroups runs behind the first.
+int multi_row_chunk(int max_vis, int num_requests, int per_cu) {
+  const int per_req = std::max(1, (per_cu * 256 + num_requests - 1) / num_requests);
+  const int chunk = ((max_vis + per_req - 1) / per_req + 255) / 256 * 256;
+  return std::min(std::max(chunk, 256), 4096);
+}
+
 MlaPlan plan_mla(const dsa_mla_args& a, bool prefill, int max_splits = 64) {
   MlaPlan pl;
   pl.Hpad = (a.num_heads + 15) / 16 * 16;
@@ -318,16 +329,17 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     st = dsa::launch_indexer_bf16(p, stream);
   } else if (a->q_fmt == DSA_Q_BF16) {
     p.q = static_cast<const __bf16*>(a->q);
-    // keys per workgroup, at most 4096.  Single-row requests stream keys and
-    // want many workgroups in flight (about 2048); multi-row requests stage
-    // their rows once per workgroup, so fewer, longer workgroups (about 512,
-    // two per CU) amortise that.
-    int64_t target = (int64_t)b.max_vis * b.num_requests / (b.max_rows_per_req == 1 ? 2048 : 512);
-    const int cap = b.max_rows_per_req > 1 ? 4096
-                    : a->keys.fmt == DSA_KEY_FP8 ? dsa::kIndexerRowChunkFp8 : dsa::kIndexerRowChunkFp4;
-    int chunk = 256;
-    while (chunk < cap && chunk * 2 <= target) chunk *= 2;
-    p.chunk = chunk;
+    if (b.max_rows_per_req == 1) {
+      // keys per workgroup: single-row requests stream keys and want many
+      // workgroups in flight (about 2048)
+      const int64_t target = (int64_t)b.max_vis * b.num_requests / 2048;
+      const int cap = a->keys.fmt == DSA_KEY_FP8 ? dsa::kIndexerRowChunkFp8 : dsa::kIndexerRowChunkFp4;
+      int chunk = 256;
+      while (chunk < cap && chunk * 2 <= target) chunk *= 2;
+      p.chunk = chunk;
+    } else {
+      p.chunk = multi_row_chunk(b.max_vis, b.num_requests, 2);  // two waves per SIMD (the kernel's registers)
+    }
     p.qrows = std::min(b.max_rows_per_req, dsa::kIndexerMaxRowsPerPass);
     p.max_rows_per_req = b.max_rows_per_req;
     st = dsa::launch_indexer_bf16(p, stream);
@@ -336,10 +348,7 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
     // instruction, keys read raw; workgroups as for BF16 multi-row requests
     p.q8 = static_cast<const uint8_t*>(a->q);
     p.q_scale = static_cast<const float*>(a->q_scale);
-    int64_t target = (int64_t)b.max_vis * b.num_requests / 768;  // three workgroups per CU (the kernel fits three waves per SIMD)
-    int chunk = 256;
-    while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
-    p.chunk = chunk;
+    p.chunk = multi_row_chunk(b.max_vis, b.num_requests, 3);  // three waves per SIMD
     p.qrows = std::min(b.max_rows_per_req, dsa::kIndexerMaxRowsPerPass);
     p.max_rows_per_req = b.max_rows_per_req;
     st = dsa::launch_indexer_bf16(p, stream);

@@ -230,16 +230,18 @@ __device__ __forceinline__ float xor32(float x, int g) {
 
 // Reduce-scatter over the four 16-lane rows: lane (g, c) holds v[0..3]; on
 // return it holds sum over g' of v_{g'}[g] (its own row's share of the sum).
-__device__ __forceinline__ float rows_reduce_scatter4(const float (&v)[4], int g) {
-  const bool odd = g & 1, upper = g >> 1;
-  // x = v[0], y = v[1]: odd rows of x receive the even rows' v[1], even rows
-  // of y receive the odd rows' v[0]; each row then sums the tile of its parity
+// After a swap every lane holds the two addends of its own share: a row swap
+// of (v0, v1) leaves an even row with (its v0, its odd neighbour's v0) and an
+// odd row with (its even neighbour's v1, its v1); the half swap of the pair
+// sums does the same across the two 32-lane halves.  So each level is one
+// swap and one add, with no select and no copy of the swapped operands.
+__device__ __forceinline__ float rows_reduce_scatter4(const float (&v)[4]) {
   const f32pair a = swap_rows16(v[0], v[1]);
-  const float s01 = odd ? v[1] + a.x : v[0] + a.y;
+  const float s01 = a.x + a.y;  // even rows: v[0] of the row pair, odd rows: v[1]
   const f32pair b = swap_rows16(v[2], v[3]);
-  const float s23 = odd ? v[3] + b.x : v[2] + b.y;
+  const float s23 = b.x + b.y;
   const f32pair h = swap_halves32(s01, s23);
-  return upper ? s23 + h.x : s01 + h.y;
+  return h.x + h.y;             // rows 0, 1: s01 of both halves; rows 2, 3: s23
 }
 
 __device__ __forceinline__ float wave_sum_xor_16_32(float v) {

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
           }
           v[kt] = x;
         }
-        const float tot = rows_reduce_scatter4(v, g);
+        const float tot = rows_reduce_scatter4(v);
         if (s < vis[j] && s < ke)
           p.scores[(int64_t)(row0 + 4 * wave + j) * p.ld + s] = (ksv == -__builtin_inff()) ? ksv : tot * ksv;
       }
