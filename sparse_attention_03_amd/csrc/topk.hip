@@ -122,6 +122,16 @@ __device__ __forceinline__ uint32_t waves_min(const uint32_t* per_wave, int nw) 
   return wave_min(lane < nw ? x : 0xFFFFFFFFu);
 }
 
+// The score threshold of an order-key threshold tau: for every score x
+// (finite or -inf), order_key(x) >= tau exactly when x >= key_threshold(tau)
+// (the key map is monotone in the score, -0 and +0 alike, and the inverse of
+// a key is a float bit pattern); tau at or below the key of -inf admits every
+// score.  NaN (a position past a row's end) passes no such test.
+__device__ __forceinline__ float key_threshold(uint32_t tau) {
+  return tau <= order_key(-__builtin_inff()) ? -__builtin_inff()
+                                              : __uint_as_float((tau & 0x80000000u) ? (tau & 0x7FFFFFFFu) : ~tau);
+}
+
 // Sampling block of a row: B = kRun (every score) for short rows, else the
 // smallest power of two >= 256 with vis / B * kRun <= kMaxSamples.
 __device__ __forceinline__ int sample_block(int vis) {
@@ -351,16 +361,19 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
   }
   const int s_end = min(s_begin + p.slice, vis);
   const float* row = p.scores + (int64_t)t * p.ld;
-  // the whole slice (8 float4 per thread) is loaded before any is compared
+  // The whole slice (8 float4 per thread) is loaded before any is compared:
+  // every float4 read is issued unconditionally, a start past the row's ld
+  // columns (ld and s_begin are multiples of 4) clamped to the last float4,
+  // and positions at or past the slice end are masked afterwards (a read
+  // under a branch made each wait for the one before).
+  const int last4 = (int)min<int64_t>(p.ld - 4, INT32_MAX - 3);
   f32x4 v[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int s = s_begin + 4 * tid + 1024 * b;
-    v[b] = (s + 3 < s_end) ? *reinterpret_cast<const f32x4*>(row + s) : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (s + 3 >= s_end)
-      for (int e = 0; e < 4; ++e) v[b][e] = (s + e < s_end) ? row[s + e] : 0.f;
+    v[b] = *reinterpret_cast<const f32x4*>(row + min(s, last4));
   }
-  const uint32_t tau = ctr[2];
+  const float tf = key_threshold(ctr[2]);
   uint32_t hit[8];  // bit e of hit[b]: score 4*tid + 1024*b + e is a candidate
   uint64_t pk[2] = {0, 0};
 #pragma unroll
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int s = s_begin + 4 * tid + 1024 * b + e;
-      if (s < s_end && order_key(v[b][e]) >= tau) m |= 1u << e;
+      if (s < s_end && v[b][e] >= tf) m |= 1u << e;
     }
     hit[b] = m;
     pk[b >> 2] |= (uint64_t)__popc(m) << (16 * (b & 3));
@@ -955,12 +968,8 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
   // ---- candidates (keys >= tau) into LDS in index order: stripe i's count
   // in 16-bit field i & 3 of word i >> 2 (a stripe holds at most 4096 keys,
   // so fields never carry), one block exclusive scan per word.  key >= tau is
-  // tested as score >= tf, tf the float whose key is tau (order keys are
-  // monotone in the score, -0 and +0 alike); tau at or below the key of -inf
-  // admits every score.
-  const float tf = tau <= order_key(-__builtin_inff())
-                       ? -__builtin_inff()
-                       : __uint_as_float((tau & 0x80000000u) ? (tau & 0x7FFFFFFFu) : ~tau);
+  // tested on the score itself.
+  const float tf = key_threshold(tau);
   auto field = [](const uint64_t (&w)[4], int i) { return (uint32_t)((w[i >> 2] >> (16 * (i & 3))) & 0xFFFFu); };
   {
     uint64_t pc[4] = {0, 0, 0, 0}, exc[4], totc[4];
