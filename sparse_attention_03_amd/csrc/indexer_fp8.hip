@@ -34,6 +34,8 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
   __shared__ float wl[kF8BM * 32];  // w * q_scale per row and head
   __shared__ int s_vmax[4];
   __shared__ int pg_lds[16384 / 16 + 1];  // page ids of this workgroup's key segment
+  // each lane's scores of the tile before (slot 4 q4 + j), written one tile late
+  __shared__ float s_out[4][8][64];
 
   const int r = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -60,8 +62,8 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
   if (kb >= vmax) return;
   const int ke = min(kb + p.chunk, vmax);
   const int lp0 = kb >> p.plog2;
-  for (int i = tid; i <= ((ke - 1) >> p.plog2) - lp0; i += 256)
-    pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
+  const int last = ((ke - 1) >> p.plog2) - lp0;  // last staged page entry
+  for (int i = tid; i <= last; i += 256) pg_lds[i] = phys_page(p.block_table, p.bt_stride, r, lp0 + i, p.num_pages);
   __syncthreads();
 
   // A fragments: rows 4*wave + j, head halves hh, lane (g, c): head 16hh + c,
@@ -91,30 +93,48 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
     wv[j][1] = *reinterpret_cast<const f32x4*>(&wl[(4 * wave + j) * 32 + 16 + 4 * g]);
   }
 
-  // key tile loader: 128 keys x 128 B = 1024 chunks of 16 B, 4 per thread
+  // key tile loader: 128 keys x 128 B = 1024 chunks of 16 B, 4 per thread.
+  // Every read is issued unconditionally (a read under a branch waited for the
+  // one before): a key past the segment or on an absent page reads the
+  // clamped / page-0 address; its scale becomes -inf on an absent page (the
+  // score is replaced by -inf) and a key past the segment is never stored.
   i32x4 kraw[4];
-  float sraw = 0.f;
+  float sraw = 0.f;  // scale of key k0 + (tid & 127) as read
+  bool sok = false;  // ... on a present page (else the key's scale is -inf)
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = tid + 256 * i;
       const int key = ch >> 3, part = ch & 7;
       const int s = k0 + key;
-      kraw[i] = i32x4{0, 0, 0, 0};
-      if (s < ke) {
-        const int pg = pg_lds[(s >> p.plog2) - lp0];
-        if (pg >= 0) kraw[i] = ld16(p.keys + (int64_t)pg * p.page_bytes + (s & (P - 1)) * 128 + part * 16);
-      }
+      const int pg = pg_lds[min((s >> p.plog2) - lp0, last)];
+      kraw[i] = ld16(p.keys + (int64_t)max(pg, 0) * p.page_bytes + (s & (P - 1)) * 128 + part * 16);
     }
-    if (tid < kF8BN) {
-      const int s = k0 + tid;
-      sraw = 0.f;
-      if (s < ke) {
-        const int pg = pg_lds[(s >> p.plog2) - lp0];
-        sraw = pg >= 0 ? *reinterpret_cast<const float*>(p.keys + (int64_t)pg * p.page_bytes + P * 128 + (s & (P - 1)) * 4)
-                       : -__builtin_inff();
-      }
+    {
+      // every thread reads a scale (threads 128 .. 255 repeat 0 .. 127); the
+      // absent-page select waits until the scale is staged, so nothing here
+      // waits for the read
+      const int s = k0 + (tid & (kF8BN - 1));
+      const int pg = pg_lds[min((s >> p.plog2) - lp0, last)];
+      sraw = *reinterpret_cast<const float*>(p.keys + (int64_t)max(pg, 0) * p.page_bytes + P * 128 + (s & (P - 1)) * 4);
+      sok = pg >= 0;
     }
+  };
+
+  // Scores are written one tile late, just before the next tile's reads are
+  // issued: the vector-memory counter also counts stores, in issue order, so
+  // a store issued after a read would make the wait for that read wait for
+  // the store too.
+  float(&outw)[8][64] = s_out[wave];
+  uint32_t pend = 0;  // bit 4 q4 + j: this lane's score in outw slot 4 q4 + j is to be written
+  int prev_k0 = 0;
+  auto flush = [&]() {
+#pragma unroll
+    for (int q4 = 0; q4 < kF8BN / 64; ++q4)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (pend >> (4 * q4 + j) & 1u)
+          p.scores[(int64_t)(row0 + 4 * wave + j) * p.ld + prev_k0 + q4 * 64 + lane] = outw[4 * q4 + j][lane];
   };
 
   load_tile(kb);
@@ -125,9 +145,15 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
       const int ch = tid + 256 * i;
       *reinterpret_cast<i32x4*>(&kl[(ch >> 3) * kF8KPad + (ch & 7) * 16]) = kraw[i];
     }
-    if (tid < kF8BN) kscale[tid] = sraw;
+    if (tid < kF8BN) kscale[tid] = sok ? sraw : -__builtin_inff();
     __syncthreads();
-    if (k0 + kF8BN < ke) load_tile(k0 + kF8BN);
+    flush();
+    pend = 0;
+    prev_k0 = k0;
+    // issued after the last tile too (reads stay in the staged pages; never
+    // used): a conditional read would make the compiler merge the paths with
+    // a wait for every store before it
+    load_tile(k0 + kF8BN);
 
 #pragma unroll
     for (int q4 = 0; q4 < kF8BN / 64; ++q4) {
@@ -163,11 +189,12 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
           v[kt] = x;
         }
         const float tot = rows_reduce_scatter4(v);
-        if (s < vis[j] && s < ke)
-          p.scores[(int64_t)(row0 + 4 * wave + j) * p.ld + s] = (ksv == -__builtin_inff()) ? ksv : tot * ksv;
+        outw[4 * q4 + j][lane] = (ksv == -__builtin_inff()) ? ksv : tot * ksv;
+        if (s < vis[j] && s < ke) pend |= 1u << (4 * q4 + j);
       }
     }
   }
+  flush();
 }
 
 dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream) {
