@@ -134,14 +134,24 @@ struct MlaPlan {
   size_t off_po, off_pl, total;
 };
 // Keys per workgroup of the multi-row indexer (a request's rows are staged
-// once per workgroup): the chunk, a multiple of the 256-key round and at most
-// 4096 keys (the staged page ids), that cuts the requests into about one wave
-// of workgroups -- per_cu per CU on 256 CUs, the kernel's occupancy -- so no
-// second, partial wave of workgroups runs behind the first.
+// once per workgroup): the multiple of the 256-key round, at most 4096 keys
+// (the staged page ids), that finishes first when the requests' chunks run in
+// waves of per_cu workgroups per CU on 256 CUs -- waves x (chunk + 256), the
+// 256 standing for a workgroup's start-up -- so a chunk that leaves a few
+// workgroups for a second, partial wave is not taken.
 int multi_row_chunk(int max_vis, int num_requests, int per_cu) {
-  const int per_req = std::max(1, (per_cu * 256 + num_requests - 1) / num_requests);
-  const int chunk = ((max_vis + per_req - 1) / per_req + 255) / 256 * 256;
-  return std::min(std::max(chunk, 256), 4096);
+  const int64_t slots = (int64_t)per_cu * 256;
+  int best = 4096;
+  int64_t best_cost = INT64_MAX;
+  for (int chunk = 256; chunk <= 4096; chunk += 256) {
+    const int64_t n = (int64_t)num_requests * ((max_vis + chunk - 1) / chunk);
+    const int64_t cost = (n + slots - 1) / slots * (chunk + 256);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = chunk;
+    }
+  }
+  return best;
 }
 
 MlaPlan plan_mla(const dsa_mla_args& a, bool prefill, int max_splits = 64) {
@@ -338,7 +348,12 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, hipStream_t stream) {
       while (chunk < cap && chunk * 2 <= target) chunk *= 2;
       p.chunk = chunk;
     } else {
-      p.chunk = multi_row_chunk(b.max_vis, b.num_requests, 2);  // two waves per SIMD (the kernel's registers)
+      // multi-row requests stage their rows once per workgroup, so fewer,
+      // longer workgroups (about 512, two per CU) amortise that
+      const int64_t target = (int64_t)b.max_vis * b.num_requests / 512;
+      int chunk = 256;
+      while (chunk < 4096 && chunk * 2 <= target) chunk *= 2;
+      p.chunk = chunk;
     }
     p.qrows = std::min(b.max_rows_per_req, dsa::kIndexerMaxRowsPerPass);
     p.max_rows_per_req = b.max_rows_per_req;

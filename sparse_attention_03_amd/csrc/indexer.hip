@@ -173,10 +173,6 @@ __global__ __launch_bounds__(256, Q8 ? 3 : 1) void indexer_bf16_kernel(IndexerPa
   __shared__ int s_vmax[kIdxWaves];
   __shared__ int s_vis[kIdxMaxRows];
   __shared__ int pg_lds[kIdxMaxChunkPages];
-  // BF16 queries: each lane's scores of the round before, one per row
-  // (written one round late: see the round loop)
-  constexpr int kOutRows = Q8 ? 1 : kIdxMaxRows;
-  __shared__ float s_out[kIdxWaves][kOutRows][64];
 
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
@@ -271,19 +267,6 @@ __global__ __launch_bounds__(256, Q8 ? 3 : 1) void indexer_bf16_kernel(IndexerPa
         }
       }
     };
-    // BF16 queries: scores are written one round late, just before the next
-    // round's loads are issued.  The vector-memory counter also counts stores,
-    // in issue order, so a store issued after a load would make the wait for
-    // that load (at the round's end) wait for the store too: 64K batch 105.6
-    // -> 104 us.  (The FP8-query variant, at three waves per SIMD, measured
-    // 90 -> 93 us with it and stores directly.)
-    float(&outw)[kOutRows][64] = s_out[wave];
-    uint32_t pend = 0;  // bit j: this lane's score of row j in outw is to be written
-    int s_prev = 0;     // key of those scores
-    auto flush = [&]() {
-      for (int j = 0; j < nr; ++j)
-        if (pend >> j & 1u) p.scores[(int64_t)(t0 + j) * p.ld + s_prev] = outw[j][lane];
-    };
     // ReLU-weighted head sum: 8 heads in-lane, then a reduce-scatter over the
     // four lane groups leaves lane (g, c) with key c of tile g
     auto epi_row = [&](int j, const f32x4 (&acc)[kIdxKT][2], int s_own, float own_mul) {
@@ -302,13 +285,8 @@ __global__ __launch_bounds__(256, Q8 ? 3 : 1) void indexer_bf16_kernel(IndexerPa
         v[kt] = x;
       }
       const float tot = rows_reduce_scatter4(v);
-      const float val = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
-      if constexpr (Q8) {
-        if (s_own < kend && s_own < vis) p.scores[(int64_t)(t0 + j) * p.ld + s_own] = val;
-      } else {
-        outw[j][lane] = val;
-        if (s_own < kend && s_own < vis) pend |= 1u << j;
-      }
+      if (s_own < kend && s_own < vis)
+        p.scores[(int64_t)(t0 + j) * p.ld + s_own] = (own_mul == -__builtin_inff()) ? own_mul : tot * own_mul;
     };
     // FP8 queries: row j's two head tiles against the raw FP8 keys
     auto mfma_row_q8 = [&](int j, const i32x8 (&kb)[kIdxKT], f32x4 (&acc)[kIdxKT][2]) {
@@ -322,9 +300,6 @@ __global__ __launch_bounds__(256, Q8 ? 3 : 1) void indexer_bf16_kernel(IndexerPa
       }
     };
     auto do_round = [&](int base, RawKeys<KFMT>& raw, int next) {
-      // BF16: every outstanding memory operation here was issued a round ago
-      // (this round's keys, the last scores): one wait for all of them
-      if constexpr (!Q8) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       const int s_own = base + wave * (kIdxKT * 16) + lane;  // key this lane stores
       const float own_mul = own_multiplier<KFMT>(raw, g);
       f32x4 acc[kIdxKT][2];
@@ -344,13 +319,7 @@ __global__ __launch_bounds__(256, Q8 ? 3 : 1) void indexer_bf16_kernel(IndexerPa
         bf16x8 bfr[kIdxKT][4];
 #pragma unroll
         for (int kt = 0; kt < kIdxKT; ++kt) dequant_tile<KFMT>(raw, kt, bfr[kt], raw.sc[kt], g);
-        flush();
-        pend = 0;
-        s_prev = s_own;
-        // issued even after the last round (its reads stay in the staged
-        // pages or page 0; never used): a conditional load would make the
-        // compiler merge the paths with a wait for every store before it
-        load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
+        if (next < kend) load_round<KFMT>(p, pg_lds, lp0, next, kend, wave, g, c, P, raw);
         for (int j = 0; j < nr; ++j) {
           mfma_row(j, bfr, acc);
           epi_row(j, acc, s_own, own_mul);
@@ -363,7 +332,6 @@ __global__ __launch_bounds__(256, Q8 ? 3 : 1) void indexer_bf16_kernel(IndexerPa
     RawKeys<KFMT> raw;
     load_round<KFMT>(p, pg_lds, lp0, k0, kend, wave, g, c, P, raw);
     for (int base = k0; base < kend; base += kIdxRound) do_round(base, raw, base + kIdxRound);
-    if constexpr (!Q8) flush();
 
     t0 += p.qrows;
     if (t0 >= re) break;

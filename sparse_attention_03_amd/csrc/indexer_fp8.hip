@@ -34,8 +34,6 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
   __shared__ float wl[kF8BM * 32];  // w * q_scale per row and head
   __shared__ int s_vmax[4];
   __shared__ int pg_lds[16384 / 16 + 1];  // page ids of this workgroup's key segment
-  // each lane's scores of the tile before (slot 4 q4 + j), written one tile late
-  __shared__ float s_out[4][8][64];
 
   const int r = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -121,22 +119,6 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
     }
   };
 
-  // Scores are written one tile late, just before the next tile's reads are
-  // issued: the vector-memory counter also counts stores, in issue order, so
-  // a store issued after a read would make the wait for that read wait for
-  // the store too.
-  float(&outw)[8][64] = s_out[wave];
-  uint32_t pend = 0;  // bit 4 q4 + j: this lane's score in outw slot 4 q4 + j is to be written
-  int prev_k0 = 0;
-  auto flush = [&]() {
-#pragma unroll
-    for (int q4 = 0; q4 < kF8BN / 64; ++q4)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (pend >> (4 * q4 + j) & 1u)
-          p.scores[(int64_t)(row0 + 4 * wave + j) * p.ld + prev_k0 + q4 * 64 + lane] = outw[4 * q4 + j][lane];
-  };
-
   load_tile(kb);
   for (int k0 = kb; k0 < ke; k0 += kF8BN) {
     __syncthreads();
@@ -147,12 +129,9 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
     }
     if (tid < kF8BN) kscale[tid] = sok ? sraw : -__builtin_inff();
     __syncthreads();
-    flush();
-    pend = 0;
-    prev_k0 = k0;
+
     // issued after the last tile too (reads stay in the staged pages; never
-    // used): a conditional read would make the compiler merge the paths with
-    // a wait for every store before it
+    // used): no branch around the reads
     load_tile(k0 + kF8BN);
 
 #pragma unroll
@@ -189,12 +168,11 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
           v[kt] = x;
         }
         const float tot = rows_reduce_scatter4(v);
-        outw[4 * q4 + j][lane] = (ksv == -__builtin_inff()) ? ksv : tot * ksv;
-        if (s < vis[j] && s < ke) pend |= 1u << (4 * q4 + j);
+        if (s < vis[j] && s < ke)
+          p.scores[(int64_t)(row0 + 4 * wave + j) * p.ld + s] = (ksv == -__builtin_inff()) ? ksv : tot * ksv;
       }
     }
   }
-  flush();
 }
 
 dsa_status launch_indexer_fp8(const IndexerParams& p, hipStream_t stream) {
