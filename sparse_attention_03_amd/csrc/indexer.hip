@@ -591,7 +591,12 @@ __global__ __launch_bounds__(256) void indexer_row_kernel(IndexerParams p) {
     idx_wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
     __syncthreads();
     float* out = p.scores + (int64_t)t * p.ld;
-    for (int i = tid; i < kend - k0; i += 256) out[k0 + i] = sc_out[i];
+    // Nontemporal stores: the scores are read once, by the top-k, and a store
+    // that allocates in the caches evicts (and writes back) whatever dirty
+    // lines they hold while the key stream runs (measured: 241 -> 213 us on
+    // the 64-request 256K MXFP4 batch, 110 -> 101 us at 1M; the top-k then
+    // reads the scores from HBM, 4-8 us more)
+    for (int i = tid; i < kend - k0; i += 256) __builtin_nontemporal_store(sc_out[i], out + k0 + i);
     if (t + 1 < t_end) __syncthreads();  // the next row rewrites the rings and sc_out
   }
 }
