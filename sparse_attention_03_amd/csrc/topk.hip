@@ -365,13 +365,14 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
   // every float4 read is issued unconditionally, a start past the row's ld
   // columns (ld and s_begin are multiples of 4) clamped to the last float4,
   // and positions at or past the slice end are masked afterwards (a read
-  // under a branch made each wait for the one before).
+  // under a branch made each wait for the one before).  The reads are
+  // nontemporal (each score is read once; 256K FP4 batch: 51 -> 43 us).
   const int last4 = (int)min<int64_t>(p.ld - 4, INT32_MAX - 3);
   f32x4 v[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int s = s_begin + 4 * tid + 1024 * b;
-    v[b] = *reinterpret_cast<const f32x4*>(row + min(s, last4));
+    v[b] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + min(s, last4)));
   }
   const float tf = key_threshold(ctr[2]);
   uint32_t hit[8];  // bit e of hit[b]: score 4*tid + 1024*b + e is a candidate
