@@ -66,20 +66,27 @@ dsa_status check_batch(const dsa_batch& b, int plog2, bool need_meta) {
 
 // ---- top-k plan
 struct TopkPlan {
-  int cand_cap, slice, nslices;
+  int cand_cap, slice, nslices, slice_cap;
   size_t off_ctr, off_cand, off_info, total;
 };
+// Long rows are filtered in slices of 8192 scores; every slice writes its
+// candidates to a region of its own of slice_cap entries (8 bytes each), so
+// the row's workgroups share no counter.  A slice with more candidates than
+// its region sends the row to the finalize's whole-row selection (the
+// threshold expects about 2900 of a row's candidates, about 90 per slice at
+// 256K scores).
 TopkPlan plan_topk(int T, int max_vis, int k) {
   (void)k;
   TopkPlan pl;
   pl.cand_cap = std::min(max_vis, dsa::kTopkFinalCap);
   pl.slice = 8192;
   pl.nslices = (max_vis + pl.slice - 1) / pl.slice;
+  pl.slice_cap = std::min(pl.cand_cap, 1024);
   size_t off = 0;
   pl.off_ctr = off;
   off = align_up(off + (size_t)T * 16, 256);
   pl.off_cand = off;
-  off = align_up(off + (size_t)T * pl.cand_cap * 8, 256);
+  off = align_up(off + (size_t)T * pl.nslices * pl.slice_cap * 8, 256);
   pl.off_info = off;
   off = align_up(off + (size_t)T * pl.nslices * 8, 256);
   pl.total = off;
@@ -513,6 +520,7 @@ dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
   p.cand = reinterpret_cast<uint32_t*>(ws + pl.off_cand);
   p.slice_info = reinterpret_cast<uint32_t*>(ws + pl.off_info);
   p.cand_cap = pl.cand_cap;
+  p.slice_cap = pl.slice_cap;
   p.slice = pl.slice;
   p.nslices = pl.nslices;
   dsa_status st = dsa::launch_topk(p, stream);
@@ -570,6 +578,7 @@ dsa_status dsa_topk_sharded(const dsa_topk_sharded_args* a, hipStream_t stream) 
   p.cand = reinterpret_cast<uint32_t*>(tws + pl.local.off_cand);
   p.slice_info = reinterpret_cast<uint32_t*>(tws + pl.local.off_info);
   p.cand_cap = pl.local.cand_cap;
+  p.slice_cap = pl.local.slice_cap;
   p.slice = pl.local.slice;
   p.nslices = pl.local.nslices;
   p.skip_empty = 1;

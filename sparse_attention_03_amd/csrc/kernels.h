@@ -67,10 +67,11 @@ struct TopkParams {
   int32_t* rows;
   int32_t* count;
   // workspace
-  uint32_t* ctr;        // [T][4]: candidates appended, -, threshold key, -
-  uint32_t* cand;       // [T][cand_cap][2]: order key, index
-  uint32_t* slice_info; // [T][nslices][2]: buffer position and count of each slice's candidates
-  int cand_cap;
+  uint32_t* ctr;        // [T][4]: -, -, threshold key, -
+  uint32_t* cand;       // [T][nslices][slice_cap][2]: each slice's candidates (order key, index)
+  uint32_t* slice_info; // [T][nslices][2]: -, count of each slice's candidates
+  int cand_cap;         // candidates the finalize selects from in LDS
+  int slice_cap;        // candidate entries of one slice's region
   int slice;            // scores per workgroup in the filter pass
   int nslices;
   int skip_empty;       // rows with no visible score write nothing (not even padding)

@@ -15,17 +15,17 @@
 //      K-th largest key when the whole row is the sample).  So with
 //      overwhelming probability at least K and not many more than K scores
 //      of the row are >= tau.
-//   2. filter: the row is cut into slices; every slice appends its keys >=
-//      tau, in index order, to the row's candidate buffer as one block behind
-//      one global atomic, and records where the block went.
+//   2. filter: the row is cut into slices; every slice writes its keys >=
+//      tau, in index order, to a region of the candidate buffer of its own
+//      (no atomic shared by the row's workgroups) and records their count.
 //   3. finalize: one workgroup per row puts the candidates in index order
 //      (blocks by slice), runs an exact radix select (12-bit digits) over
 //      their 64-bit composites (key, inverted index) -- ties go to the lower
 //      index -- and a stable compaction of the winners is the ordered result;
 //      it writes indices and physical rows.
-// The estimate only decides speed: when fewer than K or more than the
-// buffer's capacity of candidates arrived, finalize selects from the whole
-// score row instead (same result).
+// The estimate only decides speed: when fewer than K candidates arrived, more
+// than the finalize holds, or more than a slice's region holds, finalize
+// selects from the whole score row instead (same result).
 #include <type_traits>
 
 #include "common.h"
@@ -344,13 +344,12 @@ __device__ __forceinline__ void block_excl_scan_u64x4(const uint64_t (&v)[4], ui
 
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
   __shared__ uint64_t wsum[2][4];
-  __shared__ uint32_t s_base;
   const int t = blockIdx.y;
   const int tid = threadIdx.x;
   const int vis = row_vis(p, t);
   if (vis <= p.k) return;
   const int s_begin = blockIdx.x * p.slice;
-  uint32_t* ctr = p.ctr + (int64_t)t * 4;
+  const uint32_t* ctr = p.ctr + (int64_t)t * 4;
   uint32_t* info = p.slice_info + ((int64_t)t * p.nslices + blockIdx.x) * 2;
   if (s_begin >= vis) {
     if (tid == 0) {
@@ -398,25 +397,23 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkParams p) {
     off[b] = n;
     n += (uint32_t)(((b < 4 ? tot0 : tot1) >> (16 * (b & 3))) & 0xFFFFu);
   }
+  // the slice's own region (slice_cap entries; a count above it sends the
+  // row to the whole-row selection)
   if (tid == 0) {
-    const uint32_t base = atomicAdd(&ctr[0], n);
-    s_base = base;
-    info[0] = base;
+    info[0] = 0;
     info[1] = n;
   }
-  __syncthreads();
-  const uint32_t base = s_base;
-  uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
+  uint32_t* creg = p.cand + ((int64_t)t * p.nslices + blockIdx.x) * p.slice_cap * 2;
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    uint32_t pos = base + off[b] + (uint32_t)(((b < 4 ? ex0 : ex1) >> (16 * (b & 3))) & 0xFFFFu);
+    uint32_t pos = off[b] + (uint32_t)(((b < 4 ? ex0 : ex1) >> (16 * (b & 3))) & 0xFFFFu);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (hit[b] >> e & 1u) {
-        if (pos < (uint32_t)p.cand_cap) {
+        if (pos < (uint32_t)p.slice_cap) {
           const int s = s_begin + 4 * tid + 1024 * b + e;
-          candrow[2 * pos] = order_key(v[b][e]);
-          candrow[2 * pos + 1] = (uint32_t)s;
+          creg[2 * pos] = order_key(v[b][e]);
+          creg[2 * pos + 1] = (uint32_t)s;
         }
         ++pos;
       }
@@ -606,59 +603,47 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
     return;
   }
 
-  const uint32_t* ctr = p.ctr + (int64_t)t * 4;
-  const int ncand = (int)ctr[0];
-  const uint32_t* candrow = p.cand + (int64_t)t * p.cand_cap * 2;
+  // Slice counts (rows of up to 1024 slices, 8M scores), their exclusive
+  // prefix, and the candidates gathered from the slices' regions into LDS in
+  // index order; the whole score row instead when the estimate missed (fewer
+  // than K, or more than the LDS or a slice's region holds).
   const float* srow = p.scores + (int64_t)t * p.ld;
-  // candidates in LDS in index order, or (estimate missed) the whole score row
-  const bool from_row = ncand < K || ncand > p.cand_cap;
-  const int nsrc = from_row ? vis : ncand;
-  // rows of up to 1024 slices (8M scores) get their candidates in index order
-  const bool ordered = !from_row && p.nslices <= 1024;
-  if (!from_row && !ordered)
-    for (int i = tid; i < ncand; i += blockDim.x) {
-      ck[i] = candrow[2 * i];
-      ci[i] = candrow[2 * i + 1];
-    }
-  if (ordered) {
-    // Every slice's block is contiguous and in index order; blocks lie in
-    // arrival order.  A candidate at buffer position i of slice s goes to
-    // off[s] + (i - base[s]), off = exclusive prefix of the slices' counts.
-    // The candidate loads are issued together with the slice table's.
-    constexpr int kPer = kTopkFinalCap / 1024;
-    uint2 cv[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = tid + 1024 * u;
-      if (i < ncand) cv[u] = reinterpret_cast<const uint2*>(candrow)[i];
-    }
-    uint32_t* sbase = reinterpret_cast<uint32_t*>(tpre);          // [nslices <= 1024]
-    uint32_t* soff = reinterpret_cast<uint32_t*>(ord);            // [nslices <= 2048]
+  uint32_t* soff = reinterpret_cast<uint32_t*>(ord);  // [nslices <= 1024]
+  uint32_t* scnt = reinterpret_cast<uint32_t*>(tpre);  // [nslices <= 1024]
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool sliced = p.nslices <= 1024;
+  int ncand = 0;
+  bool over = !sliced;
+  if (sliced) {
     const uint32_t* info = p.slice_info + (int64_t)t * p.nslices * 2;
-    uint32_t cnt = 0, sb = 0;
-    if (tid < p.nslices) {
-      sb = info[2 * tid];
-      cnt = info[2 * tid + 1];
-    }
+    const uint32_t cnt = tid < p.nslices ? info[2 * tid + 1] : 0u;
     const int inc = (int)wave_scan_incl(cnt);
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool big = __ballot(cnt > (uint32_t)p.slice_cap) != 0;
     if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
+    if (lane == 0) sl.h[wave] = big ? 1u : 0u;
     __syncthreads();
-    uint32_t all_unused;
-    const int before = (int)waves_before(sl.wtot, 16, wave, all_unused);
+    uint32_t all;
+    const int before = (int)waves_before(sl.wtot, 16, wave, all);
+    ncand = (int)all;
+    over = waves_max(sl.h, 16) != 0u;
     if (tid < p.nslices) {
-      sbase[tid] = sb;
       soff[tid] = (uint32_t)(before + inc) - cnt;
+      scnt[tid] = cnt;
     }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = tid + 1024 * u;
-      if (i < ncand) {
-        const int sl_id = (int)cv[u].y / p.slice;
-        const uint32_t dst = soff[sl_id] + (uint32_t)i - sbase[sl_id];
-        ck[dst] = cv[u].x;
-        ci[dst] = cv[u].y;
+  }
+  const bool from_row = over || ncand < K || ncand > p.cand_cap;
+  const int nsrc = from_row ? vis : ncand;
+  const bool ordered = !from_row;
+  __syncthreads();
+  if (ordered) {
+    // wave w copies slices w, w + 16, ...; its lanes take consecutive entries
+    for (int sidx = wave; sidx < p.nslices; sidx += 16) {
+      const int n = (int)scnt[sidx], o = (int)soff[sidx];
+      const uint2* creg = reinterpret_cast<const uint2*>(p.cand + ((int64_t)t * p.nslices + sidx) * p.slice_cap * 2);
+      for (int j = lane; j < n; j += 64) {
+        const uint2 cv = creg[j];
+        ck[o + j] = cv.x;
+        ci[o + j] = cv.y;
       }
     }
   }
@@ -681,7 +666,6 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
       if (i < ncand && (composite(ck[i], ci[i]) >> hi_sh) >= prefix) m |= 1u << u;
     }
     const int inc = (int)wave_scan_incl((uint32_t)__popc(m));
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     __syncthreads();  // sl.wtot was read by select_top
     if (lane == 63) sl.wtot[wave] = (uint32_t)inc;
     __syncthreads();

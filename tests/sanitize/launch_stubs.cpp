@@ -127,7 +127,8 @@ dsa_status launch_topk(const TopkParams& p, hipStream_t) {
   }
   if (p.count) write_all(p.count, (size_t)p.T * 4);
   write_all(p.ctr, (size_t)p.T * 16);
-  write_all(p.cand, (size_t)p.T * p.cand_cap * 8);
+  write_all(p.cand, (size_t)p.T * p.nslices * p.slice_cap * 8);
+  need(p.slice_cap >= 1 && p.slice_cap <= p.cand_cap, "topk slice region");
   write_all(p.slice_info, (size_t)p.T * p.nslices * 8);
   need(p.cand_cap >= std::min(p.max_vis, kTopkFinalCap), "topk candidate buffer");
   need((int64_t)p.nslices * p.slice >= p.max_vis, "topk slices");
