@@ -316,21 +316,22 @@ __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* ws
   return before + inc - v;
 }
 
-// Four words at once, behind one barrier.  wsum: [16][4].
-__device__ __forceinline__ void block_excl_scan_u64x4(const uint64_t (&v)[4], uint64_t (&ex)[4], uint64_t (&tot)[4],
-                                                      uint64_t (*wsum)[4]) {
+// NWD (<= 4) words at once, behind one barrier.  wsum: [16][4].
+template <int NWD>
+__device__ __forceinline__ void block_excl_scan_u64x4(const uint64_t (&v)[NWD], uint64_t (&ex)[NWD],
+                                                      uint64_t (&tot)[NWD], uint64_t (*wsum)[4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint64_t inc[4];
+  uint64_t inc[NWD];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) inc[i] = wave_scan_incl_u64(v[i]);
+  for (int i = 0; i < NWD; ++i) inc[i] = wave_scan_incl_u64(v[i]);
   if (lane == 63)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wsum[wave][i] = inc[i];
+    for (int i = 0; i < NWD; ++i) wsum[wave][i] = inc[i];
   __syncthreads();
   const int nw = (int)(blockDim.x >> 6);
   const int ln = lane < nw ? lane : 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NWD; ++i) {
     const uint64_t x = lane < nw ? wsum[ln][i] : 0ull;
     const uint32_t il = wave_scan_incl((uint32_t)x), ih = wave_scan_incl((uint32_t)(x >> 32));
     tot[i] = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)il, nw - 1) |
@@ -696,10 +697,12 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
 }
 
 // Rows up to kRowMax scores: one workgroup per row does everything with the
-// row held in registers (16 float4 per thread: scores 4*tid + 4096*i + c, so
-// index order is (i, tid, c)), one read of the row, one launch, no workspace.
-//   threshold  from the sample key[tid & 15][*] (every 16th group of four
-//              scores; every score of a row up to kExactMax) by two 12-bit
+// row held in registers (NS float4 per thread: scores 4*tid + 4096*i + c, so
+// index order is (i, tid, c); NS = 16, or 8 for rows up to 32K, which halves
+// the registers and the per-score work of the prefill shape), one read of
+// the row, one launch, no workspace.
+//   threshold  from the sample key[tid & (NS-1)][*] (every NS-th group of four
+//              scores; every score of a row up to the candidate capacity) by two 12-bit
 //              histogram levels, as in the threshold kernel;
 //   select     the exact radix select runs directly over the register keys
 //              at or above the threshold (over all keys of the row when fewer
@@ -709,13 +712,17 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
 //              64-bit word, get one block exclusive scan.
 constexpr int kRowMax = 16 * 4096;
 
-constexpr int kRowCap = 8192;  // candidates the per-row kernel holds in LDS
+// Candidates the per-row kernel holds in LDS: 8192 for rows up to 64K, 4096
+// for rows up to 32K (about 2600 expected), whose workgroup then fits two to a
+// CU (75 KB of LDS, 59 registers).
+template <int NS> constexpr int row_cap() { return NS == 16 ? 8192 : 4096; }
 
-struct RowLds {
+template <int CAP>
+struct RowLdsT {
   SelectLds sl;
   uint32_t h2[4096];          // level-2 histogram (cleared with level 1's)
-  uint32_t ck[kRowCap];       // candidate scores (bits), in index order
-  uint32_t ci[kRowCap];       // their indices
+  uint32_t ck[CAP];           // candidate scores (bits), in index order
+  uint32_t ci[CAP];           // their indices
   int ord[DSA_MAX_TOPK];      // the winners in index order
   uint32_t s_lo[16], s_hi[16];
   int s_cnt[16];
@@ -739,7 +746,7 @@ __device__ __forceinline__ int block_excl_scan_i32(int v, int* wsum, int& total)
 // digits from the highest bit in which they differ).  Afterwards the keys
 // with (key >> sh) > pre win, and: full -> every key with (key >> sh) == pre
 // wins too; else (sh == 0) the first `need` keys equal to pre win.
-template <class Get>
+template <class Get, class RowLds>
 __device__ __forceinline__ void select32(Get get, int n, uint32_t K, RowLds& L, int& sh_out, uint32_t& pre_out,
                                          uint32_t& need_out, bool& full_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -798,7 +805,7 @@ __device__ __forceinline__ void select32(Get get, int n, uint32_t K, RowLds& L, 
 // chunks of 8192 keys, thread tid owning keys 8 tid .. 8 tid + 7 of a chunk;
 // block scans of the counts of equal keys (the tie-break rank) and of
 // winners, carried from chunk to chunk.
-template <class Get, class Idx>
+template <class Get, class Idx, class RowLds>
 __device__ __forceinline__ void emit_winners(Get get, Idx index_of, int n, int sh, uint32_t pre, uint32_t need,
                                              bool full, RowLds& L) {
   const int tid = threadIdx.x;
@@ -841,8 +848,10 @@ __device__ __forceinline__ void emit_winners(Get get, Idx index_of, int n, int s
   __syncthreads();
 }
 
+template <int NS>
 __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
-  __shared__ RowLds L;
+  constexpr int kRowCap = row_cap<NS>();
+  __shared__ RowLdsT<kRowCap> L;
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vis = row_vis(p, t);
@@ -862,15 +871,15 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
   // The scores stay floats: a position at or past vis holds NaN, which no
   // comparison admits (scores are finite or -inf), and the order key of a
   // score is formed only for the sample and the candidates.
-  f32x4 x[16];
+  f32x4 x[NS];
   {
     const float* row = p.scores + (int64_t)t * p.ld;
-    const int last4 = (int)min<int64_t>(p.ld - 4, kRowMax - 4);
+    const int last4 = (int)min<int64_t>(p.ld - 4, NS * 4096 - 4);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < NS; ++i)
       x[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + min(4 * tid + 4096 * i, last4)));
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < NS; ++i)
       if (4096 * (i + 1) > vis)  // (uniform) stripe i reaches past vis
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -888,14 +897,14 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
 
   // ---- threshold: keys >= tau are the candidates (tau = 1: every key)
   uint32_t tau = 1u;
-  if (vis > kExactMax) {
+  if (vis > kRowCap) {  // (a row up to the candidate capacity keeps every score)
     uint32_t samp[4];
-    const int sel = tid & 15;
+    const int sel = tid & (NS - 1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float v = x[0][c];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) v = sel == i ? x[i][c] : v;
+      for (int i = 1; i < NS; ++i) v = sel == i ? x[i][c] : v;
       samp[c] = key_of(v);
     }
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -955,11 +964,14 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
   // so fields never carry), one block exclusive scan per word.  key >= tau is
   // tested on the score itself.
   const float tf = key_threshold(tau);
-  auto field = [](const uint64_t (&w)[4], int i) { return (uint32_t)((w[i >> 2] >> (16 * (i & 3))) & 0xFFFFu); };
+  auto field = [](const uint64_t (&w)[NS / 4], int i) { return (uint32_t)((w[i >> 2] >> (16 * (i & 3))) & 0xFFFFu); };
   {
-    uint64_t pc[4] = {0, 0, 0, 0}, exc[4], totc[4];
+    constexpr int NWD = NS / 4;  // 64-bit words of four 16-bit stripe fields
+    uint64_t pc[NWD], exc[NWD], totc[NWD];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int w = 0; w < NWD; ++w) pc[w] = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
       int n = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) n += x[i][c] >= tf ? 1 : 0;
@@ -968,11 +980,11 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(TopkParams p) {
     block_excl_scan_u64x4(pc, exc, totc, L.wsum4);
     uint32_t ncand = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ncand += field(totc, i);
+    for (int i = 0; i < NS; ++i) ncand += field(totc, i);
     if (ncand >= (uint32_t)K && ncand <= (uint32_t)kRowCap) {
       uint32_t off = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < NS; ++i) {
         uint32_t pos = off + field(exc, i);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -1124,8 +1136,12 @@ dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(topk_short_kernel, dim3(p.T), dim3(kShortThreads), 0, stream, p);
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
   }
+  if (p.max_vis <= kRowMax / 2) {
+    hipLaunchKernelGGL((topk_row_kernel<8>), dim3(p.T), dim3(1024), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+  }
   if (p.max_vis <= kRowMax) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(p.T), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL((topk_row_kernel<16>), dim3(p.T), dim3(1024), 0, stream, p);
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
   }
   hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.T), dim3(1024), 0, stream, p);

@@ -168,17 +168,21 @@ def _topk_alone(scores, vis, k, gpu):
     return idx.cpu().numpy(), cnt.cpu().numpy()
 
 
-@pytest.mark.parametrize("ld", [100000, 40000, 8000])
+@pytest.mark.parametrize("ld", [100000, 40000, 30000, 8000])
 @pytest.mark.parametrize("kind", ["random", "ties", "all_equal", "short_rows", "k1", "negative", "sampled_high",
-                                  "row_sampled_high"])
+                                  "row_sampled_high", "one_slice_high"])
 def test_topk_exact_on_same_scores(kind, ld, gpu):
-    # ld 100000: threshold / filter / finalize kernels; ld 40000 and 8000: the
-    # one-workgroup-per-row kernel (sampled threshold at 40000, every score at
-    # 8000).  "all_equal" overflows the candidate buffers; "sampled_high" and
+    # ld 100000: threshold / filter / finalize kernels; ld 40000, 30000 and
+    # 8000: the one-workgroup-per-row kernel (16 float4 per thread at 40000,
+    # 8 at 30000 and 8000; sampled threshold at 40000 and 30000, every score
+    # at 8000).  "all_equal" overflows the candidate buffers; "sampled_high" and
     # "row_sampled_high" put large scores only where the threshold sample of
     # the multi-kernel path (the first 16 of every 256) or of the per-row
-    # kernel (group (p >> 12) & 15 == (p >> 2) & 15 of four) looks, so the
-    # sampled threshold comes out too high and the whole row is selected from.
+    # kernel (group (p >> 12) & m == (p >> 2) & m of four, m = 15, or 7 for
+    # rows up to 32K) looks, so the sampled threshold comes out too high and
+    # the whole row is selected from.
+    # "one_slice_high" puts 1800 of the top scores in one 8192-score slice of
+    # the filter pass, more than a slice's candidate region (1024) holds.
     g = np.random.default_rng(42)
     T, k = 6, 2048
     if kind == "random":
@@ -199,14 +203,20 @@ def test_topk_exact_on_same_scores(kind, ld, gpu):
     elif kind == "sampled_high":
         s = g.standard_normal((T, ld)).astype(np.float32)
         s[:, (np.arange(ld) % 256) < 16] += 1000.0
-    else:
+    elif kind == "row_sampled_high":
         s = g.standard_normal((T, ld)).astype(np.float32)
         pos = np.arange(ld)
-        s[:, ((pos >> 12) & 15) == ((pos >> 2) & 15)] += 1000.0
+        m = 7 if ld <= 32768 else 15
+        s[:, ((pos >> 12) & m) == ((pos >> 2) & m)] += 1000.0
+    else:
+        s = g.standard_normal((T, ld)).astype(np.float32)
+        s[:, 3 * 8192 // 4: 3 * 8192 // 4 + 1800] += 5.0 if ld < 8192 * 4 else 0.0
+        s[:, 3 * 8192: 3 * 8192 + 1800] += 5.0 if ld >= 8192 * 4 else 0.0
     if ld == 100000:
         vis = [ld, ld - 1, 30001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 70001, 65537, 8193, 4097]
-    elif ld == 40000:
-        vis = [ld, ld - 1, 30001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 40000, 12345, 8193, 4097]
+    elif ld in (40000, 30000):
+        vis = [ld, ld - 1, 30001 if ld > 30001 else 20001, 2049, 2048, 17] if kind == "short_rows" else \
+            [ld, ld - 3, ld, 12345, 8193, 4097]
     else:
         vis = [ld, ld - 1, 5001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 8000, 6345, 4097, 2049]
     idx, cnt = _topk_alone(torch.from_numpy(s), vis, k, gpu)
