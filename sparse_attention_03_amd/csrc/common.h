@@ -39,8 +39,11 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 
 // D(16x16) += A(16x128) * B(128x16) with FP8 E4M3 inputs (unit block scales).
-// Lane l supplies 32 consecutive k-values A[l%16][32*(l/16) .. +32) and
-// B[32*(l/16) .. +32)[l%16]; D layout as above.
+// Lane l supplies 32 k-values of row l%16 of A and of column l%16 of B; the
+// instruction takes bytes 0-15 as k = 16*(l/16) .. +15 and bytes 16-31 as
+// k = 64 + 16*(l/16) .. +15.  Under unit scales any k order that A and B
+// share gives the same product, so callers place k as they like (e.g. 32
+// consecutive values per lane).  D layout as above.
 __device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
   // cbsz = blgp = 0 selects FP8 E4M3 for both operands; E8M0 scale 127 = 1.0.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);

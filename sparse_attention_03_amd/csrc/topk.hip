@@ -699,8 +699,8 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(TopkParams p) {
 // Rows up to kRowMax scores: one workgroup per row does everything with the
 // row held in registers (NS float4 per thread: scores 4*tid + 4096*i + c, so
 // index order is (i, tid, c); NS = 16, or 8 for rows up to 32K, which halves
-// the registers and the per-score work of the prefill shape), one read of
-// the row, one launch, no workspace.
+// the registers and the per-score work of the prefill shape, or 4 for rows
+// up to 8K), one read of the row, one launch, no workspace.
 //   threshold  from the sample key[tid & (NS-1)][*] (every NS-th group of four
 //              scores; every score of a row up to the candidate capacity) by two 12-bit
 //              histogram levels, as in the threshold kernel;
@@ -714,8 +714,10 @@ constexpr int kRowMax = 16 * 4096;
 
 // Candidates the per-row kernel holds in LDS: 8192 for rows up to 64K, 4096
 // for rows up to 32K (about 2600 expected), whose workgroup then fits two to a
-// CU (75 KB of LDS, 59 registers).
-template <int NS> constexpr int row_cap() { return NS == 16 ? 8192 : 4096; }
+// CU (75 KB of LDS, 59 registers), and 8192 for rows up to 8K (four stripes):
+// such a row is kept whole, with no sampled threshold, and every thread
+// compares 16 register scores instead of 32.
+template <int NS> constexpr int row_cap() { return NS == 8 ? 4096 : 8192; }
 
 template <int CAP>
 struct RowLdsT {
@@ -1134,6 +1136,10 @@ dsa_status launch_topk(const TopkParams& p, hipStream_t stream) {
   // (few short rows: the 1024-thread row kernel has the shorter per-row latency)
   if (p.max_vis <= kShortMax && p.T >= kShortMinRows) {
     hipLaunchKernelGGL(topk_short_kernel, dim3(p.T), dim3(kShortThreads), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+  }
+  if (p.max_vis <= row_cap<4>()) {
+    hipLaunchKernelGGL((topk_row_kernel<4>), dim3(p.T), dim3(1024), 0, stream, p);
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
   }
   if (p.max_vis <= kRowMax / 2) {

@@ -168,14 +168,14 @@ def _topk_alone(scores, vis, k, gpu):
     return idx.cpu().numpy(), cnt.cpu().numpy()
 
 
-@pytest.mark.parametrize("ld", [100000, 40000, 30000, 8000])
+@pytest.mark.parametrize("ld", [100000, 40000, 30000, 8192, 8000])
 @pytest.mark.parametrize("kind", ["random", "ties", "all_equal", "short_rows", "k1", "negative", "sampled_high",
                                   "row_sampled_high", "one_slice_high"])
 def test_topk_exact_on_same_scores(kind, ld, gpu):
-    # ld 100000: threshold / filter / finalize kernels; ld 40000, 30000 and
-    # 8000: the one-workgroup-per-row kernel (16 float4 per thread at 40000,
-    # 8 at 30000 and 8000; sampled threshold at 40000 and 30000, every score
-    # at 8000).  "all_equal" overflows the candidate buffers; "sampled_high" and
+    # ld 100000: threshold / filter / finalize kernels; ld 40000, 30000, 8192
+    # and 8000: the one-workgroup-per-row kernel (16 float4 per thread at
+    # 40000, 8 at 30000, 4 at 8192 and 8000; sampled threshold at 40000 and
+    # 30000, every score kept at 8192 and 8000).  "all_equal" overflows the candidate buffers; "sampled_high" and
     # "row_sampled_high" put large scores only where the threshold sample of
     # the multi-kernel path (the first 16 of every 256) or of the per-row
     # kernel (group (p >> 12) & m == (p >> 2) & m of four, m = 15, or 7 for
@@ -218,7 +218,7 @@ def test_topk_exact_on_same_scores(kind, ld, gpu):
         vis = [ld, ld - 1, 30001 if ld > 30001 else 20001, 2049, 2048, 17] if kind == "short_rows" else \
             [ld, ld - 3, ld, 12345, 8193, 4097]
     else:
-        vis = [ld, ld - 1, 5001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, 8000, 6345, 4097, 2049]
+        vis = [ld, ld - 1, 5001, 2049, 2048, 17] if kind == "short_rows" else [ld, ld - 3, min(ld, 8000), 6345, 4097, 2049]
     idx, cnt = _topk_alone(torch.from_numpy(s), vis, k, gpu)
     for t in range(T):
         ref, _ = O.topk(s[t, : vis[t]].astype(np.float64), k)
