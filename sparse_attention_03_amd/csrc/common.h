@@ -99,6 +99,12 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t w, float pow2_scale)
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// 2^x on the transcendental unit (v_exp_f32, about 1 ulp): 0 for -inf, and
+// results below the normal range flush to 0, which a softmax weight (at most
+// 2^8 against its running max) can lose without effect.  exp2f adds a range
+// reduction for those results: four more instructions per weight.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // fp32 pair -> packed bf16 pair, round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v;

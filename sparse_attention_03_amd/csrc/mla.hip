@@ -192,12 +192,14 @@ __device__ __forceinline__ void mla_tile(const MlaParams& p, const __bf16* lat, 
   // (weights stay <= 256); both O and l use the same max, so the final
   // normalisation is exact
   const float mnew = (m == -__builtin_inff() || tmax > m + kRescaleLog2) ? tmax : m;
-  const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - mnew);
+  const float alpha = (m == -__builtin_inff()) ? 1.f : exp2_hw(m - mnew);
+  // (a max still -inf means every logit so far is -inf: 2^(-inf - 0) = 0)
+  const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
   float psum = 0.f;
   float pw[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const float e = (lg[x] == -__builtin_inff() || mnew == -__builtin_inff()) ? 0.f : exp2f(lg[x] - mnew);
+    const float e = exp2_hw(lg[x] - mref);
     psum += e;
     pw[x] = e * rs[x];  // FP8 row scale enters the value product here
   }
