@@ -36,7 +36,7 @@ namespace dsa {
 
 constexpr int kExactMax = 8192;     // rows up to this length are sampled completely
 constexpr int kMaxSamples = 16384;  // 16 per thread of the threshold workgroup
-constexpr int kRun = 16;            // consecutive scores per sampled block
+constexpr int kRun = 32;            // consecutive scores per sampled block (one 128-byte line)
 
 __device__ __forceinline__ int row_vis(const TopkParams& p, int t) {
   return clamp_vis(p.tok_vis[t], p.max_vis);
@@ -205,14 +205,14 @@ __global__ __launch_bounds__(1024) void topk_threshold_kernel(TopkParams p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = tid + 1024 * i;
-    const int64_t s = (int64_t)(e >> 4) * B + (e & 15);
+    const int64_t s = (int64_t)(e / kRun) * B + (e % kRun);
     v[i] = s < vis ? row[s] : 0.f;
   }
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = tid + 1024 * i;
-    const int64_t s = (int64_t)(e >> 4) * B + (e & 15);
+    const int64_t s = (int64_t)(e / kRun) * B + (e % kRun);
     key[i] = s < vis ? order_key(v[i]) : 0u;
     if (s < vis) {
       lo = min(lo, key[i]);

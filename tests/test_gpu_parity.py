@@ -177,7 +177,7 @@ def test_topk_exact_on_same_scores(kind, ld, gpu):
     # 40000, 8 at 30000, 4 at 8192 and 8000; sampled threshold at 40000 and
     # 30000, every score kept at 8192 and 8000).  "all_equal" overflows the candidate buffers; "sampled_high" and
     # "row_sampled_high" put large scores only where the threshold sample of
-    # the multi-kernel path (the first 16 of every 256) or of the per-row
+    # the multi-kernel path (the first 32 of every 256) or of the per-row
     # kernel (group (p >> 12) & m == (p >> 2) & m of four, m = 15, or 7 for
     # rows up to 32K) looks, so the sampled threshold comes out too high and
     # the whole row is selected from.
@@ -202,7 +202,7 @@ def test_topk_exact_on_same_scores(kind, ld, gpu):
         s[:, 3::7] = -0.0
     elif kind == "sampled_high":
         s = g.standard_normal((T, ld)).astype(np.float32)
-        s[:, (np.arange(ld) % 256) < 16] += 1000.0
+        s[:, (np.arange(ld) % 256) < 32] += 1000.0
     elif kind == "row_sampled_high":
         s = g.standard_normal((T, ld)).astype(np.float32)
         pos = np.arange(ld)
