@@ -706,10 +706,6 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
     copy_tile(row_of(id_at(d, c)), d);
   }
 
-  // transposed-read source of this lane: byte slot j = (lane%16)/2 -> row
-  // 4g + j%4 of dim chunk j/4 (+16 dims), half lane%2 of the 16 bytes
-  const int tj = (lane & 15) >> 1;
-  const int t_off = (tj >> 2) * 256 + (4 * g + (tj & 3)) * 16 + 8 * (lane & 1);
 
   for (int it = 0; it < ntile; ++it) {
     const int slot = it % DP;
@@ -750,11 +746,12 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
       tmax = fmaxf(tmax, xor16(tmax, g));
       tmax = fmaxf(tmax, xor32(tmax, g));
       const float mnew = (m == -__builtin_inff() || tmax > m + kRescaleLog2) ? tmax : m;
-      const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - mnew);
+      const float alpha = (m == -__builtin_inff()) ? 1.f : exp2_hw(m - mnew);
       float psum = 0.f, pw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = (lg[i] == -__builtin_inff() || mnew == -__builtin_inff()) ? 0.f : exp2f(lg[i] - mnew);
+        // (a finite logit has a finite max)
+        const float e = lg[i] == -__builtin_inff() ? 0.f : exp2_hw(lg[i] - mnew);
         psum += e;
         pw[i] = e * sc[i];
       }
@@ -774,7 +771,15 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
           for (int i = 0; i < 4; ++i) O[x][i] *= ai[i];
       }
       // ---- PV: read n covers dims 32 n + c (O[2n]) and 32 n + 16 + c (O[2n+1])
-      const uint8_t* vsrc = sl + t_off;
+      // transposed-read source of this lane: byte slot j = (lane%16)/2 -> row
+      // 4g + j%4 of dim chunk j/4 (+16 dims), half lane%2 of the 16 bytes
+      // (the lane id comes from an asm the compiler cannot hoist, so the
+      // read offset is formed here each tile: kept live through the loop it
+      // is the value spilled at 256 VGPRs)
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int tj = (ln & 15) >> 1;
+      const uint8_t* vsrc = sl + (tj >> 2) * 256 + (4 * (ln >> 4) + (tj & 3)) * 16 + 8 * (ln & 1);
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         typedef int v2i __attribute__((ext_vector_type(2)));
