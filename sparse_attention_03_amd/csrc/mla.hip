@@ -721,18 +721,18 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
       bool ok[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ok[i] = row_ok(id_at(it, 4 * g + i), p);
-      // ---- QK: four independent accumulator chains
-      f32x4 s;
+      // ---- QK: one accumulator chain (an MFMA that accumulates into the
+      // previous one's result issues behind it; the second wave per SIMD
+      // fills the gaps, and no partial sums need adding)
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
       {
         const uint8_t* src = sl + lane * 16;
-        f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int sp = 0; sp < 9; ++sp) {
           const i32x4 raw = *reinterpret_cast<const i32x4*>(src + sp * 1024);
-          sa[(2 * sp) & 3] = mfma16x16x32(e4m3x8_to_bf16x8(raw[0], raw[1]), qf[2 * sp], sa[(2 * sp) & 3]);
-          sa[(2 * sp + 1) & 3] = mfma16x16x32(e4m3x8_to_bf16x8(raw[2], raw[3]), qf[2 * sp + 1], sa[(2 * sp + 1) & 3]);
+          s = mfma16x16x32(e4m3x8_to_bf16x8(raw[0], raw[1]), qf[2 * sp], s);
+          s = mfma16x16x32(e4m3x8_to_bf16x8(raw[2], raw[3]), qf[2 * sp + 1], s);
         }
-        s = (sa[0] + sa[1]) + (sa[2] + sa[3]);
       }
       // ---- online softmax for head c over rows 4g+i
       float lg[4];
@@ -747,11 +747,13 @@ __global__ __launch_bounds__(64 * NW) void mla_f8_kernel(MlaParams p) {
       tmax = fmaxf(tmax, xor32(tmax, g));
       const float mnew = (m == -__builtin_inff() || tmax > m + kRescaleLog2) ? tmax : m;
       const float alpha = (m == -__builtin_inff()) ? 1.f : exp2_hw(m - mnew);
+      // a finite floor for the max: a -inf logit then weighs 2^-inf = 0 even
+      // while every logit so far is -inf
+      const float mref = fmaxf(mnew, -3.0e38f);
       float psum = 0.f, pw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // (a finite logit has a finite max)
-        const float e = lg[i] == -__builtin_inff() ? 0.f : exp2_hw(lg[i] - mnew);
+        const float e = exp2_hw(lg[i] - mref);
         psum += e;
         pw[i] = e * sc[i];
       }
